@@ -1,0 +1,152 @@
+/*
+ * msda.h - C ABI of the MI355X (gfx950) multi-scale deformable attention core.
+ *
+ * The operator is the bracket of Deformable DETR's Eq. 1 as chapter 1 of the
+ * msda-triton course defines it ("1. Deformable attention, from scratch",
+ * sections "The equation, term by term", "Bilinear interpolation: reading
+ * between the pixels" and "The simplest possible implementation"): for every
+ * batch b, query q and head m,
+ *
+ *   out[b, q, m*D + d] = sum_{l<L} sum_{k<K} A[b,q,m,l,k] * bilinear_l(x, y)[d]
+ *
+ * where (x, y) = (loc_x * W_l - 0.5, loc_y * H_l - 0.5) is the pixel-centre
+ * mapping of sampling_locations[b,q,m,l,k,:], the bilinear sample blends the
+ * four surrounding pixels of level l of value[b, :, m, :], and a corner that
+ * falls outside the H_l x W_l map contributes zero.  Attention weights are
+ * used as given (the DeformOps page, section "Multi-scale deformable
+ * attention", describes that default).  The backward returns the gradients of
+ * <out, grad_out> with respect to value, sampling_locations and
+ * attention_weights.
+ *
+ * Tensor layouts (all row-major, contiguous, on the device that runs the
+ * stream):
+ *   value               [B, S, M, D]        S = sum_l H_l * W_l
+ *   spatial_shapes      [L, 2] int64        rows (H_l, W_l)
+ *   level_start_index   [L]    int64        exclusive prefix sum of H_l * W_l
+ *   sampling_locations  [B, Q, M, L, K, 2]  last axis (x, y), normalised
+ *   attention_weights   [B, Q, M, L, K]
+ *   out, grad_out       [B, Q, M * D]
+ *   grad_value          [B, S, M, D]
+ *   grad_loc            [B, Q, M, L, K, 2]
+ *   grad_attn           [B, Q, M, L, K]
+ * All floating tensors of one call share `dtype`.  spatial_shapes and
+ * level_start_index are device pointers; they are read by the kernels only.
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     allocates no device memory, frees nothing and keeps no pointer after
+ *     the call returns.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and the call returns without waiting for it.  Buffers must
+ *     stay valid until that work completes.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Errors: a non-OK status is returned before anything is enqueued when the
+ *     arguments are rejected; msda_last_error() then describes the reason.
+ *     MSDA_ERR_HIP reports a failed launch.
+ *   - Supported: dtype FP32 or BF16; D in {8, 16, 32, 64}; 1 <= L <= 16;
+ *     1 <= K <= 32; L*K <= 64; B, Q >= 0; S >= 1; M >= 1; one batch image of
+ *     value (S*M*D elements) below 2^30 bytes; every element count below 2^62.
+ *     Float pointers must be 16-byte aligned.  Anything else returns
+ *     MSDA_ERR_UNSUPPORTED / MSDA_ERR_INVALID_DIMS / MSDA_ERR_MISALIGNED.
+ *   - Trusted preconditions (device data the host cannot inspect without a
+ *     sync): H_l, W_l >= 1, level_start_index is the prefix sum of H_l*W_l and
+ *     S >= its last entry + H_{L-1} * W_{L-1}.  If they are violated the
+ *     results are wrong, but every memory access stays inside value and
+ *     grad_value (reads and atomics go through range-checked buffer
+ *     descriptors).
+ *   - Sampling locations may be any float, including NaN and +-Inf: a sample
+ *     none of whose four corners lies inside its level contributes nothing
+ *     and receives zero gradients.
+ *   - Reentrant and thread-safe: no global mutable state apart from the
+ *     thread-local error string.
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSDA_OK = 0,
+    MSDA_ERR_NULL_POINTER = 1,
+    MSDA_ERR_INVALID_DIMS = 2,
+    MSDA_ERR_UNSUPPORTED = 3,
+    MSDA_ERR_MISALIGNED = 4,
+    MSDA_ERR_WORKSPACE = 5,
+    MSDA_ERR_HIP = 6
+} msda_status;
+
+typedef enum { MSDA_FP32 = 0, MSDA_BF16 = 1 } msda_dtype;
+
+/* Sizes of one call, in the pages' notation. */
+typedef struct {
+    int64_t batch;       /* B */
+    int64_t num_keys;    /* S: rows of the flattened pyramid */
+    int64_t num_heads;   /* M */
+    int64_t head_dim;    /* D: channels per head */
+    int64_t num_levels;  /* L */
+    int64_t num_queries; /* Q */
+    int64_t num_points;  /* K: sampling points per level */
+} msda_dims;
+
+/*
+ * Forward: out = MSDA(value, spatial_shapes, level_start_index,
+ * sampling_locations, attention_weights).  Accumulates in fp32 and rounds
+ * once to `dtype` (round to nearest even for BF16).  Deterministic: the
+ * same inputs give bit-identical outputs.  Q = 0 or B = 0 enqueues nothing.
+ */
+msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
+                         const int64_t *level_start_index, const void *sampling_locations,
+                         const void *attention_weights, void *out, const msda_dims *dims,
+                         msda_dtype dtype, void *stream);
+
+/*
+ * Bytes of device workspace msda_backward needs for this dtype /
+ * accumulator pair: B*S*M*D*4 for BF16 data with an FP32 accumulator, 0
+ * otherwise.  Returns 0 for a NULL dims pointer.
+ */
+size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                     msda_dtype accum_dtype);
+
+/*
+ * Backward of <out, grad_out>.  Writes (overwrites) all three gradients:
+ *   grad_value[b, row, m, :] = sum over the samples whose bilinear corner is
+ *                              `row` of A * corner_weight * grad_out[b,q,m,:]
+ *                              (zero for rows no sample touches);
+ *   grad_loc                 = d<out, grad_out> / d sampling_locations;
+ *   grad_attn                = d<out, grad_out> / d attention_weights.
+ * On a cell edge (an integer pixel coordinate) grad_loc is the derivative
+ * from the right, the side floor() assigns the point to.
+ * grad_value is accumulated with device-scope relaxed atomics, so its last
+ * bits depend on the order the hardware applies them; grad_loc and grad_attn
+ * are deterministic.
+ * accum_dtype selects the grad_value accumulator:
+ *   FP32 data:  accum must be FP32 (native fp32 atomics into grad_value).
+ *   BF16 data:  FP32 -> atomics into `workspace` (fp32, at least
+ *               msda_backward_workspace_bytes() bytes, 16-byte aligned), then
+ *               one rounding to bf16;  BF16 -> packed-bf16 atomics straight
+ *               into grad_value (every partial sum is rounded to bf16).
+ * workspace may be NULL when no workspace is needed.
+ */
+msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
+                          const int64_t *level_start_index, const void *sampling_locations,
+                          const void *attention_weights, const void *grad_out, void *grad_value,
+                          void *grad_loc, void *grad_attn, const msda_dims *dims,
+                          msda_dtype dtype, msda_dtype accum_dtype, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *msda_status_string(msda_status status);
+
+/* Thread-local detail of this thread's last non-OK return ("" if none). */
+const char *msda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

@@ -75,7 +75,13 @@ class Oracle:
         lib.msda_oracle_forward.restype = None
         lib.msda_oracle_backward.argtypes = common + [_f64p, _f64p, _f64p, _f64p] + dims
         lib.msda_oracle_backward.restype = None
+        lib.msda_oracle_threads.argtypes = []
+        lib.msda_oracle_threads.restype = ctypes.c_int
         self._lib = lib
+
+    def threads(self) -> int:
+        """OpenMP threads the oracle's loops run on."""
+        return int(self._lib.msda_oracle_threads())
 
     def forward(self, value, spatial_shapes, level_start_index, sampling_locations,
                 attention_weights):

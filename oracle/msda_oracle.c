@@ -37,8 +37,12 @@
  * other expression is fused either.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
+
+/* Threads the oracle's parallel loops use (reported beside its timings). */
+int msda_oracle_threads(void) { return omp_get_max_threads(); }
 
 /* Geometry of one bilinear sample at one pyramid level. */
 typedef struct {

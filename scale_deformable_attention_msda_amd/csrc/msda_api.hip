@@ -1,0 +1,262 @@
+// C ABI of the MSDA library: argument validation, batch chunking and dispatch.
+// Every check runs on the host before anything is enqueued; a rejected call
+// leaves the stream untouched and records the reason for msda_last_error().
+#include "msda.h"
+#include "msda_launch.h"
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+msda_status fail(msda_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+// Byte size of one launch's value image; keeps every corner offset (and its
+// fp32-workspace double) inside 31 bits, below the "outside" sentinel.
+constexpr int64_t kMaxLaunchValueBytes = (int64_t(1) << 30) - 1;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) {
+  if (a != 0 && b > kMaxElems / a) return false;
+  *r = a * b;
+  return true;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Checked {
+  int64_t B, S, M, D, L, Q, K;
+  int64_t elt;           // bytes per element of the data dtype
+  int64_t value_elems;   // B*S*M*D
+  int64_t batch_value_elems;
+  int64_t hq_elems;      // B*Q*M
+  int64_t sample_elems;  // B*Q*M*L*K
+};
+
+msda_status check_dims(const msda_dims *d, msda_dtype dtype, Checked *c) {
+  if (!d) return fail(MSDA_ERR_NULL_POINTER, "dims is NULL");
+  if (dtype != MSDA_FP32 && dtype != MSDA_BF16)
+    return fail(MSDA_ERR_UNSUPPORTED, "dtype %d is not FP32 (0) or BF16 (1)", (int)dtype);
+  c->B = d->batch;
+  c->S = d->num_keys;
+  c->M = d->num_heads;
+  c->D = d->head_dim;
+  c->L = d->num_levels;
+  c->Q = d->num_queries;
+  c->K = d->num_points;
+  if (c->B < 0 || c->Q < 0)
+    return fail(MSDA_ERR_INVALID_DIMS, "batch (%lld) and num_queries (%lld) must be >= 0",
+                (long long)c->B, (long long)c->Q);
+  if (c->S < 1 || c->M < 1)
+    return fail(MSDA_ERR_INVALID_DIMS, "num_keys (%lld) and num_heads (%lld) must be >= 1",
+                (long long)c->S, (long long)c->M);
+  if (c->L < 1 || c->K < 1)
+    return fail(MSDA_ERR_INVALID_DIMS, "num_levels (%lld) and num_points (%lld) must be >= 1",
+                (long long)c->L, (long long)c->K);
+  if (c->D != 8 && c->D != 16 && c->D != 32 && c->D != 64)
+    return fail(MSDA_ERR_UNSUPPORTED, "head_dim %lld not in {8, 16, 32, 64}", (long long)c->D);
+  if (c->L > 16 || c->K > 32 || c->L * c->K > 64)
+    return fail(MSDA_ERR_UNSUPPORTED,
+                "num_levels %lld / num_points %lld outside L <= 16, K <= 32, L*K <= 64",
+                (long long)c->L, (long long)c->K);
+  c->elt = dtype == MSDA_FP32 ? 4 : 2;
+  int64_t sm, smd, bq, bqm, lk;
+  if (!mul_ok(c->S, c->M, &sm) || !mul_ok(sm, c->D, &smd) ||
+      !mul_ok(smd, c->B, &c->value_elems) || !mul_ok(c->B, c->Q, &bq) ||
+      !mul_ok(bq, c->M, &bqm) || !mul_ok(c->L, c->K, &lk) ||
+      !mul_ok(bqm, lk * 2, &c->sample_elems))
+    return fail(MSDA_ERR_INVALID_DIMS, "element counts overflow 2^62");
+  c->sample_elems /= 2;
+  c->batch_value_elems = smd;
+  c->hq_elems = bqm;
+  if (smd * c->elt > kMaxLaunchValueBytes)
+    return fail(MSDA_ERR_UNSUPPORTED,
+                "one batch image of value is %lld bytes; at most 2^30 - 1 are supported",
+                (long long)(smd * c->elt));
+  return MSDA_OK;
+}
+
+msda_status check_ptr(const void *p, const char *name, bool needed, uintptr_t align) {
+  if (!needed) return MSDA_OK;
+  if (!p) return fail(MSDA_ERR_NULL_POINTER, "%s is NULL", name);
+  if (!aligned(p, align))
+    return fail(MSDA_ERR_MISALIGNED, "%s is not %u-byte aligned", name, (unsigned)align);
+  return MSDA_OK;
+}
+
+#define MSDA_TRY(expr)                     \
+  do {                                     \
+    msda_status _s = (expr);               \
+    if (_s != MSDA_OK) return _s;          \
+  } while (0)
+
+// Batches per launch so that one launch's value image stays below 2^30 bytes.
+int64_t batches_per_launch(const Checked &c) {
+  const int64_t per = c.batch_value_elems * c.elt;
+  int64_t nb = kMaxLaunchValueBytes / per;
+  return nb < 1 ? 1 : nb;
+}
+
+msda::LaunchArgs chunk_args(const Checked &c, int64_t b0, int64_t nb, int64_t acc_elt,
+                            const void *value, const int64_t *shapes, const int64_t *starts,
+                            const void *loc, const void *attn) {
+  msda::LaunchArgs a{};
+  const int64_t per_hq = c.Q * c.M;
+  a.value = static_cast<const char *>(value) + b0 * c.batch_value_elems * c.elt;
+  a.shapes = shapes;
+  a.starts = starts;
+  a.loc = static_cast<const char *>(loc) + b0 * per_hq * c.L * c.K * 2 * c.elt;
+  a.attn = static_cast<const char *>(attn) + b0 * per_hq * c.L * c.K * c.elt;
+  a.nb = nb;
+  a.S = c.S;
+  a.M = c.M;
+  a.D = c.D;
+  a.L = c.L;
+  a.Q = c.Q;
+  a.K = c.K;
+  a.value_bytes = (uint32_t)(nb * c.batch_value_elems * c.elt);
+  a.acc_bytes = (uint32_t)(nb * c.batch_value_elems * acc_elt);
+  return a;
+}
+
+msda_status hip_fail(hipError_t e, const char *what) {
+  return fail(MSDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
+                         const int64_t *level_start_index, const void *sampling_locations,
+                         const void *attention_weights, void *out, const msda_dims *dims,
+                         msda_dtype dtype, void *stream) {
+  g_last_error[0] = '\0';
+  Checked c;
+  MSDA_TRY(check_dims(dims, dtype, &c));
+  const bool work = c.hq_elems > 0;
+  MSDA_TRY(check_ptr(value, "value", true, 16));
+  MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
+  MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
+  MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
+  MSDA_TRY(check_ptr(attention_weights, "attention_weights", work, 16));
+  MSDA_TRY(check_ptr(out, "out", work, 16));
+  if (!work) return MSDA_OK;
+  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t step = batches_per_launch(c);
+  for (int64_t b0 = 0; b0 < c.B; b0 += step) {
+    const int64_t nb = c.B - b0 < step ? c.B - b0 : step;
+    msda::LaunchArgs a = chunk_args(c, b0, nb, c.elt, value, spatial_shapes, level_start_index,
+                                    sampling_locations, attention_weights);
+    a.out = static_cast<char *>(out) + b0 * c.Q * c.M * c.D * c.elt;
+    hipError_t e = msda::launch_forward(a, dt, s);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
+  return MSDA_OK;
+}
+
+size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                     msda_dtype accum_dtype) {
+  if (!dims || dtype != MSDA_BF16 || accum_dtype != MSDA_FP32) return 0;
+  int64_t n = 0;
+  if (dims->batch < 0 || dims->num_keys < 0 || dims->num_heads < 0 || dims->head_dim < 0) return 0;
+  if (!mul_ok(dims->batch, dims->num_keys, &n) || !mul_ok(n, dims->num_heads, &n) ||
+      !mul_ok(n, dims->head_dim, &n) || !mul_ok(n, 4, &n))
+    return 0;
+  return (size_t)n;
+}
+
+msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
+                          const int64_t *level_start_index, const void *sampling_locations,
+                          const void *attention_weights, const void *grad_out, void *grad_value,
+                          void *grad_loc, void *grad_attn, const msda_dims *dims,
+                          msda_dtype dtype, msda_dtype accum_dtype, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  Checked c;
+  MSDA_TRY(check_dims(dims, dtype, &c));
+  if (accum_dtype != MSDA_FP32 && accum_dtype != MSDA_BF16)
+    return fail(MSDA_ERR_UNSUPPORTED, "accum_dtype %d is not FP32 (0) or BF16 (1)",
+                (int)accum_dtype);
+  if (dtype == MSDA_FP32 && accum_dtype != MSDA_FP32)
+    return fail(MSDA_ERR_UNSUPPORTED, "FP32 data needs an FP32 accumulator");
+  const bool work = c.hq_elems > 0;
+  const bool use_ws = dtype == MSDA_BF16 && accum_dtype == MSDA_FP32 && work;
+  MSDA_TRY(check_ptr(value, "value", true, 16));
+  MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
+  MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
+  MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
+  MSDA_TRY(check_ptr(attention_weights, "attention_weights", work, 16));
+  MSDA_TRY(check_ptr(grad_out, "grad_out", work, 16));
+  MSDA_TRY(check_ptr(grad_value, "grad_value", c.value_elems > 0, 16));
+  MSDA_TRY(check_ptr(grad_loc, "grad_loc", work, 16));
+  MSDA_TRY(check_ptr(grad_attn, "grad_attn", work, 16));
+  if (use_ws) {
+    const size_t need = (size_t)c.value_elems * 4;
+    if (!workspace || workspace_bytes < need)
+      return fail(MSDA_ERR_WORKSPACE, "BF16 data with an FP32 accumulator needs %zu bytes of "
+                  "workspace, got %zu%s", need, workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c.value_elems == 0) return MSDA_OK;
+  hipError_t e;
+  if (!work || !use_ws) {
+    e = msda::launch_zero(grad_value, (size_t)(c.value_elems * c.elt), s);
+    if (e != hipSuccess) return hip_fail(e, "grad_value zero-fill launch");
+    if (!work) return MSDA_OK;
+  } else {
+    e = msda::launch_zero(workspace, (size_t)c.value_elems * 4, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace zero-fill launch");
+  }
+  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const auto acc = accum_dtype == MSDA_FP32 ? msda::Accum::F32 : msda::Accum::BF16;
+  const int64_t acc_elt = accum_dtype == MSDA_FP32 ? 4 : 2;
+  char *acc_base = static_cast<char *>(use_ws ? workspace : grad_value);
+  const int64_t step = batches_per_launch(c);
+  for (int64_t b0 = 0; b0 < c.B; b0 += step) {
+    const int64_t nb = c.B - b0 < step ? c.B - b0 : step;
+    msda::LaunchArgs a = chunk_args(c, b0, nb, acc_elt, value, spatial_shapes, level_start_index,
+                                    sampling_locations, attention_weights);
+    const int64_t samples0 = b0 * c.Q * c.M * c.L * c.K;
+    a.grad_out = static_cast<const char *>(grad_out) + b0 * c.Q * c.M * c.D * c.elt;
+    a.grad_acc = acc_base + b0 * c.batch_value_elems * acc_elt;
+    a.grad_loc = static_cast<char *>(grad_loc) + samples0 * 2 * c.elt;
+    a.grad_attn = static_cast<char *>(grad_attn) + samples0 * c.elt;
+    e = msda::launch_backward(a, dt, acc, s);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+  }
+  if (use_ws) {
+    e = msda::launch_cast_f32_to_bf16(static_cast<const float *>(workspace), grad_value,
+                                      (size_t)c.value_elems, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace cast launch");
+  }
+  return MSDA_OK;
+}
+
+const char *msda_status_string(msda_status status) {
+  switch (status) {
+    case MSDA_OK: return "MSDA_OK";
+    case MSDA_ERR_NULL_POINTER: return "MSDA_ERR_NULL_POINTER: a required pointer is NULL";
+    case MSDA_ERR_INVALID_DIMS: return "MSDA_ERR_INVALID_DIMS: sizes are negative, zero or overflow";
+    case MSDA_ERR_UNSUPPORTED: return "MSDA_ERR_UNSUPPORTED: dtype or size outside the supported set";
+    case MSDA_ERR_MISALIGNED: return "MSDA_ERR_MISALIGNED: a pointer is not aligned as required";
+    case MSDA_ERR_WORKSPACE: return "MSDA_ERR_WORKSPACE: workspace missing or too small";
+    case MSDA_ERR_HIP: return "MSDA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown msda_status";
+}
+
+const char *msda_last_error(void) { return g_last_error; }
+
+}  // extern "C"

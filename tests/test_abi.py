@@ -1,0 +1,112 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/msda.h
+declares, and rejects bad arguments with a status code before any launch.
+No call here reaches a kernel, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scale_deformable_attention_msda_amd as msda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msda.LIB_PATH):
+        from scale_deformable_attention_msda_amd import build
+        build.build()
+    return msda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("msda_forward", "msda_backward", "msda_backward_workspace_bytes",
+              "msda_status_string", "msda_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert msda.msda_status_string(code).startswith("MSDA_")
+    assert "unknown" in msda.msda_status_string(99)
+
+
+def dims(B=1, S=80, M=2, D=8, L=2, Q=16, K=2):
+    return msda.MsdaDims(B, S, M, D, L, Q, K)
+
+
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced by a rejected call
+
+
+def fwd(lib, d, dtype=0, value=FAKE, shapes=FAKE, starts=FAKE, loc=FAKE, attn=FAKE, out=FAKE):
+    return lib.msda_forward(value, shapes, starts, loc, attn, out,
+                            None if d is None else ctypes.byref(d), dtype, None)
+
+
+def bwd(lib, d, dtype=0, acc=0, ws=None, ws_bytes=0, **p):
+    v = {k: p.get(k, FAKE) for k in ("value", "shapes", "starts", "loc", "attn", "gout", "gv",
+                                     "gl", "ga")}
+    return lib.msda_backward(v["value"], v["shapes"], v["starts"], v["loc"], v["attn"], v["gout"],
+                             v["gv"], v["gl"], v["ga"], None if d is None else ctypes.byref(d),
+                             dtype, acc, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(D=12), 3), (dict(D=128), 3), (dict(L=0), 2), (dict(K=0), 2), (dict(L=17), 3),
+    (dict(K=33), 3), (dict(L=8, K=9), 3), (dict(B=-1), 2), (dict(Q=-1), 2), (dict(S=0), 2),
+    (dict(M=0), 2), (dict(S=1 << 58, M=8, D=64), 2), (dict(S=1 << 22, M=16, D=64), 3),
+])
+def test_forward_rejects_bad_dims(lib, kwargs, code):
+    assert fwd(lib, dims(**kwargs)) == code
+    assert msda.msda_last_error() != ""
+
+
+def test_forward_rejects_bad_pointers_and_dtype(lib):
+    assert fwd(lib, None) == 1
+    assert fwd(lib, dims(), value=None) == 1
+    assert fwd(lib, dims(), out=None) == 1
+    assert fwd(lib, dims(), loc=FAKE + 4) == 4
+    assert fwd(lib, dims(), value=FAKE + 8) == 4
+    assert fwd(lib, dims(), dtype=2) == 3
+    assert "dtype" in msda.msda_last_error()
+
+
+def test_empty_forward_is_ok_without_launch(lib):
+    # Q = 0: nothing to compute, the optional pointers may be NULL
+    assert fwd(lib, dims(Q=0), loc=None, attn=None, out=None) == 0
+    assert fwd(lib, dims(B=0), loc=None, attn=None, out=None) == 0
+
+
+def test_backward_rejections(lib):
+    assert bwd(lib, dims(), dtype=0, acc=1) == 3            # fp32 data needs fp32 accum
+    assert bwd(lib, dims(), dtype=1, acc=0) == 5            # bf16 + fp32 accum needs workspace
+    need = lib.msda_backward_workspace_bytes(ctypes.byref(dims()), 1, 0)
+    assert need == 1 * 80 * 2 * 8 * 4
+    assert bwd(lib, dims(), dtype=1, acc=0, ws=FAKE, ws_bytes=need - 1) == 5
+    assert bwd(lib, dims(), dtype=1, acc=0, ws=FAKE + 4, ws_bytes=need) == 4
+    assert bwd(lib, dims(), gv=None) == 1
+    assert bwd(lib, dims(), acc=7) == 3
+    assert lib.msda_backward_workspace_bytes(ctypes.byref(dims()), 0, 0) == 0
+    assert lib.msda_backward_workspace_bytes(ctypes.byref(dims()), 1, 1) == 0
+    assert lib.msda_backward_workspace_bytes(None, 1, 0) == 0
+
+
+def test_last_error_is_cleared_by_a_good_call(lib):
+    assert fwd(lib, dims(D=12)) == 3
+    assert msda.msda_last_error() != ""
+    assert fwd(lib, dims(Q=0), loc=None, attn=None, out=None) == 0
+    assert msda.msda_last_error() == ""

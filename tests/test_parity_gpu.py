@@ -1,0 +1,166 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by
+element, on the same seeded inputs."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+import workloads
+from parity import TOL_BF16, TOL_BWD_FP32, TOL_FWD_FP32, check, say
+
+import scale_deformable_attention_msda_amd as msda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    msda.load_library()  # raises if the library is not built
+
+
+def gate(x, g, o, accum_bf16=False):
+    if x["dtype"] == "fp32":
+        check("out", g["out"], o["out"], *TOL_FWD_FP32)
+        check("grad_value", g["grad_value"], o["grad_value"], *TOL_BWD_FP32)
+        check("grad_loc", g["grad_loc"], o["grad_loc"], *TOL_BWD_FP32)
+        check("grad_attn", g["grad_attn"], o["grad_attn"], *TOL_BWD_FP32)
+    else:
+        check("out", g["out"], o["out"], *TOL_BF16)
+        check("grad_loc", g["grad_loc"], o["grad_loc"], *TOL_BF16)
+        check("grad_attn", g["grad_attn"], o["grad_attn"], *TOL_BF16)
+        if accum_bf16:
+            say(f"  grad_value (packed-bf16 accumulator, reported): "
+                f"{parity.error_stats(g['grad_value'], o['grad_value'])}")
+        else:
+            check("grad_value", g["grad_value"], o["grad_value"], *TOL_BF16)
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
+def test_workload(wid):
+    wl = workloads.WORKLOADS[wid]
+    say(f"[parity] workload {wid} {wl.name} B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
+        f"L={wl.L} K={wl.K} {wl.dtype}")
+    x = workloads.make_inputs(wid)
+    o = parity.run_oracle(x)
+    g = parity.run_gpu(x)
+    gate(x, g, o)
+    if wl.dtype == "bf16":
+        say("  accumulator bf16:")
+        gate(x, parity.run_gpu(x, accum=torch.bfloat16), o, accum_bf16=True)
+
+
+EDGE = {
+    # several blocks and a ragged last block (B*Q*M not a multiple of any block size)
+    "ragged_fp32": workloads.custom(3, 37, 3, 32, ((7, 9), (4, 5), (1, 3)), 3),
+    "ragged_bf16": workloads.custom(3, 37, 3, 32, ((7, 9), (4, 5), (1, 3)), 3, dtype="bf16"),
+    "d8_fp32": workloads.custom(2, 50, 4, 8, ((9, 11), (5, 6)), 4),
+    "d16_fp32": workloads.custom(2, 50, 4, 16, ((9, 11), (5, 6)), 4),
+    "d64_fp32": workloads.custom(2, 50, 4, 64, ((9, 11), (5, 6)), 4),
+    "d8_bf16": workloads.custom(2, 50, 4, 8, ((9, 11), (5, 6)), 4, dtype="bf16"),
+    "d16_bf16": workloads.custom(2, 50, 4, 16, ((9, 11), (5, 6)), 4, dtype="bf16"),
+    "d64_bf16": workloads.custom(2, 50, 4, 64, ((9, 11), (5, 6)), 4, dtype="bf16"),
+    "one_level_one_point": workloads.custom(2, 33, 5, 32, ((6, 10),), 1),
+    "max_lk_16_levels": workloads.custom(1, 21, 3, 16, tuple((2 + i % 5, 3 + i % 4) for i in range(16)), 4),
+    "max_lk_32_points": workloads.custom(1, 21, 3, 32, ((8, 8), (4, 4)), 32),
+    "single_pixel_levels": workloads.custom(2, 19, 2, 32, ((1, 1), (1, 2), (2, 1)), 2, sigma_px=1.0),
+    "wide_offsets": workloads.custom(2, 40, 4, 32, ((12, 20), (6, 10)), 4, sigma_px=8.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge(name):
+    wl = EDGE[name]
+    say(f"[parity] edge {name}: B={wl.B} Q={wl.Q} M={wl.M} D={wl.D} L={wl.L} K={wl.K} {wl.dtype}")
+    x = workloads.make_inputs(wl, seed=zlib.crc32(name.encode()) % 100000)
+    o = parity.run_oracle(x)
+    gate(x, parity.run_gpu(x), o)
+    if wl.dtype == "bf16":
+        gate(x, parity.run_gpu(x, accum=torch.bfloat16), o, accum_bf16=True)
+
+
+def special_locations():
+    """Boundary and non-finite coordinates on power-of-two levels (exact x, y)."""
+    wl = workloads.custom(1, 12, 2, 32, ((8, 16), (4, 4)), 4)
+    x = workloads.make_inputs(wl, seed=7)
+    loc = x["sampling_locations"]
+    W0, H0 = 16, 8
+    cases = [
+        (-0.5 / W0, 0.5),             # x = -1 exactly: forward 0, gradient non-zero
+        (-1.5 / W0, 0.5),             # x = -2: wholly outside
+        (1.0 + 0.5 / W0, 0.5),        # x = W exactly: wholly outside
+        ((W0 - 0.5) / W0, 0.5),       # x = W - 1 exactly (last column centre)
+        (0.5, -0.5 / H0),             # y = -1 exactly
+        (0.5, 1.0 + 0.5 / H0),        # y = H exactly
+        (0.0, 0.0),                   # corner of the map: x = y = -0.5
+        (1.0, 1.0),                   # x = W - 0.5, y = H - 0.5
+        (math.nan, 0.5), (0.5, math.nan), (math.inf, 0.5), (0.5, -math.inf),
+        (1e30, 0.5), (-1e30, -1e30), (3.0, 0.5), (0.5, 3.0),
+    ]
+    q = 0
+    for i, (u, v) in enumerate(cases):
+        qq, m, k = (i // 4) % 12, i % 2, i % 4
+        loc[0, qq, m, 0, k, 0] = u
+        loc[0, qq, m, 0, k, 1] = v
+        q = max(q, qq)
+    return x
+
+
+def test_boundary_and_nonfinite_locations():
+    say("[parity] boundary and non-finite locations")
+    x = special_locations()
+    o = parity.run_oracle(x)
+    g = parity.run_gpu(x)
+    for k in g:
+        assert np.all(np.isfinite(g[k])), k
+    gate(x, g, o)
+
+
+def test_empty_queries_zero_grad_value():
+    say("[parity] Q = 0: forward is a no-op, backward zero-fills grad_value")
+    wl = workloads.custom(2, 0, 2, 32, ((4, 4), (2, 2)), 2)
+    x = workloads.make_inputs(wl, seed=1)
+    t = parity.upload(x)
+    out = msda.msda_forward(*parity.operands(t))
+    assert out.shape == (2, 0, 64)
+    gv = torch.full_like(t["value"], float("nan"))
+    gv, gl, ga = msda.msda_backward(*parity.operands(t), t["grad_out"], grad_value=gv)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gv).item() == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_outputs_are_overwritten_and_deterministic(dtype):
+    say(f"[parity] overwrite + determinism {dtype}")
+    wl = workloads.custom(2, 45, 8, 32, workloads.PYRAMID_DETR, 4, dtype=dtype)
+    x = workloads.make_inputs(wl, seed=11)
+    t = parity.upload(x)
+    ops = parity.operands(t)
+    junk = lambda like: torch.full_like(like, float("nan"))
+    out1 = msda.msda_forward(*ops, out=junk(t["grad_out"]))
+    out2 = msda.msda_forward(*ops)
+    gv1, gl1, ga1 = msda.msda_backward(*ops, t["grad_out"], grad_value=junk(t["value"]),
+                                       grad_loc=junk(t["sampling_locations"]),
+                                       grad_attn=junk(t["attention_weights"]))
+    gv2, gl2, ga2 = msda.msda_backward(*ops, t["grad_out"])
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "forward must be bit-identical across runs"
+    assert torch.equal(gl1, gl2) and torch.equal(ga1, ga2)
+    for v in (out1, gv1, gl1, ga1):
+        assert torch.isfinite(v).all()
+    o = parity.run_oracle(x)
+    gate(x, {k: v.double().cpu().numpy() for k, v in
+             dict(out=out1, grad_value=gv1, grad_loc=gl1, grad_attn=ga1).items()}, o)
+
+
+def test_side_stream():
+    say("[parity] non-default stream")
+    x = workloads.make_inputs(1)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = parity.run_gpu(x, stream=s)
+    gate(x, g, parity.run_oracle(x))

@@ -98,12 +98,14 @@ def level_start_index(shapes) -> np.ndarray:
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); return float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    bias = ((bits >> 16) & 1) + 0x7FFF
-    rounded = ((bits + bias) & 0xFFFF0000).astype(np.uint32)
+    bits = x.view(np.uint32)
+    # finite values never carry out of the top bit here; NaNs are restored below
+    rounded = (bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))))
+    rounded &= np.uint32(0xFFFF0000)
+    out = rounded.view(np.float32)
     nan = np.isnan(x)
-    out = rounded.view(np.float32).copy()
-    out[nan] = np.float32(np.nan)
+    if nan.any():
+        out[nan] = np.float32(np.nan)
     return out
 
 
