@@ -40,24 +40,33 @@ def log(*a):
 
 
 def bytes_model(wl: workloads.Workload) -> dict:
-    """Algorithmic (compulsory) HBM bytes per call, each tensor counted once.
+    """Algorithmic (compulsory) HBM bytes per launch of each kernel, each tensor once.
 
     For the encoder workloads every pyramid pixel is the reference point of a
     query and offsets are a few pixels, so every value row is touched and the
-    whole value tensor counts."""
+    whole value tensor counts.  Per-sample figures: loc 2 elements, attn 1
+    element, a 4-byte sample id for the binned path."""
     elt = 4 if wl.dtype == "fp32" else 2
     B, S, Q, M, D, L, K = wl.B, wl.S, wl.num_queries, wl.M, wl.D, wl.L, wl.K
+    n = B * Q * M * L * K
     value = B * S * M * D * elt
-    loc = B * Q * M * L * K * 2 * elt
-    attn = B * Q * M * L * K * elt
+    loc = n * 2 * elt
+    attn = n * elt
     out = B * Q * M * D * elt
+    ids = n * 4
     return {
-        "samples": B * Q * M * L * K,
+        "samples": n,
+        # forward: gather value, read loc / attn, write out
         "fwd": value + loc + attn + out,
-        # the scatter kernel: value, loc, attn, grad_out read once; grad_value,
-        # grad_loc, grad_attn written once
-        "bwd_kernel": value + loc + attn + out + value + loc + attn,
-        "zero_fill": value,
+        # atomic backward: value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written
+        "bwd_atomic": value + loc + attn + out + value + loc + attn,
+        "zero": value,
+        # binned passes
+        "bin_count": loc,
+        "bin_scatter": loc + ids,
+        "bin_tile": value + ids + loc + attn + out + value + loc + attn,
+        "bin_merge": 0,
+        "bin_plan": 0,
         "value": value,
     }
 
@@ -96,6 +105,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload id in workloads.py")
     ap.add_argument("--rotate", type=int, default=4, help="input batches cycled over")
+    ap.add_argument("--scatter", default="binned", choices=["binned", "atomic"],
+                    help="how the backward forms grad_value")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -130,84 +141,69 @@ def main(argv=None) -> int:
         t["level_start_index"] = torch.from_numpy(x["level_start_index"]).to(dev)
         batches.append(t)
     t0 = batches[0]
+    shapes_host = host[0]["spatial_shapes"]
     out = torch.empty_like(t0["grad_out"])
     gv = torch.empty_like(t0["value"])
     gl = torch.empty_like(t0["sampling_locations"])
     ga = torch.empty_like(t0["attention_weights"])
-    ws = None
     dims = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
-    need = msda.msda_backward_workspace_bytes(dims, 0 if wl.dtype == "fp32" else 1, 0)
-    if need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    sc = msda.MSDA_SCATTER_BINNED if args.scatter == "binned" else msda.MSDA_SCATTER_ATOMIC
+    need = msda.msda_backward_workspace_bytes(dims, 0 if wl.dtype == "fp32" else 1,
+                                              msda.MSDA_FP32, sc, shapes_host)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    log(f"[bench] scatter={args.scatter}, workspace {need / 2**20:.1f} MiB")
 
     def ops(t):
         return (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"],
                 t["attention_weights"])
 
-    def step(i, ev=None):
+    def step(i):
         t = batches[i % len(batches)]
-        if ev is not None:
-            ev[0].record(stream)
         msda.msda_forward(*ops(t), out=out, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         msda.msda_backward(*ops(t), t["grad_out"], grad_value=gv, grad_loc=gl, grad_attn=ga,
+                           scatter=args.scatter, spatial_shapes_host=shapes_host,
                            workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region: K steps, every library kernel bracketed by HIP events on `stream`
+    msda.msda_profile_start(64 * args.steps)
     w0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-
-    # zero-fill alone: a backward call with no queries only zero-fills grad_value
-    fill_ms = []
-    empty = {k: v for k, v in t0.items()}
-    empty["sampling_locations"] = t0["sampling_locations"][:, :0]
-    empty["attention_weights"] = t0["attention_weights"][:, :0]
-    empty["grad_out"] = t0["grad_out"][:, :0]
-    for i in range(args.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record(stream)
-        msda.msda_backward(*ops(empty), empty["grad_out"], grad_value=gv,
-                           grad_loc=gl[:, :0], grad_attn=ga[:, :0], workspace=ws, stream=stream)
-        e[1].record(stream)
-        fill_ms.append(e)
-    torch.cuda.synchronize()
-    fill_ms = np.array([e[0].elapsed_time(e[1]) for e in fill_ms])
+    records = msda.msda_profile_stop(64 * args.steps)
 
     bm = bytes_model(wl)
-    fwd_us = float(np.mean(fwd_ms)) * 1e3
-    bwd_us = float(np.mean(bwd_ms)) * 1e3
-    fill_us = float(np.mean(fill_ms)) * 1e3
-    scatter_us = max(bwd_us - fill_us, 1e-3)
+    per_kernel = {}
+    for name, ms in records:
+        per_kernel.setdefault(name, []).append(ms)
+    kernels = {}
+    for name, v in per_kernel.items():
+        us = float(np.mean(v)) * 1e3
+        launches_per_step = len(v) / args.steps
+        nbytes = bm.get(name, 0)
+        kernels[name] = {"us": round(us, 3), "launches_per_step": launches_per_step,
+                         "alg_bytes": nbytes,
+                         "gbps": round(nbytes / (us * 1e-6) / 1e9, 1) if nbytes else None}
+    fwd_us = sum(k["us"] * k["launches_per_step"] for n, k in kernels.items() if n == "fwd")
+    bwd_us = sum(k["us"] * k["launches_per_step"] for n, k in kernels.items() if n != "fwd")
     ms_per_step = wall / args.steps * 1e3
-    kernels = {
-        "fwd": {"us": fwd_us, "bytes": bm["fwd"]},
-        "bwd": {"us": scatter_us, "bytes": bm["bwd_kernel"]},
-    }
-    dom_name = max(kernels, key=lambda k: kernels[k]["us"])
+    dom_name = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"])
     dom = kernels[dom_name]
-    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    achieved = dom["alg_bytes"] / (dom["us"] * 1e-6) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            rec = tj.get(f"{wl.name}/{dom_name}")
+            rec = tj.get(f"{wl.name}/{args.scatter}/{dom_name}")
             if rec and rec.get("valid", False):
                 traffic = rec["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
-    fwdbwd_gbps = (bm["fwd"] + bm["bwd_kernel"] + bm["zero_fill"]) / (ms_per_step * 1e-3) / 1e9
+    step_bytes = bm["fwd"] + (bm["bwd_atomic"] if args.scatter == "atomic" else bm["bin_tile"])
     res = {
         "metric": METRIC,
         "value": round(ms_per_step * 1e3, 3),
@@ -223,17 +219,15 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.B} Q=S={wl.num_queries} M={wl.M} D={wl.D} "
                                f"L={wl.L} (" + ", ".join(f"{h}x{w}" for h, w in wl.shapes) +
-                               f") K={wl.K} {wl.dtype}, fwd+bwd",
-                   "rotate": args.rotate},
+                               f") K={wl.K} {wl.dtype}, forward + backward",
+                   "scatter": args.scatter, "rotate": args.rotate},
         "fwd_us": round(fwd_us, 3),
         "bwd_us": round(bwd_us, 3),
-        "bwd_zero_fill_us": round(fill_us, 3),
-        "bwd_kernel_us": round(scatter_us, 3),
-        "queries_per_s": wl.B * wl.num_queries / (ms_per_step * 1e-3),
+        "kernels": kernels,
+        "queries_per_s": round(wl.B * wl.num_queries / (ms_per_step * 1e-3), 1),
         "fwd_hbm_gbps": round(bm["fwd"] / (fwd_us * 1e-6) / 1e9, 1),
         "fwd_hbm_frac": round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-        "bwd_hbm_gbps": round(bm["bwd_kernel"] / (scatter_us * 1e-6) / 1e9, 1),
-        "fwdbwd_hbm_gbps": round(fwdbwd_gbps, 1),
+        "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},

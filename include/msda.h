@@ -104,13 +104,32 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          const void *attention_weights, void *out, const msda_dims *dims,
                          msda_dtype dtype, void *stream);
 
+/* How msda_backward forms grad_value. */
+typedef enum {
+    /* Samples are counting-sorted by destination tile (batch, head, level,
+     * 8x8 pixels); one block per tile accumulates its grad_value rows in LDS
+     * and stores each row once.  No floating-point global atomics; needs a
+     * workspace and a host copy of spatial_shapes.  fp32 accumulation. */
+    MSDA_SCATTER_BINNED = 0,
+    /* Each sample adds A * w_c * grad_out into its four corner rows with
+     * device-scope atomics (fp32, or packed bf16 for BF16 data). */
+    MSDA_SCATTER_ATOMIC = 1
+} msda_scatter;
+
 /*
- * Bytes of device workspace msda_backward needs for this dtype /
- * accumulator pair: B*S*M*D*4 for BF16 data with an FP32 accumulator, 0
- * otherwise.  Returns 0 for a NULL dims pointer.
+ * Bytes of device workspace msda_backward needs for these sizes, dtype,
+ * accumulator and scatter:
+ *   BINNED:            bin tables, sorted sample ids and tile-rim partials
+ *                      (planned from spatial_shapes_host, [L,2] on the host);
+ *   ATOMIC, BF16 data,
+ *   FP32 accumulator:  B*S*M*D*4 (the fp32 accumulator);
+ *   otherwise          0.
+ * Returns SIZE_MAX when the arguments would be rejected by msda_backward
+ * (msda_last_error() then says why).
  */
 size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
-                                     msda_dtype accum_dtype);
+                                     msda_dtype accum_dtype, msda_scatter scatter,
+                                     const int64_t *spatial_shapes_host);
 
 /*
  * Backward of <out, grad_out>.  Writes (overwrites) all three gradients:
@@ -120,24 +139,49 @@ size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
  *   grad_loc                 = d<out, grad_out> / d sampling_locations;
  *   grad_attn                = d<out, grad_out> / d attention_weights.
  * On a cell edge (an integer pixel coordinate) grad_loc is the derivative
- * from the right, the side floor() assigns the point to.
- * grad_value is accumulated with device-scope relaxed atomics, so its last
- * bits depend on the order the hardware applies them; grad_loc and grad_attn
- * are deterministic.
- * accum_dtype selects the grad_value accumulator:
- *   FP32 data:  accum must be FP32 (native fp32 atomics into grad_value).
- *   BF16 data:  FP32 -> atomics into `workspace` (fp32, at least
- *               msda_backward_workspace_bytes() bytes, 16-byte aligned), then
- *               one rounding to bf16;  BF16 -> packed-bf16 atomics straight
- *               into grad_value (every partial sum is rounded to bf16).
- * workspace may be NULL when no workspace is needed.
+ * from the right, the side floor() assigns the point to.  A sample with no
+ * corner inside its level gets zero grad_loc and grad_attn.
+ * The order in which contributions reach a grad_value row is not fixed (LDS
+ * or global atomics), so its last bits may differ between runs; grad_loc and
+ * grad_attn do not depend on that order.
+ * scatter / accum_dtype:
+ *   BINNED: accum_dtype must be FP32; spatial_shapes_host ([L,2] int64 on
+ *           the host, the same values as spatial_shapes) plans the tiles.
+ *   ATOMIC: FP32 data -> accum FP32 (fp32 atomics into grad_value);
+ *           BF16 data -> accum FP32 (atomics into an fp32 workspace, then one
+ *           rounding to bf16) or accum BF16 (packed-bf16 atomics straight
+ *           into grad_value, every partial sum rounded to bf16).
+ *           spatial_shapes_host may be NULL.
+ * workspace must hold at least msda_backward_workspace_bytes() bytes
+ * (16-byte aligned; NULL when that is 0).  Its contents on entry do not
+ * matter and are clobbered.
  */
 msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           const int64_t *level_start_index, const void *sampling_locations,
                           const void *attention_weights, const void *grad_out, void *grad_value,
                           void *grad_loc, void *grad_attn, const msda_dims *dims,
-                          msda_dtype dtype, msda_dtype accum_dtype, void *workspace,
+                          msda_dtype dtype, msda_dtype accum_dtype, msda_scatter scatter,
+                          const int64_t *spatial_shapes_host, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * Kernel timing for benchmarks.  Between msda_profile_start() and
+ * msda_profile_stop() on one thread, every kernel this library enqueues from
+ * that thread is bracketed by two HIP events recorded on its stream.
+ * msda_profile_stop() waits for the last recorded event, copies at most `max`
+ * records (kernel name, milliseconds between its events) into `out`, ends the
+ * session and returns the number of kernels recorded (which may exceed `max`),
+ * or -1 when a HIP event call failed.  Records past `capacity` are dropped.
+ * The events are created by the library (host-side HIP objects, no device
+ * memory) and kept for reuse until the process ends.
+ */
+typedef struct {
+    const char *name; /* static string, e.g. "fwd_kernel<f32,32>" */
+    float ms;
+} msda_kernel_time;
+
+msda_status msda_profile_start(int capacity);
+int msda_profile_stop(msda_kernel_time *out, int max);
 
 /* Static description of a status code. */
 const char *msda_status_string(msda_status status);

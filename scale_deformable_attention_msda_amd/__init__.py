@@ -9,9 +9,11 @@ The functions keep the C names:
                  attention_weights, out=None, stream=None) -> out
     msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
                   attention_weights, grad_out, grad_value=None, grad_loc=None,
-                  grad_attn=None, accum_dtype=None, workspace=None, stream=None)
+                  grad_attn=None, accum_dtype=None, scatter="binned",
+                  spatial_shapes_host=None, workspace=None, stream=None)
                   -> (grad_value, grad_loc, grad_attn)
-    msda_backward_workspace_bytes(dims, dtype, accum_dtype) -> int
+    msda_backward_workspace_bytes(dims, dtype, accum_dtype, scatter,
+                                  spatial_shapes_host) -> int
     msda_status_string(status) -> str
     msda_last_error() -> str
 Shapes follow chapter 1 of the msda-triton course ("The equation, term by
@@ -32,7 +34,11 @@ LIB_PATH = os.path.join(_PKG, "libmsda.so")
 MSDA_OK = 0
 MSDA_FP32 = 0
 MSDA_BF16 = 1
+MSDA_SCATTER_BINNED = 0
+MSDA_SCATTER_ATOMIC = 1
 _DTYPES = {torch.float32: MSDA_FP32, torch.bfloat16: MSDA_BF16}
+_SCATTER = {"binned": MSDA_SCATTER_BINNED, "atomic": MSDA_SCATTER_ATOMIC}
+SIZE_MAX = 2 ** 64 - 1
 
 
 class MsdaDims(ctypes.Structure):
@@ -40,6 +46,10 @@ class MsdaDims(ctypes.Structure):
                 ("num_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
                 ("num_levels", ctypes.c_int64), ("num_queries", ctypes.c_int64),
                 ("num_points", ctypes.c_int64)]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
 
 
 class MsdaError(RuntimeError):
@@ -64,14 +74,19 @@ def load_library(path: str = LIB_PATH):
     lib.msda_forward.argtypes = [vp, i64p, i64p, vp, vp, vp, dims_p, ctypes.c_int, vp]
     lib.msda_forward.restype = ctypes.c_int
     lib.msda_backward.argtypes = [vp, i64p, i64p, vp, vp, vp, vp, vp, vp, dims_p, ctypes.c_int,
-                                  ctypes.c_int, vp, ctypes.c_size_t, vp]
+                                  ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
     lib.msda_backward.restype = ctypes.c_int
-    lib.msda_backward_workspace_bytes.argtypes = [dims_p, ctypes.c_int, ctypes.c_int]
+    lib.msda_backward_workspace_bytes.argtypes = [dims_p, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int, vp]
     lib.msda_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_last_error.argtypes = []
     lib.msda_last_error.restype = ctypes.c_char_p
+    lib.msda_profile_start.argtypes = [ctypes.c_int]
+    lib.msda_profile_start.restype = ctypes.c_int
+    lib.msda_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
+    lib.msda_profile_stop.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -82,6 +97,22 @@ def msda_status_string(status: int) -> str:
 
 def msda_last_error() -> str:
     return load_library().msda_last_error().decode()
+
+
+def msda_profile_start(capacity: int) -> None:
+    """Time every kernel the library enqueues from this thread (HIP events on its stream)."""
+    st = load_library().msda_profile_start(capacity)
+    if st != MSDA_OK:
+        raise MsdaError(st, "msda_profile_start")
+
+
+def msda_profile_stop(max_records: int = 1 << 16) -> list:
+    """End the session; return [(kernel name, milliseconds), ...] in launch order."""
+    buf = (KernelTime * max_records)()
+    n = load_library().msda_profile_stop(buf, max_records)
+    if n < 0:
+        raise RuntimeError("msda_profile_stop: a HIP event call failed")
+    return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(min(n, max_records))]
 
 
 def _dims_of(value: torch.Tensor, spatial_shapes: torch.Tensor,
@@ -145,25 +176,52 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
     return out
 
 
-def msda_backward_workspace_bytes(dims: MsdaDims, dtype: int, accum_dtype: int) -> int:
-    return int(load_library().msda_backward_workspace_bytes(ctypes.byref(dims), dtype,
-                                                            accum_dtype))
+def _host_shapes(spatial_shapes, spatial_shapes_host):
+    """A contiguous int64 host array of the level shapes (kept alive by the caller)."""
+    import numpy as np
+
+    if spatial_shapes_host is None:
+        spatial_shapes_host = spatial_shapes.detach().cpu()  # one device-to-host copy
+    if isinstance(spatial_shapes_host, torch.Tensor):
+        spatial_shapes_host = spatial_shapes_host.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(spatial_shapes_host, dtype=np.int64))
+
+
+def msda_backward_workspace_bytes(dims: MsdaDims, dtype: int, accum_dtype: int,
+                                  scatter: int = MSDA_SCATTER_BINNED,
+                                  spatial_shapes_host=None) -> int:
+    """Workspace bytes msda_backward needs; raises when the call would be rejected."""
+    host = None
+    if spatial_shapes_host is not None:
+        import numpy as np
+        host = np.ascontiguousarray(np.asarray(spatial_shapes_host, dtype=np.int64))
+    n = int(load_library().msda_backward_workspace_bytes(
+        ctypes.byref(dims), dtype, accum_dtype, scatter,
+        None if host is None else host.ctypes.data))
+    if n == SIZE_MAX:
+        raise ValueError(f"msda_backward_workspace_bytes: {msda_last_error()}")
+    return n
 
 
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
                   attention_weights, grad_out, grad_value=None, grad_loc=None, grad_attn=None,
-                  accum_dtype=None, workspace=None, stream=None):
+                  accum_dtype=None, scatter="binned", spatial_shapes_host=None, workspace=None,
+                  stream=None):
     """Gradients of <out, grad_out> w.r.t. value, sampling_locations, attention_weights.
 
-    accum_dtype: torch.float32 (default) or torch.bfloat16 (packed-bf16 atomics, bf16 data
-    only).  A bf16 call with an fp32 accumulator needs a workspace; one is allocated here
-    when none is given."""
+    scatter: "binned" (default; destination-sorted, LDS accumulation, fp32) or "atomic"
+    (device-scope atomics).  accum_dtype: torch.float32 (default) or torch.bfloat16
+    (atomic scatter of bf16 data only: packed-bf16 atomics).  spatial_shapes_host: the
+    level shapes on the host (array-like [L, 2]); read from spatial_shapes when omitted.
+    A workspace is allocated here when none is given."""
     dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations,
                        attention_weights)
     B, S, M, D, L, Q, K = (dims.batch, dims.num_keys, dims.num_heads, dims.head_dim,
                            dims.num_levels, dims.num_queries, dims.num_points)
     _check(grad_out, "grad_out", dt, (B, Q, M * D))
     acc = _DTYPES[accum_dtype if accum_dtype is not None else torch.float32]
+    sc = _SCATTER[scatter]
+    host = _host_shapes(spatial_shapes, spatial_shapes_host) if sc == MSDA_SCATTER_BINNED else None
     dev = value.device
     if grad_value is None:
         grad_value = torch.empty_like(value)
@@ -174,15 +232,15 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
     _check(grad_value, "grad_value", dt, value.shape)
     _check(grad_loc, "grad_loc", dt, sampling_locations.shape)
     _check(grad_attn, "grad_attn", dt, attention_weights.shape)
-    need = msda_backward_workspace_bytes(dims, _DTYPES[dt], acc)
+    need = msda_backward_workspace_bytes(dims, _DTYPES[dt], acc, sc, host)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().msda_backward(
         _ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),
         _ptr(attention_weights), _ptr(grad_out), _ptr(grad_value), _ptr(grad_loc),
-        _ptr(grad_attn), ctypes.byref(dims), _DTYPES[dt], acc, _ptr(workspace), ws_bytes,
-        _stream(stream))
+        _ptr(grad_attn), ctypes.byref(dims), _DTYPES[dt], acc, sc,
+        None if host is None else host.ctypes.data, _ptr(workspace), ws_bytes, _stream(stream))
     if st != MSDA_OK:
         raise MsdaError(st, "msda_backward")
     return grad_value, grad_loc, grad_attn

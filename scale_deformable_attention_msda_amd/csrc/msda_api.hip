@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstddef>
 
 namespace {
 
@@ -165,33 +166,77 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
   return MSDA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct BackwardSetup {
+  Checked c;
+  bool work = false;     // at least one sample
+  bool binned = false;
+  bool use_ws = false;   // atomic path with an fp32 workspace
+  msda::BinPlan plan{};
+  size_t ws_need = 0;
+};
+
+msda_status backward_setup(const msda_dims *dims, msda_dtype dtype, msda_dtype accum_dtype,
+                           msda_scatter scatter, const int64_t *shapes_host, BackwardSetup *su) {
+  MSDA_TRY(check_dims(dims, dtype, &su->c));
+  const Checked &c = su->c;
+  if (accum_dtype != MSDA_FP32 && accum_dtype != MSDA_BF16)
+    return fail(MSDA_ERR_UNSUPPORTED, "accum_dtype %d is not FP32 (0) or BF16 (1)",
+                (int)accum_dtype);
+  if (scatter != MSDA_SCATTER_BINNED && scatter != MSDA_SCATTER_ATOMIC)
+    return fail(MSDA_ERR_UNSUPPORTED, "scatter %d is not BINNED (0) or ATOMIC (1)", (int)scatter);
+  su->work = c.hq_elems > 0;
+  if (scatter == MSDA_SCATTER_BINNED) {
+    su->binned = true;
+    if (accum_dtype != MSDA_FP32)
+      return fail(MSDA_ERR_UNSUPPORTED, "the binned scatter accumulates in fp32 only");
+    if (su->work) {
+      if (!shapes_host)
+        return fail(MSDA_ERR_NULL_POINTER, "the binned scatter needs spatial_shapes_host");
+      const char *why = "";
+      if (!msda::make_bin_plan(su->plan, c.B, c.Q, c.S, (int)c.M, (int)c.D, (int)c.L, (int)c.K,
+                               shapes_host, &why))
+        return fail(MSDA_ERR_UNSUPPORTED, "binned scatter: %s", why);
+      su->ws_need = msda::binned_workspace_bytes(su->plan);
+    }
+  } else {
+    if (dtype == MSDA_FP32 && accum_dtype != MSDA_FP32)
+      return fail(MSDA_ERR_UNSUPPORTED, "FP32 data needs an FP32 accumulator");
+    su->use_ws = dtype == MSDA_BF16 && accum_dtype == MSDA_FP32 && su->work;
+    su->ws_need = su->use_ws ? (size_t)c.value_elems * 4 : 0;
+  }
+  return MSDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
-                                     msda_dtype accum_dtype) {
-  if (!dims || dtype != MSDA_BF16 || accum_dtype != MSDA_FP32) return 0;
-  int64_t n = 0;
-  if (dims->batch < 0 || dims->num_keys < 0 || dims->num_heads < 0 || dims->head_dim < 0) return 0;
-  if (!mul_ok(dims->batch, dims->num_keys, &n) || !mul_ok(n, dims->num_heads, &n) ||
-      !mul_ok(n, dims->head_dim, &n) || !mul_ok(n, 4, &n))
-    return 0;
-  return (size_t)n;
+                                     msda_dtype accum_dtype, msda_scatter scatter,
+                                     const int64_t *spatial_shapes_host) {
+  g_last_error[0] = '\0';
+  BackwardSetup su;
+  if (backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su) != MSDA_OK)
+    return SIZE_MAX;
+  return su.ws_need;
 }
 
 msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           const int64_t *level_start_index, const void *sampling_locations,
                           const void *attention_weights, const void *grad_out, void *grad_value,
                           void *grad_loc, void *grad_attn, const msda_dims *dims,
-                          msda_dtype dtype, msda_dtype accum_dtype, void *workspace,
+                          msda_dtype dtype, msda_dtype accum_dtype, msda_scatter scatter,
+                          const int64_t *spatial_shapes_host, void *workspace,
                           size_t workspace_bytes, void *stream) {
   g_last_error[0] = '\0';
-  Checked c;
-  MSDA_TRY(check_dims(dims, dtype, &c));
-  if (accum_dtype != MSDA_FP32 && accum_dtype != MSDA_BF16)
-    return fail(MSDA_ERR_UNSUPPORTED, "accum_dtype %d is not FP32 (0) or BF16 (1)",
-                (int)accum_dtype);
-  if (dtype == MSDA_FP32 && accum_dtype != MSDA_FP32)
-    return fail(MSDA_ERR_UNSUPPORTED, "FP32 data needs an FP32 accumulator");
-  const bool work = c.hq_elems > 0;
-  const bool use_ws = dtype == MSDA_BF16 && accum_dtype == MSDA_FP32 && work;
+  BackwardSetup su;
+  MSDA_TRY(backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su));
+  const Checked &c = su.c;
+  const bool work = su.work;
   MSDA_TRY(check_ptr(value, "value", true, 16));
   MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
   MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
@@ -201,25 +246,43 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
   MSDA_TRY(check_ptr(grad_value, "grad_value", c.value_elems > 0, 16));
   MSDA_TRY(check_ptr(grad_loc, "grad_loc", work, 16));
   MSDA_TRY(check_ptr(grad_attn, "grad_attn", work, 16));
-  if (use_ws) {
-    const size_t need = (size_t)c.value_elems * 4;
-    if (!workspace || workspace_bytes < need)
-      return fail(MSDA_ERR_WORKSPACE, "BF16 data with an FP32 accumulator needs %zu bytes of "
-                  "workspace, got %zu%s", need, workspace_bytes, workspace ? "" : " (NULL)");
+  if (su.ws_need > 0) {
+    if (!workspace || workspace_bytes < su.ws_need)
+      return fail(MSDA_ERR_WORKSPACE, "this backward needs %zu bytes of workspace, got %zu%s",
+                  su.ws_need, workspace_bytes, workspace ? "" : " (NULL)");
     if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (c.value_elems == 0) return MSDA_OK;
   hipError_t e;
-  if (!work || !use_ws) {
+  if (!work) {
+    e = msda::launch_zero(grad_value, (size_t)(c.value_elems * c.elt), s);
+    return e == hipSuccess ? MSDA_OK : hip_fail(e, "grad_value zero-fill launch");
+  }
+  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  if (su.binned) {
+    msda::BinArgs a{};
+    a.value = value;
+    a.starts = level_start_index;
+    a.loc = sampling_locations;
+    a.attn = attention_weights;
+    a.grad_out = grad_out;
+    a.grad_value = grad_value;
+    a.grad_loc = grad_loc;
+    a.grad_attn = grad_attn;
+    a.p = su.plan;
+    a.w = msda::carve_bin_scratch(su.plan, workspace);
+    e = msda::launch_backward_binned(a, dt, s);
+    return e == hipSuccess ? MSDA_OK : hip_fail(e, "binned backward launch");
+  }
+  const bool use_ws = su.use_ws;
+  if (!use_ws) {
     e = msda::launch_zero(grad_value, (size_t)(c.value_elems * c.elt), s);
     if (e != hipSuccess) return hip_fail(e, "grad_value zero-fill launch");
-    if (!work) return MSDA_OK;
   } else {
     e = msda::launch_zero(workspace, (size_t)c.value_elems * 4, s);
     if (e != hipSuccess) return hip_fail(e, "workspace zero-fill launch");
   }
-  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
   const auto acc = accum_dtype == MSDA_FP32 ? msda::Accum::F32 : msda::Accum::BF16;
   const int64_t acc_elt = accum_dtype == MSDA_FP32 ? 4 : 2;
   char *acc_base = static_cast<char *>(use_ws ? workspace : grad_value);

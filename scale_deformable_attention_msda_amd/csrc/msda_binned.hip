@@ -1,0 +1,774 @@
+// Destination-binned MSDA backward for gfx950: grad_value without global
+// floating-point atomics.
+//
+// The gradients are those of <out, grad_out> for the operator of "1.
+// Deformable attention, from scratch" (msda-triton course, chapter 1):
+//   p_c         = <grad_out[b,q,m,:], V_c>           (V_c = corner row, 0 outside)
+//   grad_attn   = sum_c w_c p_c
+//   grad_loc_x  = A * W * ((1-ly)(p01-p00) + ly(p11-p10))
+//   grad_loc_y  = A * H * ((1-lx)(p10-p00) + lx(p11-p01))
+//   grad_value[row_c] += A * w_c * grad_out[b,q,m,:]
+// The pages' kernels scatter grad_value with global atomics ("Efficient
+// Multi-Scale Deformable Attention on GPUs", section "The backward pass is an
+// atomics problem").  On this GPU a device-scope fp32 atomic add sustains far
+// fewer updates per second than the gather side needs, so this path first
+// sorts the samples by destination and then accumulates each tile of
+// grad_value in LDS, writing every row once with plain stores:
+//   count    per-block LDS histogram of samples per bin, one global integer
+//            atomic per touched bin (dead samples get zero gradients here);
+//   plan     one block: exclusive scan -> bin starts, chunks of <= `chunk`
+//            samples per bin, partial-tile slots for bins split in chunks;
+//   scatter  recount in LDS, reserve each block's range per bin with one
+//            atomic, write sample ids in bin order;
+//   tile     one block per chunk: stage the (T+1)^2 value rows of the tile
+//            (plus rim) in LDS, counting-sort the chunk's samples by their
+//            bilinear cell (integer LDS atomics), then one lane group per
+//            cell keeps the cell's four corner rows and four accumulators in
+//            registers while it walks the cell's samples: p_c, grad_loc,
+//            grad_attn, and A * w_c * grad_out summed in registers.  Each cell
+//            stores its four sums once to LDS; every pixel then adds the (up
+//            to four) cells around it.  Interior rows go straight to
+//            grad_value, edge / rim rows (or the whole partial tile of a
+//            split bin) to scratch.  No floating-point atomics: on this GPU
+//            they are an order of magnitude slower than plain LDS traffic;
+//   merge    one block per bin: add the neighbours' rims and the partial
+//            tiles into the rows still missing, store them once.
+#include "msda_device.h"
+#include "msda_launch.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace msda {
+namespace {
+
+constexpr int kTile = 8;               // tile edge in pixels
+constexpr int kEdge = kTile + 1;       // tile plus its one-pixel rim, per side
+constexpr int kCells = kEdge * kEdge;  // bilinear cells whose top-left corner is in [-1, T)
+constexpr int kChunk = 1024;           // samples per tile-kernel block at most
+constexpr int kCountSamples = 4096;    // samples per count / scatter block
+constexpr int kHistLdsBytes = 48 * 1024;
+constexpr uint32_t kNoSlot = 0xffffffffu;
+
+// -------------------------------------------------------------- geometry
+
+struct Cell {
+  int x0, y0;     // top-left corner of the bilinear cell
+  float lx, ly;   // fractional parts
+};
+
+// Cell of normalised (u, v) on an H x W level: x = u*W - 0.5, y = v*H - 0.5,
+// x0 = floor(x).  Coordinates are formed and floored in fp64, where u*W is
+// exact, so the cell is the exact one.  Returns false when no corner of the
+// cell lies inside the map (also for NaN / Inf / huge coordinates).
+__device__ inline bool cell_of(float u, float v, int H, int W, Cell &c) {
+  const double x = (double)u * (double)W - 0.5;
+  const double y = (double)v * (double)H - 0.5;
+  const double xf = floor(x), yf = floor(y);
+  if (!(xf >= -1.0 && xf < (double)W && yf >= -1.0 && yf < (double)H)) return false;
+  c.x0 = (int)xf;
+  c.y0 = (int)yf;
+  c.lx = (float)(x - xf);
+  c.ly = (float)(y - yf);
+  return true;
+}
+
+// Tile of a cell: the one holding its top-left corner, clamped into the map.
+__device__ inline int tile_of(const BinPlan &p, int l, const Cell &c) {
+  const int x = max(c.x0, 0), y = max(c.y0, 0);
+  return (y / kTile) * p.ntx[l] + (x / kTile);
+}
+
+template <typename T>
+__device__ inline float ldf(const void *base, int64_t i) {
+  return to_float<T>(reinterpret_cast<const T *>(base)[i]);
+}
+
+// Global bin of batch-local histogram slot e of batch b.
+__device__ inline int bin_of_slot(const BinPlan &p, int b, int e) {
+  int l = 0;
+  while (l + 1 < p.L && !(e >= p.hist_base[l] && e < p.hist_base[l] + p.M * p.ntiles[l])) ++l;
+  const int rem = e - p.hist_base[l];
+  const int m = rem / p.ntiles[l], t = rem - m * p.ntiles[l];
+  return p.bin_base[l] + (b * p.M + m) * p.ntiles[l] + t;
+}
+
+// Histogram slot of sample s (batch-local index, < 2^32) or -1 for a dead sample.
+template <typename T>
+__device__ inline int slot_of_sample(const BinArgs &a, int64_t id, uint32_t s) {
+  const BinPlan &p = a.p;
+  const uint32_t hq = fdiv(s, p.div_lk);
+  const uint32_t j = s - hq * (uint32_t)(p.L * p.K);
+  const uint32_t m = hq - fdiv(hq, p.div_m) * (uint32_t)p.M;
+  const int l = (int)fdiv(j, p.div_k);
+  Cell c;
+  if (!cell_of(ldf<T>(a.loc, 2 * id), ldf<T>(a.loc, 2 * id + 1), p.H[l], p.W[l], c)) return -1;
+  return p.hist_base[l] + (int)m * p.ntiles[l] + tile_of(p, l, c);
+}
+
+// --------------------------------------------------------------- count pass
+
+template <typename T>
+__global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
+  extern __shared__ uint32_t hist[];
+  const BinPlan &p = a.p;
+  const int b = blockIdx.y;
+  const int64_t per_b = a.p.Q * p.M * p.L * p.K;
+  const int64_t s0 = (int64_t)blockIdx.x * kCountSamples;
+  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kCountSamples; i += blockDim.x) {
+    const int64_t s = s0 + i;
+    if (s >= per_b) break;
+    const int64_t id = b * per_b + s;
+    const int e = slot_of_sample<T>(a, id, (uint32_t)s);
+    if (e < 0) {
+      // no corner inside its level: zero gradients, never binned
+      store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, 0.0f);
+      store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * id, 0.0f);
+      store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * id + 1, 0.0f);
+      continue;
+    }
+    __hip_atomic_fetch_add(&hist[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
+    const uint32_t n = hist[e];
+    if (n) __hip_atomic_fetch_add(&a.w.counts[bin_of_slot(p, b, e)], n, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------- plan pass
+
+// One block of 1024 threads: exclusive scans of counts, chunk counts and
+// split-bin slot counts, then the chunk table.
+__global__ __launch_bounds__(1024) void plan_kernel(BinArgs a) {
+  __shared__ uint32_t part[3][1024];
+  const BinPlan &p = a.p;
+  const int n = p.nbins;
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  uint32_t s_cnt = 0, s_ch = 0, s_slot = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t c = a.w.counts[i];
+    const uint32_t nch = c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
+    s_cnt += c;
+    s_ch += nch;
+    s_slot += nch > 1 ? nch : 0;
+  }
+  // inclusive Hillis-Steele scan of the three per-thread totals
+  part[0][threadIdx.x] = s_cnt;
+  part[1][threadIdx.x] = s_ch;
+  part[2][threadIdx.x] = s_slot;
+  __syncthreads();
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+    uint32_t v0 = 0, v1 = 0, v2 = 0;
+    if ((int)threadIdx.x >= off) {
+      v0 = part[0][threadIdx.x - off];
+      v1 = part[1][threadIdx.x - off];
+      v2 = part[2][threadIdx.x - off];
+    }
+    __syncthreads();
+    part[0][threadIdx.x] += v0;
+    part[1][threadIdx.x] += v1;
+    part[2][threadIdx.x] += v2;
+    __syncthreads();
+  }
+  if (threadIdx.x == blockDim.x - 1) *a.w.nchunks = part[1][threadIdx.x];
+  // exclusive prefix of this thread's segment
+  part[0][threadIdx.x] -= s_cnt;
+  part[1][threadIdx.x] -= s_ch;
+  part[2][threadIdx.x] -= s_slot;
+  uint32_t pos = part[0][threadIdx.x], ch = part[1][threadIdx.x], slot = part[2][threadIdx.x];
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t c = a.w.counts[i];
+    const uint32_t nch = c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
+    a.w.bin_start[i] = pos;
+    a.w.bin_nch[i] = nch;
+    a.w.bin_slot0[i] = nch > 1 ? slot : kNoSlot;
+    for (uint32_t k = 0; k < nch; ++k) {
+      const uint32_t first = k * (uint32_t)p.chunk;
+      const uint32_t cnt = c > first ? min((uint32_t)p.chunk, c - first) : 0u;
+      a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
+    }
+    pos += c;
+    ch += nch;
+    slot += nch > 1 ? nch : 0;
+  }
+}
+
+// ------------------------------------------------------------- scatter pass
+
+template <typename T>
+__global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
+  constexpr int kPer = kCountSamples / 256;
+  extern __shared__ uint32_t hist[];
+  const BinPlan &p = a.p;
+  const int b = blockIdx.y;
+  const int64_t per_b = a.p.Q * p.M * p.L * p.K;
+  const int64_t s0 = (int64_t)blockIdx.x * kCountSamples;
+  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  int slot[kPer];
+  uint32_t rank[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t s = s0 + r * 256 + threadIdx.x;
+    slot[r] = -1;
+    rank[r] = 0;
+    if (s < per_b) {
+      slot[r] = slot_of_sample<T>(a, b * per_b + s, (uint32_t)s);
+      if (slot[r] >= 0)
+        rank[r] = __hip_atomic_fetch_add(&hist[slot[r]], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
+    const uint32_t n = hist[e];
+    if (n) {
+      const int bin = bin_of_slot(p, b, e);
+      hist[e] = a.w.bin_start[bin] + __hip_atomic_fetch_add(&a.w.cursor[bin], n, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    if (slot[r] >= 0) {
+      const int64_t s = s0 + r * 256 + threadIdx.x;
+      a.w.ids[hist[slot[r]] + rank[r]] = (uint32_t)(b * per_b + s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- tile pass
+
+// One sample of a chunk, as the cell loop needs it.
+struct SampleRec {
+  uint32_t id;  // sample id
+  float a;      // attention weight
+  float lx, ly; // fractional parts of the pixel coordinate
+};
+
+// Channels per lane / lanes per sample for fp32 rows of D channels in LDS.
+template <int D>
+struct TileLayout {
+  static constexpr int VEC = D >= 16 ? 4 : 2;
+  static constexpr int G = D / VEC;
+  static constexpr int RS = D + 4;  // LDS row stride in floats (16-byte pad against bank conflicts)
+};
+
+// LDS carve-up of the tile kernel (floats unless stated):
+//   vt     [kEdge^2 + 1][RS]   value rows of the tile and its rim, then one zero row
+//   stage  [kCells][4][RS]     per-cell corner sums; also the unsorted records in phase A
+//   sorted [kChunk]            SampleRec, sorted by cell
+//   tag    [kChunk] u32        cell | rank << 8 of each unsorted record (~0: dropped)
+//   cnt    [kCells + 1] u32    samples per cell, then (after the scan) the cell starts
+template <int D>
+struct TileSmem {
+  static constexpr int RS = TileLayout<D>::RS;
+  static constexpr size_t vt = 0;
+  static constexpr size_t stage = vt + (size_t)(kEdge * kEdge + 1) * RS * 4;
+  static constexpr size_t cell_bytes = (size_t)kCells * 4 * RS * 4;
+  static constexpr size_t rec_bytes = (size_t)kChunk * sizeof(SampleRec);
+  static constexpr size_t stage_bytes = cell_bytes > rec_bytes ? cell_bytes : rec_bytes;
+  static constexpr size_t sorted = stage + stage_bytes;
+  static constexpr size_t tag = sorted + (size_t)kChunk * sizeof(SampleRec);
+  static constexpr size_t cnt = tag + (size_t)kChunk * 4;
+  static constexpr size_t bytes = cnt + (size_t)(kCells + 1) * 4 * 2;
+};
+
+__device__ inline void decode_bin(const BinPlan &p, int bin, int &l, int &b, int &m, int &ty,
+                                  int &tx) {
+  l = 0;
+  while (l + 1 < p.L && !(bin >= p.bin_base[l] && bin < p.bin_base[l] + (int)p.B * p.M * p.ntiles[l]))
+    ++l;
+  const int rem = bin - p.bin_base[l];
+  const int bm = rem / p.ntiles[l], t = rem - bm * p.ntiles[l];
+  b = bm / p.M;
+  m = bm - b * p.M;
+  ty = t / p.ntx[l];
+  tx = t - ty * p.ntx[l];
+}
+
+// Rim row (0 .. 4T-1) of tile-local pixel (iy, ix) that is an edge or halo pixel:
+//   [0, T]        bottom halo row iy = T, ix = 0..T
+//   [T+1, 2T]     right halo column ix = T, iy = 0..T-1
+//   [2T+1, 3T]    top edge row iy = 0, ix = 0..T-1
+//   [3T+1, 4T-1]  left edge column ix = 0, iy = 1..T-1
+__device__ inline int rim_row(int iy, int ix) {
+  if (iy == kTile) return ix;
+  if (ix == kTile) return kTile + 1 + iy;
+  if (iy == 0) return 2 * kTile + 1 + ix;
+  return 3 * kTile + iy;  // ix == 0, iy >= 1
+}
+
+template <typename T, int VEC>
+__device__ inline void load_grad_out_row(const BinArgs &a, uint32_t id, int lane, float (&g)[VEC]) {
+  const int64_t hq = fdiv(id, a.p.div_lk);
+  const T *src = reinterpret_cast<const T *>(a.grad_out) + hq * a.p.D + lane * VEC;
+  if constexpr (sizeof(T) == 4 && VEC == 4) {
+    const float4 v = *reinterpret_cast<const float4 *>(src);
+    g[0] = v.x; g[1] = v.y; g[2] = v.z; g[3] = v.w;
+  } else if constexpr (sizeof(T) == 2 && VEC == 4) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(src);
+    g[0] = __uint_as_float(v.x << 16); g[1] = __uint_as_float(v.x & 0xffff0000u);
+    g[2] = __uint_as_float(v.y << 16); g[3] = __uint_as_float(v.y & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) g[i] = to_float<T>(src[i]);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
+  using TL = TileLayout<D>;
+  using SM = TileSmem<D>;
+  constexpr int VEC = TL::VEC, G = TL::G, RS = TL::RS;
+  constexpr int NROWS = kEdge * kEdge;
+  constexpr int kZeroRow = NROWS;
+  constexpr uint32_t kDropped = 0xffffffffu;
+  extern __shared__ __align__(16) char smem[];
+  float *vt = reinterpret_cast<float *>(smem + SM::vt);
+  float *stage = reinterpret_cast<float *>(smem + SM::stage);
+  SampleRec *raw = reinterpret_cast<SampleRec *>(smem + SM::stage);  // phase A only
+  SampleRec *sorted = reinterpret_cast<SampleRec *>(smem + SM::sorted);
+  uint32_t *tag = reinterpret_cast<uint32_t *>(smem + SM::tag);
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + SM::cnt);   // [kCells + 1]
+  uint32_t *cstart = cnt + kCells + 1;                              // [kCells + 1]
+
+  const BinPlan &p = a.p;
+  if (blockIdx.x >= *a.w.nchunks) return;
+  const uint4 ck = a.w.chunks[blockIdx.x];
+  const int bin = (int)ck.x;
+  const uint32_t first = ck.y, count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
+  int l, b, m, ty, tx;
+  decode_bin(p, bin, l, b, m, ty, tx);
+  const int H = p.H[l], W = p.W[l];
+  const int px0 = tx * kTile, py0 = ty * kTile;
+  const int64_t start = a.starts[l];
+  const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
+  const int grp = threadIdx.x / G, lane = threadIdx.x % G;
+  constexpr int NG = 256 / G;
+
+  // stage value rows (zero outside the map) and clear the cell counters
+  for (int r = grp; r < NROWS + 1; r += NG) {
+    const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
+    const int py = py0 + iy, px = px0 + ix;
+    const int64_t prow = start + (int64_t)py * W + px;  // pyramid row inside the batch image
+    float v[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
+    if (count > 0 && r < NROWS && py < H && px < W && prow >= 0 && prow < p.S) {
+      const int64_t e = (((int64_t)b * p.S + prow) * p.M + m) * D + lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] = ldf<T>(a.value, e + i);
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) vt[r * RS + lane * VEC + i] = v[i];
+  }
+  for (int c = threadIdx.x; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
+  __syncthreads();
+
+  // phase A: geometry of each sample, its cell, and its rank inside the cell
+  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+    uint32_t t = kDropped;
+    const uint32_t id = a.w.ids[first + i];
+    if (id < p.total) {
+      const uint32_t hq = fdiv(id, p.div_lk);
+      const uint32_t j = id - hq * (uint32_t)(p.L * p.K);
+      Cell c;
+      if ((int)fdiv(j, p.div_k) == l &&
+          cell_of(ldf<T>(a.loc, 2 * (int64_t)id), ldf<T>(a.loc, 2 * (int64_t)id + 1), H, W, c)) {
+        const int cy = c.y0 - py0 + 1, cx = c.x0 - px0 + 1;
+        if (cy >= 0 && cy < kEdge && cx >= 0 && cx < kEdge) {
+          const uint32_t cell = (uint32_t)(cy * kEdge + cx);
+          const uint32_t rank = __hip_atomic_fetch_add(&cnt[cell], 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+          raw[i] = SampleRec{id, ldf<T>(a.attn, id), c.lx, c.ly};
+          t = cell | (rank << 8);
+        }
+      }
+    }
+    tag[i] = t;
+  }
+  __syncthreads();
+  // exclusive scan of the cell counts (one wave, two entries per lane)
+  if (threadIdx.x < 64) {
+    const int i0 = 2 * threadIdx.x, i1 = i0 + 1;
+    const uint32_t c0 = i0 < kCells ? cnt[i0] : 0u, c1 = i1 < kCells ? cnt[i1] : 0u;
+    uint32_t inc = c0 + c1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(inc, off, 64);
+      if ((int)threadIdx.x >= off) inc += v;
+    }
+    const uint32_t exc = inc - c0 - c1;
+    if (i0 <= kCells) cstart[i0] = exc;
+    if (i1 <= kCells) cstart[i1] = exc + c0;
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+    const uint32_t t = tag[i];
+    if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
+  }
+  __syncthreads();
+
+  // cell loop: one group per cell, corner rows and sums in registers
+  for (int cell = grp; cell < kCells; cell += NG) {
+    const int cy = cell / kEdge, cx = cell - (cell / kEdge) * kEdge;
+    const uint32_t s0 = cstart[cell], n = cstart[cell + 1] - s0;
+    float V[4][VEC], acc[4][VEC];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // corner q of cell (cy, cx) is tile-local pixel (cy - 1 + q/2, cx - 1 + q%2)
+      const int iy = cy - 1 + (q >> 1), ix = cx - 1 + (q & 1);
+      const bool in = iy >= 0 && ix >= 0 && py0 + iy < H && px0 + ix < W;
+      const float *src = vt + (in ? iy * kEdge + ix : kZeroRow) * RS + lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        V[q][i] = n ? src[i] : 0.0f;
+        acc[q][i] = 0.0f;
+      }
+    }
+    constexpr int U = 4;  // samples whose grad_out rows are loaded together
+    for (uint32_t k0 = 0; k0 < n; k0 += U) {
+      SampleRec rec[U];
+      float g[U][VEC];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        rec[u] = sorted[s0 + min(k0 + u, n - 1)];
+        load_grad_out_row<T, VEC>(a, rec[u].id, lane, g[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u >= n) break;
+        float pc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) sum = fmaf(g[u][i], V[q][i], sum);
+          pc[q] = group_sum<G>(sum);
+        }
+        const float lx = rec[u].lx, ly = rec[u].ly, av = rec[u].a;
+        const float w[4] = {(1.0f - lx) * (1.0f - ly), lx * (1.0f - ly), (1.0f - lx) * ly, lx * ly};
+        if (lane == 0) {
+          const uint32_t id = rec[u].id;
+          const float ga = w[0] * pc[0] + w[1] * pc[1] + w[2] * pc[2] + w[3] * pc[3];
+          const float gx = av * (float)W * ((1.0f - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
+          const float gy = av * (float)H * ((1.0f - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
+          store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, ga);
+          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id, gx);
+          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id + 1, gy);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float aw = av * w[q];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw, g[u][i], acc[q][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) stage[(cell * 4 + q) * RS + lane * VEC + i] = acc[q][i];
+  }
+  __syncthreads();
+
+  // every pixel of the tile and its rim sums the cells it is a corner of, then
+  // goes to grad_value (interior), the rim (edge / halo) or the chunk's slot
+  for (int r = grp; r < NROWS; r += NG) {
+    const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
+    const int py = py0 + iy, px = px0 + ix;
+    if (py >= H || px >= W) continue;
+    float v[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
+    // pixel (iy, ix) is corner 00 of cell (iy+1, ix+1), 01 of (iy+1, ix), 10 of (iy, ix+1), 11 of (iy, ix)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cy = iy + 1 - (q >> 1), cx = ix + 1 - (q & 1);
+      if (cy >= kEdge || cx >= kEdge) continue;
+      const float *src = stage + ((cy * kEdge + cx) * 4 + q) * RS + lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] += src[i];
+    }
+    if (slot != kNoSlot) {
+      float *dst = a.w.slots + ((int64_t)slot * NROWS + r) * D + lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dst[i] = v[i];
+    } else if (iy > 0 && ix > 0 && iy < kTile && ix < kTile) {
+      const int64_t prow = start + (int64_t)py * W + px;
+      if (prow < 0 || prow >= p.S) continue;  // inconsistent level_start_index: skip
+      T *dst = reinterpret_cast<T *>(a.grad_value) + ((row0 + (int64_t)py * W + px) * p.M + m) * D +
+               lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) store_scalar<T>(dst + i, v[i]);
+    } else {
+      float *dst = a.w.rim + ((int64_t)bin * 4 * kTile + rim_row(iy, ix)) * D + lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dst[i] = v[i];
+    }
+  }
+}
+
+// --------------------------------------------------------------- merge pass
+
+// Contribution of bin `nb` (a neighbour, or the tile itself) at its tile-local
+// pixel (iy, ix), from its rim (single-chunk) or its partial-tile slots.
+template <int VEC, int D>
+__device__ inline void add_part(const BinArgs &a, int nb, int iy, int ix, int lane, float *v) {
+  constexpr int E = kTile + 1;
+  const uint32_t nch = a.w.bin_nch[nb];
+  if (nch <= 1) {
+    const float *src = a.w.rim + ((int64_t)nb * 4 * kTile + rim_row(iy, ix)) * D + lane * VEC;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] += src[i];
+  } else {
+    const uint32_t s0 = a.w.bin_slot0[nb];
+    for (uint32_t k = 0; k < nch; ++k) {
+      const float *src = a.w.slots + ((int64_t)(s0 + k) * E * E + iy * E + ix) * D + lane * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] += src[i];
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(BinArgs a) {
+  using TL = TileLayout<D>;
+  constexpr int VEC = TL::VEC, G = TL::G;
+  constexpr int NG = 256 / G;
+  const BinPlan &p = a.p;
+  const int bin = blockIdx.x;
+  int l, b, m, ty, tx;
+  decode_bin(p, bin, l, b, m, ty, tx);
+  const int H = p.H[l], W = p.W[l], ntx = p.ntx[l];
+  const int px0 = tx * kTile, py0 = ty * kTile;
+  const int64_t row0 = (int64_t)b * p.S + a.starts[l];
+  const bool split = a.w.bin_nch[bin] > 1;
+  const int grp = threadIdx.x / G, lane = threadIdx.x % G;
+  // rows to finish: the whole interior of a split bin, else its top row and left column
+  const int nrows = split ? kTile * kTile : 2 * kTile - 1;
+  for (int r = grp; r < nrows; r += NG) {
+    int iy, ix;
+    if (split) {
+      iy = r / kTile;
+      ix = r - iy * kTile;
+    } else if (r < kTile) {
+      iy = 0;
+      ix = r;
+    } else {
+      iy = r - kTile + 1;
+      ix = 0;
+    }
+    const int py = py0 + iy, px = px0 + ix;
+    if (py >= H || px >= W) continue;
+    const int64_t prow = a.starts[l] + (int64_t)py * W + px;
+    if (prow < 0 || prow >= p.S) continue;  // inconsistent level_start_index: skip
+    float v[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
+    add_part<VEC, D>(a, bin, iy, ix, lane, v);                       // own rows
+    if (ix == 0 && tx > 0) add_part<VEC, D>(a, bin - 1, iy, kTile, lane, v);        // left's right halo
+    if (iy == 0 && ty > 0) add_part<VEC, D>(a, bin - ntx, kTile, ix, lane, v);      // top's bottom halo
+    if (ix == 0 && iy == 0 && tx > 0 && ty > 0)
+      add_part<VEC, D>(a, bin - ntx - 1, kTile, kTile, lane, v);                    // top-left corner
+    T *dst = reinterpret_cast<T *>(a.grad_value) + ((row0 + (int64_t)py * W + px) * p.M + m) * D +
+             lane * VEC;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) store_scalar<T>(dst + i, v[i]);
+  }
+}
+
+// Rows [pyramid_rows, S) of every batch image belong to no level: zero them.
+template <typename T>
+__global__ __launch_bounds__(256) void zero_tail_kernel(BinArgs a) {
+  const BinPlan &p = a.p;
+  const int64_t per_row = (int64_t)p.M * p.D;
+  const int64_t tail = (p.S - p.pyramid_rows) * per_row;
+  const int64_t n = p.B * tail;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = i / tail, r = i - b * tail;
+    store_scalar<T>(reinterpret_cast<T *>(a.grad_value) + b * p.S * per_row +
+                        p.pyramid_rows * per_row + r, 0.0f);
+  }
+}
+
+template <typename T, int D>
+size_t tile_lds_bytes() {
+  return TileSmem<D>::bytes;
+}
+
+template <typename T, int D>
+hipError_t launch_tile_and_merge(const BinArgs &a, hipStream_t s) {
+  const size_t lds = tile_lds_bytes<T, D>();
+  prof_begin(s);
+  hipLaunchKernelGGL((tile_kernel<T, D>), dim3(a.p.max_chunks), dim3(256), lds, s, a);
+  prof_end(s, "bin_tile");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin(s);
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.p.nbins), dim3(256), 0, s, a);
+  prof_end(s, "bin_merge");
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
+  const BinPlan &p = a.p;
+  hipError_t e;
+  // counts and cursor are adjacent: clear both
+  e = launch_zero(a.w.counts, (size_t)2 * ((p.nbins + 3) / 4 * 4) * sizeof(uint32_t), s);
+  if (e != hipSuccess) return e;
+  if (p.S > p.pyramid_rows) {
+    prof_begin(s);
+  hipLaunchKernelGGL((zero_tail_kernel<T>), dim3(1024), dim3(256), 0, s, a);
+  prof_end(s, "bin_zero_tail");
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t per_b = p.Q * p.M * p.L * p.K;
+  const dim3 grid((unsigned)((per_b + kCountSamples - 1) / kCountSamples), (unsigned)p.B);
+  const size_t hist = (size_t)p.hist_size * sizeof(uint32_t);
+  prof_begin(s);
+  hipLaunchKernelGGL((count_kernel<T>), grid, dim3(256), hist, s, a);
+  prof_end(s, "bin_count");
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin(s);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  prof_end(s, "bin_plan");
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin(s);
+  hipLaunchKernelGGL((scatter_kernel<T>), grid, dim3(256), hist, s, a);
+  prof_end(s, "bin_scatter");
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  switch (p.D) {
+    case 8: return launch_tile_and_merge<T, 8>(a, s);
+    case 16: return launch_tile_and_merge<T, 16>(a, s);
+    case 32: return launch_tile_and_merge<T, 32>(a, s);
+    case 64: return launch_tile_and_merge<T, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, int L, int K,
+                   const int64_t *shapes_host, const char **why) {
+  std::memset(&p, 0, sizeof(p));
+  p.B = B;
+  p.Q = Q;
+  p.S = S;
+  p.M = M;
+  p.D = D;
+  p.L = L;
+  p.K = K;
+  p.tile = kTile;
+  p.chunk = kChunk;
+  if (L > kMaxLevels) {
+    *why = "too many levels for the binned backward";
+    return false;
+  }
+  int64_t rows = 0, tiles = 0;
+  for (int l = 0; l < L; ++l) {
+    const int64_t h = shapes_host[2 * l], w = shapes_host[2 * l + 1];
+    if (h < 1 || w < 1 || h > (1 << 20) || w > (1 << 20)) {
+      *why = "level shapes must be between 1 and 2^20 pixels per side";
+      return false;
+    }
+    p.H[l] = (int)h;
+    p.W[l] = (int)w;
+    p.ntx[l] = (int)((w + kTile - 1) / kTile);
+    p.ntiles[l] = (int)(((h + kTile - 1) / kTile) * p.ntx[l]);
+    rows += h * w;
+    tiles += p.ntiles[l];
+  }
+  if (rows > S) {
+    *why = "the levels hold more pixels than num_keys";
+    return false;
+  }
+  p.pyramid_rows = rows;
+  const int64_t total = B * Q * M * L * K;
+  const int64_t nbins = B * M * tiles;
+  if (total >= (int64_t(1) << 32) - 1 || nbins >= (int64_t(1) << 30)) {
+    *why = "too many samples or bins for the binned backward";
+    return false;
+  }
+  if ((int64_t)M * tiles * 4 > kHistLdsBytes) {
+    *why = "num_heads x tiles of the pyramid exceed the per-block histogram";
+    return false;
+  }
+  p.total = (uint32_t)total;
+  p.div_lk = make_fastdiv((uint32_t)(L * K));
+  p.div_k = make_fastdiv((uint32_t)K);
+  p.div_m = make_fastdiv((uint32_t)M);
+  p.nbins = (int)nbins;
+  p.hist_size = (int)(M * tiles);
+  // coarsest level (highest index) first
+  int run_bins = 0, run_hist = 0;
+  for (int l = L - 1; l >= 0; --l) {
+    p.bin_base[l] = run_bins;
+    p.hist_base[l] = run_hist;
+    run_bins += (int)(B * M) * p.ntiles[l];
+    run_hist += M * p.ntiles[l];
+  }
+  const int64_t extra = (total + kChunk - 1) / kChunk;
+  p.max_chunks = (int)(nbins + extra);
+  p.max_slots = (int)(2 * extra);
+  return true;
+}
+
+static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
+  const int E = kTile + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  const size_t nb4 = (size_t)(p.nbins + 3) / 4 * 4;
+  char *cc = take(2 * nb4 * sizeof(uint32_t));  // counts + cursor, cleared together
+  char *bs = take(nb4 * sizeof(uint32_t));
+  char *bn = take(nb4 * sizeof(uint32_t));
+  char *b0 = take(nb4 * sizeof(uint32_t));
+  char *nc = take(16);
+  char *ch = take((size_t)p.max_chunks * sizeof(uint4));
+  char *ids = take((size_t)p.total * sizeof(uint32_t));
+  char *rim = take((size_t)p.nbins * 4 * kTile * p.D * sizeof(float));
+  char *sl = take((size_t)p.max_slots * E * E * p.D * sizeof(float));
+  if (w) {
+    w->counts = reinterpret_cast<uint32_t *>(cc);
+    w->cursor = reinterpret_cast<uint32_t *>(cc) + nb4;
+    w->bin_start = reinterpret_cast<uint32_t *>(bs);
+    w->bin_nch = reinterpret_cast<uint32_t *>(bn);
+    w->bin_slot0 = reinterpret_cast<uint32_t *>(b0);
+    w->nchunks = reinterpret_cast<uint32_t *>(nc);
+    w->chunks = reinterpret_cast<uint4 *>(ch);
+    w->ids = reinterpret_cast<uint32_t *>(ids);
+    w->rim = reinterpret_cast<float *>(rim);
+    w->slots = reinterpret_cast<float *>(sl);
+  }
+  return off;
+}
+
+size_t binned_workspace_bytes(const BinPlan &p) { return layout(p, nullptr, nullptr); }
+
+BinScratch carve_bin_scratch(const BinPlan &p, void *workspace) {
+  BinScratch w{};
+  layout(p, &w, static_cast<char *>(workspace));
+  return w;
+}
+
+hipError_t launch_backward_binned(const BinArgs &a, Dtype dt, hipStream_t stream) {
+  if (a.p.total == 0) return hipSuccess;
+  return dt == Dtype::F32 ? launch_binned_t<float>(a, stream) : launch_binned_t<bf16_t>(a, stream);
+}
+
+}  // namespace msda

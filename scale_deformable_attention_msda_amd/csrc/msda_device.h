@@ -91,6 +91,27 @@ __device__ inline bool sample_corners(float u, float v, const Level &lv, uint32_
   return true;
 }
 
+// ------------------------------------------------------- integer division
+
+// Division of a 32-bit unsigned numerator by a divisor fixed at launch time,
+// as a multiply-high, an add and a shift (exact for every 32-bit numerator):
+// with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// n / d = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while (s < 32 && (uint64_t(1) << s) < d) ++s;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+
+__device__ inline uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.s);
+}
+
 // ---------------------------------------------------------------- dtypes
 
 struct bf16_t {

@@ -30,7 +30,6 @@
 namespace msda {
 namespace {
 
-constexpr int kMaxLevels = 16;
 constexpr int kMaxBlock = 256;
 constexpr int kGeoLdsBudget = 64 * 1024;
 
@@ -286,8 +285,10 @@ hipError_t fwd_launch(const LaunchArgs &a, hipStream_t stream) {
   const int64_t blocks = (total_hq + hqb - 1) / hqb;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t lds = (size_t)LK * hqb * sizeof(Corners);
+  prof_begin(stream);
   hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds, stream,
                      a, hqb);
+  prof_end(stream, "fwd");
   return hipGetLastError();
 }
 
@@ -301,8 +302,10 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
   const int64_t blocks = (total_hq + hqb - 1) / hqb;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t lds = (size_t)LK * hqb * per_sample;
+  prof_begin(stream);
   hipLaunchKernelGGL((bwd_kernel<T, D, AccT>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
                      stream, a, hqb);
+  prof_end(stream, "bwd_atomic");
   return hipGetLastError();
 }
 
@@ -346,8 +349,10 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
   const size_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((n16 + 255) / 256, 4096);
+  prof_begin(stream);
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<uint4 *>(p), n16);
+  prof_end(stream, "zero");
   return hipGetLastError();
 }
 
@@ -355,8 +360,10 @@ hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, size_t n, hipStr
   const size_t n8 = n / 8;
   if (n8 == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((n8 + 255) / 256, 4096);
+  prof_begin(stream);
   hipLaunchKernelGGL(cast_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const float4 *>(src), reinterpret_cast<uint4 *>(dst), n8);
+  prof_end(stream, "cast");
   return hipGetLastError();
 }
 

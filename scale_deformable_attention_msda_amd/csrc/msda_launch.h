@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "msda_device.h"
+
 namespace msda {
 
 // One launch covers batches [b0, b0 + nb) of a call.  Pointers are already
@@ -24,12 +26,85 @@ struct LaunchArgs {
   uint32_t acc_bytes;           // nb*S*M*D*sizeof(accumulator)
 };
 
+// ------------------------------------------------ destination-binned backward
+//
+// The pyramid of every (batch b, head m, level l) is cut into square tiles of
+// `tile` x `tile` pixels.  A sample belongs to the tile that holds its
+// top-left corner (x0, y0) (clamped to the map), so its four corners lie in
+// that tile or in the one-pixel rim to its right / below.  Bins (one per tile
+// of every (b, m)) are numbered coarsest level first, so the largest bins are
+// scheduled first:
+//   bin = bin_base[l] + (b*M + m) * ntiles[l] + ty * ntx[l] + tx.
+constexpr int kMaxLevels = 16;
+
+struct BinPlan {
+  int64_t B, Q, S;
+  int M, D, L, K;
+  int tile;                    // tile edge T in pixels
+  int chunk;                   // most samples one tile-kernel block processes
+  int H[kMaxLevels], W[kMaxLevels];
+  int ntx[kMaxLevels];         // tiles per row of level l
+  int ntiles[kMaxLevels];      // tiles of level l (per batch and head)
+  int bin_base[kMaxLevels];    // first bin of level l
+  int hist_base[kMaxLevels];   // first per-batch histogram slot of level l
+  int nbins;                   // B * M * (tiles of all levels)
+  int hist_size;               // M * (tiles of all levels): one batch's bins
+  int max_chunks;              // nbins + ceil(total / chunk)
+  int max_slots;               // 2 * ceil(total / chunk)
+  int64_t pyramid_rows;        // sum_l H_l * W_l
+  uint32_t total;              // B*Q*M*L*K samples
+  FastDiv div_lk, div_k, div_m;  // by L*K, K and M
+};
+
+// Device scratch carved out of the caller's workspace (byte offsets into it
+// are fixed by binned_layout()).
+struct BinScratch {
+  uint32_t *counts;     // [nbins] samples per bin
+  uint32_t *cursor;     // [nbins] fill cursor of the id scatter
+  uint32_t *bin_start;  // [nbins] first sorted position of a bin
+  uint32_t *bin_nch;    // [nbins] chunks of a bin
+  uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
+  uint32_t *nchunks;    // [1] chunks in use
+  uint4 *chunks;        // [max_chunks] (bin, first position, count, slot or ~0)
+  uint32_t *ids;        // [total] sample ids sorted by bin
+  float *rim;           // [nbins][4*tile][D] edge rows and halo of single-chunk tiles
+  float *slots;         // [max_slots][(tile+1)^2][D] whole partial tiles of split bins
+};
+
+struct BinArgs {
+  const void *value;
+  const int64_t *starts;  // device level_start_index
+  const void *loc;
+  const void *attn;
+  const void *grad_out;
+  void *grad_value;
+  void *grad_loc;
+  void *grad_attn;
+  BinPlan p;
+  BinScratch w;
+};
+
+// Kernel timing hooks (no-ops unless a profiling session is open on this
+// thread): every launch site calls prof_begin() before and prof_end() after
+// enqueueing its kernel.
+void prof_begin(hipStream_t stream);
+void prof_end(hipStream_t stream, const char *name);
+
 enum class Dtype { F32, BF16 };
 enum class Accum { F32, BF16 };
 
 hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream);
 hipError_t launch_backward(const LaunchArgs &a, Dtype dt, Accum acc, hipStream_t stream);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+
+// Binned backward: plan from host-side level shapes (returns false and a
+// reason when the pyramid cannot be tiled within the kernel limits), size and
+// carve the workspace, and enqueue the passes.
+bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, int L, int K,
+                   const int64_t *shapes_host, const char **why);
+size_t binned_workspace_bytes(const BinPlan &p);
+BinScratch carve_bin_scratch(const BinPlan &p, void *workspace);
+hipError_t launch_backward_binned(const BinArgs &a, Dtype dt, hipStream_t stream);
 hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, size_t n, hipStream_t stream);
 
 }  // namespace msda

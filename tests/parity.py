@@ -43,10 +43,11 @@ def operands(t: dict):
             t["attention_weights"])
 
 
-def run_gpu(x: dict, accum=None, stream=None) -> dict:
+def run_gpu(x: dict, accum=None, stream=None, scatter="binned") -> dict:
     t = upload(x)
     out = msda.msda_forward(*operands(t), stream=stream)
-    gv, gl, ga = msda.msda_backward(*operands(t), t["grad_out"], accum_dtype=accum, stream=stream)
+    gv, gl, ga = msda.msda_backward(*operands(t), t["grad_out"], accum_dtype=accum, stream=stream,
+                                    scatter=scatter, spatial_shapes_host=x["spatial_shapes"])
     torch.cuda.synchronize()
     return {k: v.double().cpu().numpy() for k, v in
             dict(out=out, grad_value=gv, grad_loc=gl, grad_attn=ga).items()}

@@ -57,12 +57,19 @@ def fwd(lib, d, dtype=0, value=FAKE, shapes=FAKE, starts=FAKE, loc=FAKE, attn=FA
                             None if d is None else ctypes.byref(d), dtype, None)
 
 
-def bwd(lib, d, dtype=0, acc=0, ws=None, ws_bytes=0, **p):
+SHAPES = (ctypes.c_int64 * 4)(8, 8, 4, 4)  # host copy of [[8, 8], [4, 4]]
+
+
+def bwd(lib, d, dtype=0, acc=0, scatter=1, shapes_host=None, ws=None, ws_bytes=0, **p):
     v = {k: p.get(k, FAKE) for k in ("value", "shapes", "starts", "loc", "attn", "gout", "gv",
                                      "gl", "ga")}
     return lib.msda_backward(v["value"], v["shapes"], v["starts"], v["loc"], v["attn"], v["gout"],
                              v["gv"], v["gl"], v["ga"], None if d is None else ctypes.byref(d),
-                             dtype, acc, ws, ws_bytes, None)
+                             dtype, acc, scatter, shapes_host, ws, ws_bytes, None)
+
+
+def ws_bytes(lib, d, dtype=0, acc=0, scatter=0, shapes_host=None):
+    return lib.msda_backward_workspace_bytes(ctypes.byref(d), dtype, acc, scatter, shapes_host)
 
 
 @pytest.mark.parametrize("kwargs,code", [
@@ -91,18 +98,36 @@ def test_empty_forward_is_ok_without_launch(lib):
     assert fwd(lib, dims(B=0), loc=None, attn=None, out=None) == 0
 
 
-def test_backward_rejections(lib):
+def test_backward_rejections_atomic(lib):
     assert bwd(lib, dims(), dtype=0, acc=1) == 3            # fp32 data needs fp32 accum
     assert bwd(lib, dims(), dtype=1, acc=0) == 5            # bf16 + fp32 accum needs workspace
-    need = lib.msda_backward_workspace_bytes(ctypes.byref(dims()), 1, 0)
+    need = ws_bytes(lib, dims(), 1, 0, scatter=1)
     assert need == 1 * 80 * 2 * 8 * 4
     assert bwd(lib, dims(), dtype=1, acc=0, ws=FAKE, ws_bytes=need - 1) == 5
     assert bwd(lib, dims(), dtype=1, acc=0, ws=FAKE + 4, ws_bytes=need) == 4
     assert bwd(lib, dims(), gv=None) == 1
     assert bwd(lib, dims(), acc=7) == 3
-    assert lib.msda_backward_workspace_bytes(ctypes.byref(dims()), 0, 0) == 0
-    assert lib.msda_backward_workspace_bytes(ctypes.byref(dims()), 1, 1) == 0
-    assert lib.msda_backward_workspace_bytes(None, 1, 0) == 0
+    assert bwd(lib, dims(), scatter=5) == 3
+    assert ws_bytes(lib, dims(), 0, 0, scatter=1) == 0
+    assert ws_bytes(lib, dims(), 1, 1, scatter=1) == 0
+    assert lib.msda_backward_workspace_bytes(None, 1, 0, 1, None) == 2 ** 64 - 1
+
+
+def test_backward_rejections_binned(lib):
+    assert bwd(lib, dims(), scatter=0) == 1                  # needs the host shapes
+    assert "spatial_shapes_host" in msda.msda_last_error()
+    assert bwd(lib, dims(), scatter=0, acc=1, dtype=1, shapes_host=SHAPES) == 3
+    need = ws_bytes(lib, dims(), 0, 0, scatter=0, shapes_host=SHAPES)
+    assert 0 < need < 1 << 24
+    assert bwd(lib, dims(), scatter=0, shapes_host=SHAPES, ws=FAKE, ws_bytes=need - 1) == 5
+    assert bwd(lib, dims(), scatter=0, shapes_host=SHAPES, ws=None, ws_bytes=need) == 5
+    bad = (ctypes.c_int64 * 4)(8, 0, 4, 4)
+    assert bwd(lib, dims(), scatter=0, shapes_host=bad) == 3
+    too_big = (ctypes.c_int64 * 4)(16, 16, 4, 4)          # 272 pixels > num_keys = 80
+    assert bwd(lib, dims(), scatter=0, shapes_host=too_big) == 3
+    assert ws_bytes(lib, dims(), 0, 0, scatter=0, shapes_host=bad) == 2 ** 64 - 1
+    # no samples: nothing to plan, no workspace
+    assert ws_bytes(lib, dims(Q=0), 0, 0, scatter=0, shapes_host=None) == 0
 
 
 def test_last_error_is_cleared_by_a_good_call(lib):

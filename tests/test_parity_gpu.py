@@ -40,18 +40,30 @@ def gate(x, g, o, accum_bf16=False):
             check("grad_value", g["grad_value"], o["grad_value"], *TOL_BF16)
 
 
+_CACHE = {}
+
+
+def workload_case(wid):
+    """Inputs and oracle results of a workload, computed once per test session."""
+    if wid not in _CACHE:
+        x = workloads.make_inputs(wid)
+        _CACHE.clear()
+        _CACHE[wid] = (x, parity.run_oracle(x))
+    return _CACHE[wid]
+
+
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
 @pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
-def test_workload(wid):
+def test_workload(wid, scatter):
     wl = workloads.WORKLOADS[wid]
     say(f"[parity] workload {wid} {wl.name} B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
-        f"L={wl.L} K={wl.K} {wl.dtype}")
-    x = workloads.make_inputs(wid)
-    o = parity.run_oracle(x)
-    g = parity.run_gpu(x)
+        f"L={wl.L} K={wl.K} {wl.dtype} scatter={scatter}")
+    x, o = workload_case(wid)
+    g = parity.run_gpu(x, scatter=scatter)
     gate(x, g, o)
-    if wl.dtype == "bf16":
+    if wl.dtype == "bf16" and scatter == "atomic":
         say("  accumulator bf16:")
-        gate(x, parity.run_gpu(x, accum=torch.bfloat16), o, accum_bf16=True)
+        gate(x, parity.run_gpu(x, accum=torch.bfloat16, scatter="atomic"), o, accum_bf16=True)
 
 
 EDGE = {
@@ -73,14 +85,16 @@ EDGE = {
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
-def test_edge(name):
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_edge(name, scatter):
     wl = EDGE[name]
-    say(f"[parity] edge {name}: B={wl.B} Q={wl.Q} M={wl.M} D={wl.D} L={wl.L} K={wl.K} {wl.dtype}")
+    say(f"[parity] edge {name}: B={wl.B} Q={wl.Q} M={wl.M} D={wl.D} L={wl.L} K={wl.K} {wl.dtype} "
+        f"scatter={scatter}")
     x = workloads.make_inputs(wl, seed=zlib.crc32(name.encode()) % 100000)
     o = parity.run_oracle(x)
-    gate(x, parity.run_gpu(x), o)
-    if wl.dtype == "bf16":
-        gate(x, parity.run_gpu(x, accum=torch.bfloat16), o, accum_bf16=True)
+    gate(x, parity.run_gpu(x, scatter=scatter), o)
+    if wl.dtype == "bf16" and scatter == "atomic":
+        gate(x, parity.run_gpu(x, accum=torch.bfloat16, scatter="atomic"), o, accum_bf16=True)
 
 
 def special_locations():
@@ -110,32 +124,36 @@ def special_locations():
     return x
 
 
-def test_boundary_and_nonfinite_locations():
-    say("[parity] boundary and non-finite locations")
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_boundary_and_nonfinite_locations(scatter):
+    say(f"[parity] boundary and non-finite locations, scatter={scatter}")
     x = special_locations()
     o = parity.run_oracle(x)
-    g = parity.run_gpu(x)
+    g = parity.run_gpu(x, scatter=scatter)
     for k in g:
         assert np.all(np.isfinite(g[k])), k
     gate(x, g, o)
 
 
-def test_empty_queries_zero_grad_value():
-    say("[parity] Q = 0: forward is a no-op, backward zero-fills grad_value")
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_empty_queries_zero_grad_value(scatter):
+    say(f"[parity] Q = 0: forward is a no-op, backward zero-fills grad_value ({scatter})")
     wl = workloads.custom(2, 0, 2, 32, ((4, 4), (2, 2)), 2)
     x = workloads.make_inputs(wl, seed=1)
     t = parity.upload(x)
     out = msda.msda_forward(*parity.operands(t))
     assert out.shape == (2, 0, 64)
     gv = torch.full_like(t["value"], float("nan"))
-    gv, gl, ga = msda.msda_backward(*parity.operands(t), t["grad_out"], grad_value=gv)
+    gv, gl, ga = msda.msda_backward(*parity.operands(t), t["grad_out"], grad_value=gv,
+                                    scatter=scatter, spatial_shapes_host=x["spatial_shapes"])
     torch.cuda.synchronize()
     assert torch.count_nonzero(gv).item() == 0
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_outputs_are_overwritten_and_deterministic(dtype):
-    say(f"[parity] overwrite + determinism {dtype}")
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_outputs_are_overwritten_and_deterministic(dtype, scatter):
+    say(f"[parity] overwrite + determinism {dtype} scatter={scatter}")
     wl = workloads.custom(2, 45, 8, 32, workloads.PYRAMID_DETR, 4, dtype=dtype)
     x = workloads.make_inputs(wl, seed=11)
     t = parity.upload(x)
@@ -143,10 +161,11 @@ def test_outputs_are_overwritten_and_deterministic(dtype):
     junk = lambda like: torch.full_like(like, float("nan"))
     out1 = msda.msda_forward(*ops, out=junk(t["grad_out"]))
     out2 = msda.msda_forward(*ops)
+    kw = dict(scatter=scatter, spatial_shapes_host=x["spatial_shapes"])
     gv1, gl1, ga1 = msda.msda_backward(*ops, t["grad_out"], grad_value=junk(t["value"]),
                                        grad_loc=junk(t["sampling_locations"]),
-                                       grad_attn=junk(t["attention_weights"]))
-    gv2, gl2, ga2 = msda.msda_backward(*ops, t["grad_out"])
+                                       grad_attn=junk(t["attention_weights"]), **kw)
+    gv2, gl2, ga2 = msda.msda_backward(*ops, t["grad_out"], **kw)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2), "forward must be bit-identical across runs"
     assert torch.equal(gl1, gl2) and torch.equal(ga1, ga2)
