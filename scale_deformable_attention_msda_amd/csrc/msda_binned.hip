@@ -48,6 +48,10 @@ constexpr int kCells = kEdge * kEdge;  // bilinear cells whose top-left corner i
 constexpr int kChunk = 1024;           // samples per tile-kernel block at most
 constexpr int kCountSamples = 4096;    // samples per count / scatter block
 constexpr int kHistLdsBytes = 48 * 1024;
+// Per-bin counters are striped over kStripes addresses (block index modulo
+// kStripes): a coarse-level bin collects counts from ~100 blocks, and integer
+// atomics on one address from many blocks serialize.
+constexpr int kStripes = 8;
 constexpr uint32_t kNoSlot = 0xffffffffu;
 
 // -------------------------------------------------------------- geometry
@@ -74,9 +78,9 @@ __device__ inline bool cell_of(float u, float v, int H, int W, Cell &c) {
 }
 
 // Tile of a cell: the one holding its top-left corner, clamped into the map.
-__device__ inline int tile_of(const BinPlan &p, int l, const Cell &c) {
+__device__ inline int tile_of(int ntx, const Cell &c) {
   const int x = max(c.x0, 0), y = max(c.y0, 0);
-  return (y / kTile) * p.ntx[l] + (x / kTile);
+  return (y / kTile) * ntx + (x / kTile);
 }
 
 template <typename T>
@@ -84,44 +88,87 @@ __device__ inline float ldf(const void *base, int64_t i) {
   return to_float<T>(reinterpret_cast<const T *>(base)[i]);
 }
 
-// Global bin of batch-local histogram slot e of batch b.
-__device__ inline int bin_of_slot(const BinPlan &p, int b, int e) {
-  int l = 0;
-  while (l + 1 < p.L && !(e >= p.hist_base[l] && e < p.hist_base[l] + p.M * p.ntiles[l])) ++l;
-  const int rem = e - p.hist_base[l];
-  const int m = rem / p.ntiles[l], t = rem - m * p.ntiles[l];
-  return p.bin_base[l] + (b * p.M + m) * p.ntiles[l] + t;
+// Per-level plan entries, staged in LDS at block start: indexing the kernel
+// argument's arrays with a per-sample level would turn every access into a
+// dependent load from the argument segment.
+struct LevelTab {
+  int H, W, ntx, ntiles, hist_base, bin_base;
+};
+
+__device__ inline void stage_level_tab(const BinPlan &p, LevelTab *t) {
+  if (threadIdx.x < (unsigned)p.L) {
+    const int l = threadIdx.x;
+    t[l] = LevelTab{p.H[l], p.W[l], p.ntx[l], p.ntiles[l], p.hist_base[l], p.bin_base[l]};
+  }
 }
 
-// Histogram slot of sample s (batch-local index, < 2^32) or -1 for a dead sample.
-template <typename T>
-__device__ inline int slot_of_sample(const BinArgs &a, int64_t id, uint32_t s) {
-  const BinPlan &p = a.p;
+// Global bin of batch-local histogram slot e of batch b.
+__device__ inline int bin_of_slot(const BinPlan &p, const LevelTab *lt, int b, int e) {
+  int l = 0;
+  while (l + 1 < p.L && !(e >= lt[l].hist_base && e < lt[l].hist_base + p.M * lt[l].ntiles)) ++l;
+  const int rem = e - lt[l].hist_base;
+  const int m = rem / lt[l].ntiles, t = rem - m * lt[l].ntiles;
+  return lt[l].bin_base + (b * p.M + m) * lt[l].ntiles + t;
+}
+
+// Histogram slot of batch-local sample s (< 2^32) at normalised (u, v), or -1
+// for a dead sample (no corner inside its level).
+__device__ inline int slot_of_sample(const BinPlan &p, const LevelTab *lt, uint32_t s, float u,
+                                     float v) {
   const uint32_t hq = fdiv(s, p.div_lk);
   const uint32_t j = s - hq * (uint32_t)(p.L * p.K);
   const uint32_t m = hq - fdiv(hq, p.div_m) * (uint32_t)p.M;
-  const int l = (int)fdiv(j, p.div_k);
+  const LevelTab t = lt[fdiv(j, p.div_k)];
   Cell c;
-  if (!cell_of(ldf<T>(a.loc, 2 * id), ldf<T>(a.loc, 2 * id + 1), p.H[l], p.W[l], c)) return -1;
-  return p.hist_base[l] + (int)m * p.ntiles[l] + tile_of(p, l, c);
+  if (!cell_of(u, v, t.H, t.W, c)) return -1;
+  return t.hist_base + (int)m * t.ntiles + tile_of(t.ntx, c);
+}
+
+// Sampling location of sample `id` (both coordinates in one load).
+template <typename T>
+__device__ inline void load_loc(const void *loc, int64_t id, float &u, float &v) {
+  if constexpr (sizeof(T) == 4) {
+    const float2 x = reinterpret_cast<const float2 *>(loc)[id];
+    u = x.x;
+    v = x.y;
+  } else {
+    const uint32_t x = reinterpret_cast<const uint32_t *>(loc)[id];
+    u = __uint_as_float(x << 16);
+    v = __uint_as_float(x & 0xffff0000u);
+  }
 }
 
 // --------------------------------------------------------------- count pass
+
+// Every thread owns kPer samples s0 + r*256 + threadIdx.x; all their locations
+// are loaded before any is used, so the loads overlap.
+constexpr int kPer = kCountSamples / 256;
 
 template <typename T>
 __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   extern __shared__ uint32_t hist[];
   const BinPlan &p = a.p;
   const int b = blockIdx.y;
+  const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
+  __shared__ LevelTab lt[kMaxLevels];
+  stage_level_tab(p, lt);
   const int64_t per_b = a.p.Q * p.M * p.L * p.K;
   const int64_t s0 = (int64_t)blockIdx.x * kCountSamples;
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
+  // branch-free loads (clamped index) so all kPer loads are in flight together
+  float u[kPer], v[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t s = min(s0 + r * 256 + (int64_t)threadIdx.x, per_b - 1);
+    load_loc<T>(a.loc, b * per_b + s, u[r], v[r]);
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < kCountSamples; i += blockDim.x) {
-    const int64_t s = s0 + i;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t s = s0 + r * 256 + threadIdx.x;
     if (s >= per_b) break;
     const int64_t id = b * per_b + s;
-    const int e = slot_of_sample<T>(a, id, (uint32_t)s);
+    const int e = slot_of_sample(p, lt, (uint32_t)s, u[r], v[r]);
     if (e < 0) {
       // no corner inside its level: zero gradients, never binned
       store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, 0.0f);
@@ -134,15 +181,26 @@ __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   __syncthreads();
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
     const uint32_t n = hist[e];
-    if (n) __hip_atomic_fetch_add(&a.w.counts[bin_of_slot(p, b, e)], n, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+    if (n) __hip_atomic_fetch_add(&a.w.counts[bin_of_slot(p, lt, b, e) * kStripes + stripe], n,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ---------------------------------------------------------------- plan pass
 
-// One block of 1024 threads: exclusive scans of counts, chunk counts and
-// split-bin slot counts, then the chunk table.
+// Counts of bin i, one per stripe.
+__device__ inline void load_stripes(const BinArgs &a, int i, uint32_t (&c)[kStripes]) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(a.w.counts + (size_t)i * kStripes);
+#pragma unroll
+  for (int k = 0; k < kStripes / 4; ++k) {
+    const uint4 v = src[k];
+    c[4 * k] = v.x; c[4 * k + 1] = v.y; c[4 * k + 2] = v.z; c[4 * k + 3] = v.w;
+  }
+}
+
+// One block of 1024 threads: exclusive scans of the bin counts, chunk counts
+// and split-bin slot counts; then each bin's start, its stripe cursors (each
+// stripe's first sorted position) and its chunk-table entries.
 __global__ __launch_bounds__(1024) void plan_kernel(BinArgs a) {
   __shared__ uint32_t part[3][1024];
   const BinPlan &p = a.p;
@@ -151,7 +209,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(BinArgs a) {
   const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
   uint32_t s_cnt = 0, s_ch = 0, s_slot = 0;
   for (int i = lo; i < hi; ++i) {
-    const uint32_t c = a.w.counts[i];
+    uint32_t cs[kStripes];
+    load_stripes(a, i, cs);
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kStripes; ++k) c += cs[k];
     const uint32_t nch = c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
     s_cnt += c;
     s_ch += nch;
@@ -176,13 +238,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(BinArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == blockDim.x - 1) *a.w.nchunks = part[1][threadIdx.x];
-  // exclusive prefix of this thread's segment
-  part[0][threadIdx.x] -= s_cnt;
-  part[1][threadIdx.x] -= s_ch;
-  part[2][threadIdx.x] -= s_slot;
-  uint32_t pos = part[0][threadIdx.x], ch = part[1][threadIdx.x], slot = part[2][threadIdx.x];
+  uint32_t pos = part[0][threadIdx.x] - s_cnt, ch = part[1][threadIdx.x] - s_ch;
+  uint32_t slot = part[2][threadIdx.x] - s_slot;
   for (int i = lo; i < hi; ++i) {
-    const uint32_t c = a.w.counts[i];
+    uint32_t cs[kStripes];
+    load_stripes(a, i, cs);
+    uint32_t c = 0;
+    uint4 *cur = reinterpret_cast<uint4 *>(a.w.cursor + (size_t)i * kStripes);
+#pragma unroll
+    for (int k = 0; k < kStripes; k += 4) {
+      const uint32_t c0 = pos + c, c1 = c0 + cs[k], c2 = c1 + cs[k + 1], c3 = c2 + cs[k + 2];
+      cur[k / 4] = make_uint4(c0, c1, c2, c3);
+      c += cs[k] + cs[k + 1] + cs[k + 2] + cs[k + 3];
+    }
     const uint32_t nch = c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
     a.w.bin_start[i] = pos;
     a.w.bin_nch[i] = nch;
@@ -202,13 +270,22 @@ __global__ __launch_bounds__(1024) void plan_kernel(BinArgs a) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
-  constexpr int kPer = kCountSamples / 256;
   extern __shared__ uint32_t hist[];
   const BinPlan &p = a.p;
   const int b = blockIdx.y;
+  const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
+  __shared__ LevelTab lt[kMaxLevels];
+  stage_level_tab(p, lt);
   const int64_t per_b = a.p.Q * p.M * p.L * p.K;
   const int64_t s0 = (int64_t)blockIdx.x * kCountSamples;
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
+  // branch-free loads (clamped index) so all kPer loads are in flight together
+  float u[kPer], v[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t s = min(s0 + r * 256 + (int64_t)threadIdx.x, per_b - 1);
+    load_loc<T>(a.loc, b * per_b + s, u[r], v[r]);
+  }
   __syncthreads();
   int slot[kPer];
   uint32_t rank[kPer];
@@ -218,7 +295,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
     slot[r] = -1;
     rank[r] = 0;
     if (s < per_b) {
-      slot[r] = slot_of_sample<T>(a, b * per_b + s, (uint32_t)s);
+      slot[r] = slot_of_sample(p, lt, (uint32_t)s, u[r], v[r]);
       if (slot[r] >= 0)
         rank[r] = __hip_atomic_fetch_add(&hist[slot[r]], 1u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -228,9 +305,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
     const uint32_t n = hist[e];
     if (n) {
-      const int bin = bin_of_slot(p, b, e);
-      hist[e] = a.w.bin_start[bin] + __hip_atomic_fetch_add(&a.w.cursor[bin], n, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
+      // the cursor of (bin, stripe) starts at that stripe's first sorted position
+      const int bin = bin_of_slot(p, lt, b, e);
+      hist[e] = __hip_atomic_fetch_add(&a.w.cursor[bin * kStripes + stripe], n, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();
@@ -249,23 +327,27 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
 struct SampleRec {
   uint32_t id;  // sample id
   float a;      // attention weight
-  float lx, ly; // fractional parts of the pixel coordinate
+  float u, v;   // normalised sampling location
 };
 
-// Channels per lane / lanes per sample for fp32 rows of D channels in LDS.
+// Lanes per sample and channels per lane for fp32 rows of D channels in LDS:
+// 4 lanes x 8 channels for D = 32 keeps the cross-lane reductions to two
+// steps; RS pads LDS rows by 16 bytes against bank conflicts.
 template <int D>
 struct TileLayout {
-  static constexpr int VEC = D >= 16 ? 4 : 2;
+  static constexpr int VEC = D >= 32 ? 8 : D / 4;
   static constexpr int G = D / VEC;
-  static constexpr int RS = D + 4;  // LDS row stride in floats (16-byte pad against bank conflicts)
+  static constexpr int RS = D + 4;
 };
 
-// LDS carve-up of the tile kernel (floats unless stated):
-//   vt     [kEdge^2 + 1][RS]   value rows of the tile and its rim, then one zero row
-//   stage  [kCells][4][RS]     per-cell corner sums; also the unsorted records in phase A
-//   sorted [kChunk]            SampleRec, sorted by cell
-//   tag    [kChunk] u32        cell | rank << 8 of each unsorted record (~0: dropped)
-//   cnt    [kCells + 1] u32    samples per cell, then (after the scan) the cell starts
+// LDS carve-up of the tile kernel (bytes):
+//   vt     [kEdge^2 + 1][RS] f32  value rows of the tile and its rim, then one zero row
+//   stage  [kCells][4][RS] f32    per-cell corner sums; holds the unsorted records in phase A
+//   sorted [kChunk] SampleRec     samples sorted by cell
+//   tag    [kChunk] u32           cell | rank << 8 of each unsorted record (~0: dropped)
+//   cnt    [kCells + 1] u32       samples per cell
+//   cstart [kCells + 1] u32       first sorted position of each cell
+//   order  [kCells] u32           cells by decreasing sample count
 template <int D>
 struct TileSmem {
   static constexpr int RS = TileLayout<D>::RS;
@@ -277,20 +359,44 @@ struct TileSmem {
   static constexpr size_t sorted = stage + stage_bytes;
   static constexpr size_t tag = sorted + (size_t)kChunk * sizeof(SampleRec);
   static constexpr size_t cnt = tag + (size_t)kChunk * 4;
-  static constexpr size_t bytes = cnt + (size_t)(kCells + 1) * 4 * 2;
+  static constexpr size_t cstart = cnt + (size_t)(kCells + 1) * 4;
+  static constexpr size_t order = cstart + (size_t)(kCells + 1) * 4;
+  static constexpr size_t bytes = order + (size_t)kCells * 4;
 };
 
-__device__ inline void decode_bin(const BinPlan &p, int bin, int &l, int &b, int &m, int &ty,
-                                  int &tx) {
-  l = 0;
-  while (l + 1 < p.L && !(bin >= p.bin_base[l] && bin < p.bin_base[l] + (int)p.B * p.M * p.ntiles[l]))
-    ++l;
-  const int rem = bin - p.bin_base[l];
-  const int bm = rem / p.ntiles[l], t = rem - bm * p.ntiles[l];
-  b = bm / p.M;
-  m = bm - b * p.M;
-  ty = t / p.ntx[l];
-  tx = t - ty * p.ntx[l];
+// Level, batch, head and tile of a bin.  The search runs over compile-time
+// level indices only, so the plan arrays stay in scalar registers instead of
+// being fetched from the argument segment with a computed index.
+struct BinPos {
+  int l, b, m, ty, tx, H, W, ntx;
+};
+
+__device__ inline BinPos decode_bin(const BinPlan &p, int bin) {
+  const int BM = (int)p.B * p.M;
+  int l = 0, base = 0, nt = 1, ntx = 1, H = 1, W = 1;
+#pragma unroll
+  for (int k = 0; k < kMaxLevels; ++k) {
+    if (k < p.L && bin >= p.bin_base[k] && bin < p.bin_base[k] + BM * p.ntiles[k]) {
+      l = k;
+      base = p.bin_base[k];
+      nt = p.ntiles[k];
+      ntx = p.ntx[k];
+      H = p.H[k];
+      W = p.W[k];
+    }
+  }
+  BinPos r;
+  const int rem = bin - base;
+  const int bm = rem / nt, t = rem - bm * nt;
+  r.l = l;
+  r.b = bm / p.M;
+  r.m = bm - r.b * p.M;
+  r.ty = t / ntx;
+  r.tx = t - r.ty * ntx;
+  r.H = H;
+  r.W = W;
+  r.ntx = ntx;
+  return r;
 }
 
 // Rim row (0 .. 4T-1) of tile-local pixel (iy, ix) that is an edge or halo pixel:
@@ -305,20 +411,27 @@ __device__ inline int rim_row(int iy, int ix) {
   return 3 * kTile + iy;  // ix == 0, iy >= 1
 }
 
+// VEC consecutive elements of T at element offset e (a multiple of VEC), as fp32.
 template <typename T, int VEC>
-__device__ inline void load_grad_out_row(const BinArgs &a, uint32_t id, int lane, float (&g)[VEC]) {
-  const int64_t hq = fdiv(id, a.p.div_lk);
-  const T *src = reinterpret_cast<const T *>(a.grad_out) + hq * a.p.D + lane * VEC;
-  if constexpr (sizeof(T) == 4 && VEC == 4) {
-    const float4 v = *reinterpret_cast<const float4 *>(src);
-    g[0] = v.x; g[1] = v.y; g[2] = v.z; g[3] = v.w;
-  } else if constexpr (sizeof(T) == 2 && VEC == 4) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(src);
-    g[0] = __uint_as_float(v.x << 16); g[1] = __uint_as_float(v.x & 0xffff0000u);
-    g[2] = __uint_as_float(v.y << 16); g[3] = __uint_as_float(v.y & 0xffff0000u);
+__device__ inline void load_vec(const void *base, int64_t e, float (&o)[VEC]) {
+  const T *src = reinterpret_cast<const T *>(base) + e;
+  if constexpr (sizeof(T) == 4 && VEC % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) {
+      const float4 v = reinterpret_cast<const float4 *>(src)[k];
+      o[4 * k] = v.x; o[4 * k + 1] = v.y; o[4 * k + 2] = v.z; o[4 * k + 3] = v.w;
+    }
+  } else if constexpr (sizeof(T) == 2 && VEC == 8) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(src);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = __uint_as_float(w[k] << 16);
+      o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) g[i] = to_float<T>(src[i]);
+    for (int i = 0; i < VEC; ++i) o[i] = to_float<T>(src[i]);
   }
 }
 
@@ -329,6 +442,9 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   constexpr int VEC = TL::VEC, G = TL::G, RS = TL::RS;
   constexpr int NROWS = kEdge * kEdge;
   constexpr int kZeroRow = NROWS;
+  constexpr int NG = 256 / G;
+  constexpr int kPer = kChunk / 256;                 // phase-A samples per thread
+  constexpr int kRowIters = (NROWS + 1 + NG - 1) / NG;
   constexpr uint32_t kDropped = 0xffffffffu;
   extern __shared__ __align__(16) char smem[];
   float *vt = reinterpret_cast<float *>(smem + SM::vt);
@@ -336,58 +452,79 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   SampleRec *raw = reinterpret_cast<SampleRec *>(smem + SM::stage);  // phase A only
   SampleRec *sorted = reinterpret_cast<SampleRec *>(smem + SM::sorted);
   uint32_t *tag = reinterpret_cast<uint32_t *>(smem + SM::tag);
-  uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + SM::cnt);   // [kCells + 1]
-  uint32_t *cstart = cnt + kCells + 1;                              // [kCells + 1]
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + SM::cnt);
+  uint32_t *cstart = reinterpret_cast<uint32_t *>(smem + SM::cstart);
+  uint32_t *order = reinterpret_cast<uint32_t *>(smem + SM::order);
 
   const BinPlan &p = a.p;
   if (blockIdx.x >= *a.w.nchunks) return;
   const uint4 ck = a.w.chunks[blockIdx.x];
   const int bin = (int)ck.x;
   const uint32_t first = ck.y, count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
-  int l, b, m, ty, tx;
-  decode_bin(p, bin, l, b, m, ty, tx);
-  const int H = p.H[l], W = p.W[l];
+  const BinPos bp = decode_bin(p, bin);
+  const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
   const int px0 = tx * kTile, py0 = ty * kTile;
   const int64_t start = a.starts[l];
   const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
   const int grp = threadIdx.x / G, lane = threadIdx.x % G;
-  constexpr int NG = 256 / G;
 
-  // stage value rows (zero outside the map) and clear the cell counters
-  for (int r = grp; r < NROWS + 1; r += NG) {
+  // ---- loads first: sample ids and value rows together, then locations
+  for (int c = threadIdx.x; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
+  // branch-free loads (clamped indices) so they are all in flight together
+  uint32_t ids[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const uint32_t i = threadIdx.x + r * 256;
+    const uint32_t id = a.w.ids[count > 0 ? first + min(i, count - 1) : 0u];
+    ids[r] = i < count ? id : kDropped;
+  }
+  float vrow[kRowIters][VEC];
+  bool vin[kRowIters];
+#pragma unroll
+  for (int k = 0; k < kRowIters; ++k) {
+    const int r = grp + k * NG;
     const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
     const int py = py0 + iy, px = px0 + ix;
     const int64_t prow = start + (int64_t)py * W + px;  // pyramid row inside the batch image
-    float v[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
-    if (count > 0 && r < NROWS && py < H && px < W && prow >= 0 && prow < p.S) {
-      const int64_t e = (((int64_t)b * p.S + prow) * p.M + m) * D + lane * VEC;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] = ldf<T>(a.value, e + i);
-    }
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) vt[r * RS + lane * VEC + i] = v[i];
+    vin[k] = count > 0 && r < NROWS && py < H && px < W && prow >= 0 && prow < p.S;
+    // branch-free: rows outside the map load the level's first row and are zeroed below
+    const int64_t row = vin[k] ? prow : (start >= 0 && start < p.S ? start : 0);
+    load_vec<T, VEC>(a.value, (((int64_t)b * p.S + row) * p.M + m) * D + lane * VEC, vrow[k]);
   }
-  for (int c = threadIdx.x; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
+  float lu[kPer], lv[kPer], la[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const uint32_t id = min(ids[r], p.total - 1);
+    load_loc<T>(a.loc, id, lu[r], lv[r]);
+    la[r] = ldf<T>(a.attn, id);
+  }
+#pragma unroll
+  for (int k = 0; k < kRowIters; ++k) {
+    const int r = grp + k * NG;
+    if (r < NROWS + 1)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) vt[r * RS + lane * VEC + i] = vin[k] ? vrow[k][i] : 0.0f;
+  }
   __syncthreads();
 
-  // phase A: geometry of each sample, its cell, and its rank inside the cell
-  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+  // ---- phase A: cell of each sample and its rank inside the cell
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const uint32_t i = threadIdx.x + r * 256;
+    if (i >= count) break;
     uint32_t t = kDropped;
-    const uint32_t id = a.w.ids[first + i];
+    const uint32_t id = ids[r];
     if (id < p.total) {
       const uint32_t hq = fdiv(id, p.div_lk);
       const uint32_t j = id - hq * (uint32_t)(p.L * p.K);
       Cell c;
-      if ((int)fdiv(j, p.div_k) == l &&
-          cell_of(ldf<T>(a.loc, 2 * (int64_t)id), ldf<T>(a.loc, 2 * (int64_t)id + 1), H, W, c)) {
+      if ((int)fdiv(j, p.div_k) == l && cell_of(lu[r], lv[r], H, W, c)) {
         const int cy = c.y0 - py0 + 1, cx = c.x0 - px0 + 1;
         if (cy >= 0 && cy < kEdge && cx >= 0 && cx < kEdge) {
           const uint32_t cell = (uint32_t)(cy * kEdge + cx);
           const uint32_t rank = __hip_atomic_fetch_add(&cnt[cell], 1u, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_WORKGROUP);
-          raw[i] = SampleRec{id, ldf<T>(a.attn, id), c.lx, c.ly};
+          raw[i] = SampleRec{id, la[r], lu[r], lv[r]};
           t = cell | (rank << 8);
         }
       }
@@ -410,17 +547,34 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     if (i1 <= kCells) cstart[i1] = exc + c0;
   }
   __syncthreads();
+  // scatter the records into cell order; rank the cells by decreasing count
   for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
     const uint32_t t = tag[i];
     if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
   }
+  if (threadIdx.x < kCells) {
+    const uint32_t c = threadIdx.x, n = cnt[c];
+    uint32_t rank = 0;
+    for (uint32_t o = 0; o < (uint32_t)kCells; ++o) {
+      const uint32_t no = cnt[o];
+      rank += (no > n || (no == n && o < c)) ? 1u : 0u;
+    }
+    order[rank] = c;
+  }
   __syncthreads();
 
-  // cell loop: one group per cell, corner rows and sums in registers
-  for (int cell = grp; cell < kCells; cell += NG) {
+  // ---- cell loop: one group per cell (largest cells first, snaking over the
+  // groups so the groups of a wave get cells of similar size); the cell's
+  // corner rows (fp64) and its four corner sums (fp32) stay in registers
+  for (int round = 0; round * NG < kCells; ++round) {
+    const int rank = round * NG + ((round & 1) ? NG - 1 - grp : grp);
+    if (rank >= kCells) continue;
+    const int cell = (int)order[rank];
     const int cy = cell / kEdge, cx = cell - (cell / kEdge) * kEdge;
     const uint32_t s0 = cstart[cell], n = cstart[cell + 1] - s0;
-    float V[4][VEC], acc[4][VEC];
+    const double x0 = (double)(px0 + cx - 1), y0 = (double)(py0 + cy - 1);
+    double V[4][VEC];
+    float acc[4][VEC];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // corner q of cell (cy, cx) is tile-local pixel (cy - 1 + q/2, cx - 1 + q%2)
@@ -429,7 +583,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       const float *src = vt + (in ? iy * kEdge + ix : kZeroRow) * RS + lane * VEC;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
-        V[q][i] = n ? src[i] : 0.0f;
+        V[q][i] = (double)src[i];
         acc[q][i] = 0.0f;
       }
     }
@@ -440,36 +594,42 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         rec[u] = sorted[s0 + min(k0 + u, n - 1)];
-        load_grad_out_row<T, VEC>(a, rec[u].id, lane, g[u]);
+        load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(rec[u].id, p.div_lk) * D + lane * VEC, g[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (k0 + u >= n) break;
-        float pc[4];
+        // fp64 partial dot products <g, V_c> over this lane's channels (exact products)
+        double pc[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float sum = 0.0f;
+          double sum = 0.0;
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) sum = fmaf(g[u][i], V[q][i], sum);
-          pc[q] = group_sum<G>(sum);
+          for (int i = 0; i < VEC; ++i) sum = fma((double)g[u][i], V[q][i], sum);
+          pc[q] = sum;
         }
-        const float lx = rec[u].lx, ly = rec[u].ly, av = rec[u].a;
-        const float w[4] = {(1.0f - lx) * (1.0f - ly), lx * (1.0f - ly), (1.0f - lx) * ly, lx * ly};
+        const double lx = ((double)rec[u].u * (double)W - 0.5) - x0;
+        const double ly = ((double)rec[u].v * (double)H - 0.5) - y0;
+        const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
+        const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
+        // grad_attn = sum_c w_c p_c ; grad_loc = (A W d/dlx, A H d/dly), all linear in the p_c
+        const double ga = group_sum_f64<G>(w0 * pc[0] + w1 * pc[1] + w2 * pc[2] + w3 * pc[3]);
+        const double gx = group_sum_f64<G>((1.0 - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
+        const double gy = group_sum_f64<G>((1.0 - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
+        const float av = rec[u].a;
         if (lane == 0) {
           const uint32_t id = rec[u].id;
-          const float ga = w[0] * pc[0] + w[1] * pc[1] + w[2] * pc[2] + w[3] * pc[3];
-          const float gx = av * (float)W * ((1.0f - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
-          const float gy = av * (float)H * ((1.0f - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
-          store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, ga);
-          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id, gx);
-          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id + 1, gy);
+          store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, (float)ga);
+          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id,
+                          (float)((double)av * (double)W * gx));
+          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id + 1,
+                          (float)((double)av * (double)H * gy));
         }
+        const float aw[4] = {av * (float)w0, av * (float)w1, av * (float)w2, av * (float)w3};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float aw = av * w[q];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw, g[u][i], acc[q][i]);
-        }
+          for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw[q], g[u][i], acc[q][i]);
       }
     }
 #pragma unroll
@@ -479,7 +639,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   }
   __syncthreads();
 
-  // every pixel of the tile and its rim sums the cells it is a corner of, then
+  // ---- every pixel of the tile and its rim sums the cells it is a corner of, then
   // goes to grad_value (interior), the rim (edge / halo) or the chunk's slot
   for (int r = grp; r < NROWS; r += NG) {
     const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
@@ -529,12 +689,22 @@ __device__ inline void add_part(const BinArgs &a, int nb, int iy, int ix, int la
 #pragma unroll
     for (int i = 0; i < VEC; ++i) v[i] += src[i];
   } else {
+    // four independent partial sums so the slot loads overlap
     const uint32_t s0 = a.w.bin_slot0[nb];
-    for (uint32_t k = 0; k < nch; ++k) {
-      const float *src = a.w.slots + ((int64_t)(s0 + k) * E * E + iy * E + ix) * D + lane * VEC;
+    const int64_t stride = (int64_t)E * E * D;
+    const float *base = a.w.slots + ((int64_t)s0 * E * E + iy * E + ix) * D + lane * VEC;
+    float part[4][VEC] = {};
+    uint32_t k = 0;
+    for (; k + 4 <= nch; k += 4)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] += src[i];
-    }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) part[j][i] += base[(k + j) * stride + i];
+    for (; k < nch; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) part[0][i] += base[k * stride + i];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] += (part[0][i] + part[1][i]) + (part[2][i] + part[3][i]);
   }
 }
 
@@ -545,9 +715,9 @@ __global__ __launch_bounds__(256) void merge_kernel(BinArgs a) {
   constexpr int NG = 256 / G;
   const BinPlan &p = a.p;
   const int bin = blockIdx.x;
-  int l, b, m, ty, tx;
-  decode_bin(p, bin, l, b, m, ty, tx);
-  const int H = p.H[l], W = p.W[l], ntx = p.ntx[l];
+  const BinPos bp = decode_bin(p, bin);
+  const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
+  const int ntx = bp.ntx;
   const int px0 = tx * kTile, py0 = ty * kTile;
   const int64_t row0 = (int64_t)b * p.S + a.starts[l];
   const bool split = a.w.bin_nch[bin] > 1;
@@ -623,8 +793,8 @@ template <typename T>
 hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   const BinPlan &p = a.p;
   hipError_t e;
-  // counts and cursor are adjacent: clear both
-  e = launch_zero(a.w.counts, (size_t)2 * ((p.nbins + 3) / 4 * 4) * sizeof(uint32_t), s);
+  // the striped counts start at zero; the plan writes the cursors
+  e = launch_zero(a.w.counts, (size_t)p.nbins * kStripes * sizeof(uint32_t), s);
   if (e != hipSuccess) return e;
   if (p.S > p.pyramid_rows) {
     prof_begin(s);
@@ -734,7 +904,8 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
     return base ? base + o : nullptr;
   };
   const size_t nb4 = (size_t)(p.nbins + 3) / 4 * 4;
-  char *cc = take(2 * nb4 * sizeof(uint32_t));  // counts + cursor, cleared together
+  char *cc = take((size_t)p.nbins * kStripes * sizeof(uint32_t));
+  char *cu = take((size_t)p.nbins * kStripes * sizeof(uint32_t));
   char *bs = take(nb4 * sizeof(uint32_t));
   char *bn = take(nb4 * sizeof(uint32_t));
   char *b0 = take(nb4 * sizeof(uint32_t));
@@ -745,7 +916,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
   char *sl = take((size_t)p.max_slots * E * E * p.D * sizeof(float));
   if (w) {
     w->counts = reinterpret_cast<uint32_t *>(cc);
-    w->cursor = reinterpret_cast<uint32_t *>(cc) + nb4;
+    w->cursor = reinterpret_cast<uint32_t *>(cu);
     w->bin_start = reinterpret_cast<uint32_t *>(bs);
     w->bin_nch = reinterpret_cast<uint32_t *>(bn);
     w->bin_slot0 = reinterpret_cast<uint32_t *>(b0);

@@ -259,6 +259,25 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
+template <int CTRL>
+__device__ inline double dpp_move_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// fp64 sum over an aligned group of G lanes (same pattern as group_sum).
+template <int G>
+__device__ inline double group_sum_f64(double x) {
+  static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
+  x += dpp_move_f64<kDppQuadXor1>(x);
+  x += dpp_move_f64<kDppQuadXor2>(x);
+  if constexpr (G >= 8) x += dpp_move_f64<kDppRowHalfMirror>(x);
+  if constexpr (G >= 16) x += dpp_move_f64<kDppRowMirror>(x);
+  return x;
+}
+
 // ----------------------------------------------------------- lane layout
 
 // How a head row (D channels of T) is spread over a group of lanes: each lane

@@ -36,8 +36,8 @@ constexpr int kGeoLdsBudget = 64 * 1024;
 // Per-sample data the backward needs beyond the corners.
 struct SampleAux {
   float a;   // attention weight (0 for a sample with no corner inside)
-  float lx;  // fractional parts of the pixel coordinate
-  float ly;
+  float u;   // normalised location (the fractions are recomputed in fp64)
+  float v;
   int l;     // level
 };
 
@@ -45,6 +45,24 @@ template <typename T>
 __device__ inline float ld(const void *base, int64_t i) {
   return to_float<T>(reinterpret_cast<const T *>(base)[i]);
 }
+
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// block index.  Remap so that XCD x runs one contiguous range of logical
+// blocks: neighbouring head-queries, which sample neighbouring pixels, then
+// share that XCD's L2.  The grid is a multiple of 8; logical blocks past the
+// end return at once.
+constexpr int kXcds = 8;
+
+__device__ inline int64_t logical_block() {
+#ifdef MSDA_NO_XCD_REMAP
+  return blockIdx.x;
+#else
+  const uint32_t per = gridDim.x / kXcds;
+  return (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+#endif
+}
+
+inline int64_t padded_grid(int64_t blocks) { return (blocks + kXcds - 1) / kXcds * kXcds; }
 
 __device__ inline void stage_levels(Level *lv, const LaunchArgs &a) {
   if (threadIdx.x < a.L) {
@@ -66,7 +84,8 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
 
   const int K = (int)a.K, LK = (int)(a.L * a.K), M = (int)a.M;
   const int64_t total_hq = a.nb * a.Q * a.M;
-  const int64_t hq0 = (int64_t)blockIdx.x * hqb;
+  const int64_t hq0 = logical_block() * hqb;
+  if (hq0 >= total_hq) return;
   const int nhq = (int)min((int64_t)hqb, total_hq - hq0);
   stage_levels(lv, a);
   __syncthreads();
@@ -162,7 +181,8 @@ __global__ __launch_bounds__(kMaxBlock) void bwd_kernel(LaunchArgs a, int hqb) {
   float *res = reinterpret_cast<float *>(aux + LK * hqb);      // [hqb*LK][3] in sample order
 
   const int64_t total_hq = a.nb * a.Q * a.M;
-  const int64_t hq0 = (int64_t)blockIdx.x * hqb;
+  const int64_t hq0 = logical_block() * hqb;
+  if (hq0 >= total_hq) return;
   const int nhq = (int)min((int64_t)hqb, total_hq - hq0);
   stage_levels(lv, a);
   __syncthreads();
@@ -180,9 +200,12 @@ __global__ __launch_bounds__(kMaxBlock) void bwd_kernel(LaunchArgs a, int hqb) {
     const float w = ld<T>(a.attn, gs);
     Corners cs;
     SampleAux ax;
+    float lx, ly;
     const bool any = sample_corners(u, v, lv[j / K], (uint32_t)(b * a.S), row_stride,
-                                    (uint32_t)(m * D * (int)sizeof(T)), cs, ax.lx, ax.ly);
+                                    (uint32_t)(m * D * (int)sizeof(T)), cs, lx, ly);
     ax.a = any ? w : 0.0f;
+    ax.u = u;
+    ax.v = v;
     ax.l = j / K;
     geo[j * hqb + hl] = cs;
     aux[j * hqb + hl] = ax;
@@ -210,26 +233,33 @@ __global__ __launch_bounds__(kMaxBlock) void bwd_kernel(LaunchArgs a, int hqb) {
       uint32_t raw[4][RL::WORDS];
 #pragma unroll
       for (int c = 0; c < 4; ++c) buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[c]);
-      float p[4];
+      // fp64 partial dot products <g, V_c> (exact products), reduced across the group
+      double p[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float x[RL::VEC];
         unpack<T, RL::WORDS>(raw[c], x);
-        float s = 0.0f;
+        double s = 0.0;
 #pragma unroll
-        for (int i = 0; i < RL::VEC; ++i) s = fmaf(g[i], x[i], s);
-        p[c] = group_sum<G>(s);
+        for (int i = 0; i < RL::VEC; ++i) s = fma((double)g[i], (double)x[i], s);
+        p[c] = s;
       }
+      const int W = lv[ax.l].W, H = lv[ax.l].H;
+      const double x = (double)ax.u * (double)W - 0.5, y = (double)ax.v * (double)H - 0.5;
+      const double lx = x - floor(x), ly = y - floor(y);
+      // bilinear weights in fp64; 0 for corners outside the level (their p_c is 0 too)
+      const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
+      const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
+      const double ga = group_sum_f64<G>(w0 * p[0] + w1 * p[1] + w2 * p[2] + w3 * p[3]);
+      const double gx = group_sum_f64<G>((1.0 - ly) * (p[1] - p[0]) + ly * (p[3] - p[2]));
+      const double gy = group_sum_f64<G>((1.0 - lx) * (p[2] - p[0]) + lx * (p[3] - p[1]));
       if (lane == 0) {
-        const float lx = ax.lx, ly = ax.ly;
-        const float ga = cs.w[0] * p[0] + cs.w[1] * p[1] + cs.w[2] * p[2] + cs.w[3] * p[3];
-        const float aW = ax.a * (float)lv[ax.l].W, aH = ax.a * (float)lv[ax.l].H;
-        const float gx = aW * ((1.0f - ly) * (p[1] - p[0]) + ly * (p[3] - p[2]));
-        const float gy = aH * ((1.0f - lx) * (p[2] - p[0]) + lx * (p[3] - p[1]));
         const int s = grp * LK + j;
-        res[3 * s] = ga;
-        res[3 * s + 1] = gx;
-        res[3 * s + 2] = gy;
+        const bool live = ax.a != 0.0f || cs.off[0] != kOutside || cs.off[1] != kOutside ||
+                          cs.off[2] != kOutside || cs.off[3] != kOutside;
+        res[3 * s] = live ? (float)ga : 0.0f;
+        res[3 * s + 1] = live ? (float)((double)ax.a * W * gx) : 0.0f;
+        res[3 * s + 2] = live ? (float)((double)ax.a * H * gy) : 0.0f;
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -282,7 +312,7 @@ hipError_t fwd_launch(const LaunchArgs &a, hipStream_t stream) {
   const int LK = (int)(a.L * a.K);
   const int hqb = pick_hqb(RL::G, LK, (int)sizeof(Corners));
   const int64_t total_hq = a.nb * a.Q * a.M;
-  const int64_t blocks = (total_hq + hqb - 1) / hqb;
+  const int64_t blocks = padded_grid((total_hq + hqb - 1) / hqb);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t lds = (size_t)LK * hqb * sizeof(Corners);
   prof_begin(stream);
@@ -299,7 +329,7 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
   constexpr int per_sample = (int)(sizeof(Corners) + sizeof(SampleAux) + 3 * sizeof(float));
   const int hqb = pick_hqb(RL::G, LK, per_sample);
   const int64_t total_hq = a.nb * a.Q * a.M;
-  const int64_t blocks = (total_hq + hqb - 1) / hqb;
+  const int64_t blocks = padded_grid((total_hq + hqb - 1) / hqb);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t lds = (size_t)LK * hqb * per_sample;
   prof_begin(stream);

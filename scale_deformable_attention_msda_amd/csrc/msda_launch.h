@@ -59,8 +59,8 @@ struct BinPlan {
 // Device scratch carved out of the caller's workspace (byte offsets into it
 // are fixed by binned_layout()).
 struct BinScratch {
-  uint32_t *counts;     // [nbins] samples per bin
-  uint32_t *cursor;     // [nbins] fill cursor of the id scatter
+  uint32_t *counts;     // [nbins][stripes] samples per bin, per block stripe
+  uint32_t *cursor;     // [nbins][stripes] fill cursor of the id scatter
   uint32_t *bin_start;  // [nbins] first sorted position of a bin
   uint32_t *bin_nch;    // [nbins] chunks of a bin
   uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
