@@ -45,7 +45,8 @@ def bytes_model(wl: workloads.Workload) -> dict:
     For the encoder workloads every pyramid pixel is the reference point of a
     query and offsets are a few pixels, so every value row is touched and the
     whole value tensor counts.  Per-sample figures: loc 2 elements, attn 1
-    element, a 4-byte sample id for the binned path."""
+    element; the binned path also writes and reads one 16-byte record
+    (id, location, weight) per sample."""
     elt = 4 if wl.dtype == "fp32" else 2
     B, S, Q, M, D, L, K = wl.B, wl.S, wl.num_queries, wl.M, wl.D, wl.L, wl.K
     n = B * Q * M * L * K
@@ -53,7 +54,7 @@ def bytes_model(wl: workloads.Workload) -> dict:
     loc = n * 2 * elt
     attn = n * elt
     out = B * Q * M * D * elt
-    ids = n * 4
+    recs = n * 16
     return {
         "samples": n,
         # forward: gather value, read loc / attn, write out
@@ -63,12 +64,47 @@ def bytes_model(wl: workloads.Workload) -> dict:
         "zero": value,
         # binned passes
         "bin_count": loc,
-        "bin_scatter": loc + ids,
-        "bin_tile": value + ids + loc + attn + out + value + loc + attn,
+        "bin_scatter": loc + attn + recs,
+        "bin_tile": value + recs + out + value + loc + attn,
         "bin_merge": 0,
         "bin_plan": 0,
         "value": value,
     }
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources: measured traffic is void once they change."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scale_deformable_attention_msda_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str, workload: str, scatter: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a profiles/ summary, or None.
+
+    The summary holds lines `sources: <digest>` and
+    `traffic <workload>/<scatter>/<kernel>: <bytes>`; figures taken from other
+    sources than the current ones are ignored."""
+    if not os.path.exists(path):
+        return None
+    digest, key, value = None, f"traffic {workload}/{scatter}/{kernel}:", None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("sources:"):
+            digest = line.split(":", 1)[1].strip()
+        elif line.startswith(key):
+            try:
+                value = int(float(line.split(":", 1)[1].split()[0]))
+            except (ValueError, IndexError):
+                value = None
+    if digest != kernel_source_digest():
+        return None
+    return value
 
 
 def cpu_baseline(x: dict, budget_s: float = 10.0) -> dict:
@@ -108,8 +144,10 @@ def main(argv=None) -> int:
     ap.add_argument("--scatter", default="binned", choices=["binned", "atomic"],
                     help="how the backward forms grad_value")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_encoder.txt"),
                     help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -124,6 +162,16 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         log("no GPU visible")
         return 1
+    if args.calibrate_copy:
+        # a copy of known size: FETCH_SIZE / WRITE_SIZE of its kernel calibrate the counters
+        n = 256 * 2 ** 20 // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}))
+        return 0
     msda.load_library()
     wl = workloads.WORKLOADS[args.workload]
     dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
@@ -194,15 +242,7 @@ def main(argv=None) -> int:
     dom_name = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"])
     dom = kernels[dom_name]
     achieved = dom["alg_bytes"] / (dom["us"] * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            rec = tj.get(f"{wl.name}/{args.scatter}/{dom_name}")
-            if rec and rec.get("valid", False):
-                traffic = rec["bytes_per_launch"]
-        except (OSError, ValueError, KeyError):
-            traffic = None
+    traffic = read_traffic(args.traffic_file, wl.name, args.scatter, dom_name)
     step_bytes = bm["fwd"] + (bm["bwd_atomic"] if args.scatter == "atomic" else bm["bin_tile"])
     res = {
         "metric": METRIC,

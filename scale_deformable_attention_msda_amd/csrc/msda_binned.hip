@@ -19,7 +19,9 @@
 //   plan     one block: exclusive scan -> bin starts, chunks of <= `chunk`
 //            samples per bin, partial-tile slots for bins split in chunks;
 //   scatter  recount in LDS, reserve each block's range per bin with one
-//            atomic, write sample ids in bin order;
+//            atomic, write a 16-byte record (id, location, weight) of every
+//            sample in bin order, so the tile pass reads its samples
+//            contiguously instead of gathering 8- and 4-byte pieces;
 //   tile     one block per chunk: stage the (T+1)^2 value rows of the tile
 //            (plus rim) in LDS, counting-sort the chunk's samples by their
 //            bilinear cell (integer LDS atomics), then one lane group per
@@ -287,6 +289,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
     load_loc<T>(a.loc, b * per_b + s, u[r], v[r]);
   }
   __syncthreads();
+  float aw[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t s = min(s0 + r * 256 + (int64_t)threadIdx.x, per_b - 1);
+    aw[r] = ldf<T>(a.attn, b * per_b + s);
+  }
   int slot[kPer];
   uint32_t rank[kPer];
 #pragma unroll
@@ -316,7 +324,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
   for (int r = 0; r < kPer; ++r) {
     if (slot[r] >= 0) {
       const int64_t s = s0 + r * 256 + threadIdx.x;
-      a.w.ids[hist[slot[r]] + rank[r]] = (uint32_t)(b * per_b + s);
+      a.w.recs[hist[slot[r]] + rank[r]] = make_uint4((uint32_t)(b * per_b + s), __float_as_uint(u[r]),
+                                                     __float_as_uint(v[r]), __float_as_uint(aw[r]));
     }
   }
 }
@@ -468,15 +477,14 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
   const int grp = threadIdx.x / G, lane = threadIdx.x % G;
 
-  // ---- loads first: sample ids and value rows together, then locations
+  // ---- loads first: the chunk's sample records and the tile's value rows,
+  // all branch-free (clamped indices) so they are in flight together
   for (int c = threadIdx.x; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
-  // branch-free loads (clamped indices) so they are all in flight together
-  uint32_t ids[kPer];
+  uint4 rc[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const uint32_t i = threadIdx.x + r * 256;
-    const uint32_t id = a.w.ids[count > 0 ? first + min(i, count - 1) : 0u];
-    ids[r] = i < count ? id : kDropped;
+    rc[r] = a.w.recs[count > 0 ? first + min(i, count - 1) : 0u];
   }
   float vrow[kRowIters][VEC];
   bool vin[kRowIters];
@@ -490,13 +498,6 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     // branch-free: rows outside the map load the level's first row and are zeroed below
     const int64_t row = vin[k] ? prow : (start >= 0 && start < p.S ? start : 0);
     load_vec<T, VEC>(a.value, (((int64_t)b * p.S + row) * p.M + m) * D + lane * VEC, vrow[k]);
-  }
-  float lu[kPer], lv[kPer], la[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const uint32_t id = min(ids[r], p.total - 1);
-    load_loc<T>(a.loc, id, lu[r], lv[r]);
-    la[r] = ldf<T>(a.attn, id);
   }
 #pragma unroll
   for (int k = 0; k < kRowIters; ++k) {
@@ -513,18 +514,19 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     const uint32_t i = threadIdx.x + r * 256;
     if (i >= count) break;
     uint32_t t = kDropped;
-    const uint32_t id = ids[r];
+    const uint32_t id = rc[r].x;
+    const float su = __uint_as_float(rc[r].y), sv = __uint_as_float(rc[r].z);
     if (id < p.total) {
       const uint32_t hq = fdiv(id, p.div_lk);
       const uint32_t j = id - hq * (uint32_t)(p.L * p.K);
       Cell c;
-      if ((int)fdiv(j, p.div_k) == l && cell_of(lu[r], lv[r], H, W, c)) {
+      if ((int)fdiv(j, p.div_k) == l && cell_of(su, sv, H, W, c)) {
         const int cy = c.y0 - py0 + 1, cx = c.x0 - px0 + 1;
         if (cy >= 0 && cy < kEdge && cx >= 0 && cx < kEdge) {
           const uint32_t cell = (uint32_t)(cy * kEdge + cx);
           const uint32_t rank = __hip_atomic_fetch_add(&cnt[cell], 1u, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_WORKGROUP);
-          raw[i] = SampleRec{id, la[r], lu[r], lv[r]};
+          raw[i] = SampleRec{id, __uint_as_float(rc[r].w), su, sv};
           t = cell | (rank << 8);
         }
       }
@@ -911,7 +913,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
   char *b0 = take(nb4 * sizeof(uint32_t));
   char *nc = take(16);
   char *ch = take((size_t)p.max_chunks * sizeof(uint4));
-  char *ids = take((size_t)p.total * sizeof(uint32_t));
+  char *recs = take((size_t)p.total * sizeof(uint4));
   char *rim = take((size_t)p.nbins * 4 * kTile * p.D * sizeof(float));
   char *sl = take((size_t)p.max_slots * E * E * p.D * sizeof(float));
   if (w) {
@@ -922,7 +924,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
     w->bin_slot0 = reinterpret_cast<uint32_t *>(b0);
     w->nchunks = reinterpret_cast<uint32_t *>(nc);
     w->chunks = reinterpret_cast<uint4 *>(ch);
-    w->ids = reinterpret_cast<uint32_t *>(ids);
+    w->recs = reinterpret_cast<uint4 *>(recs);
     w->rim = reinterpret_cast<float *>(rim);
     w->slots = reinterpret_cast<float *>(sl);
   }

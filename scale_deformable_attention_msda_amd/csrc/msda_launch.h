@@ -66,7 +66,7 @@ struct BinScratch {
   uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
   uint32_t *nchunks;    // [1] chunks in use
   uint4 *chunks;        // [max_chunks] (bin, first position, count, slot or ~0)
-  uint32_t *ids;        // [total] sample ids sorted by bin
+  uint4 *recs;          // [total] (id, u, v, A) of every live sample, sorted by bin
   float *rim;           // [nbins][4*tile][D] edge rows and halo of single-chunk tiles
   float *slots;         // [max_slots][(tile+1)^2][D] whole partial tiles of split bins
 };
