@@ -349,29 +349,42 @@ struct TileLayout {
   static constexpr int RS = D + 4;
 };
 
+// Work items of a chunk.  The samples of every cell (in cell order) are cut
+// into pieces of at most P samples, P the smallest multiple of kU that leaves
+// at most kMaxItems pieces, so that one lane group can own a piece's four
+// corner rows and four accumulators in registers while the lane groups get
+// similar amounts of work even when a few cells hold most of the chunk.
+constexpr int kU = 4;               // samples a lane group loads and processes together
+constexpr int kMaxItems = kCells;   // stage slots, one per item
+
 // LDS carve-up of the tile kernel (bytes):
-//   vt     [kEdge^2 + 1][RS] f32  value rows of the tile and its rim, then one zero row
-//   stage  [kCells][4][RS] f32    per-cell corner sums; holds the unsorted records in phase A
-//   sorted [kChunk] SampleRec     samples sorted by cell
-//   tag    [kChunk] u32           cell | rank << 8 of each unsorted record (~0: dropped)
-//   cnt    [kCells + 1] u32       samples per cell
-//   cstart [kCells + 1] u32       first sorted position of each cell
-//   order  [kCells] u32           cells by decreasing sample count
+//   vt     [kEdge^2 + 1][RS] f32   value rows of the tile and its rim, then one zero row
+//   stage  [kMaxItems][4][RS] f32  per-item corner sums; holds the unsorted records in phase A
+//   sorted [kChunk] SampleRec      samples sorted by cell
+//   tag    [kChunk] u32            cell | rank << 8 of each unsorted record (~0: dropped)
+//   cnt    [kCells + 1] u32        samples per cell
+//   cstart [kCells + 1] u32        first sorted position of each cell
+//   istart [kCells + 1] u32        first item of each cell; istart[kCells] = items in all
+//   items  [kMaxItems] u32         first | (len - 1) << 10 | cell << 20 of each item
+//   sched  [kMaxItems] u32         items by decreasing number of batches
 template <int D>
 struct TileSmem {
   static constexpr int RS = TileLayout<D>::RS;
   static constexpr size_t vt = 0;
   static constexpr size_t stage = vt + (size_t)(kEdge * kEdge + 1) * RS * 4;
-  static constexpr size_t cell_bytes = (size_t)kCells * 4 * RS * 4;
+  static constexpr size_t item_bytes = (size_t)kMaxItems * 4 * RS * 4;
   static constexpr size_t rec_bytes = (size_t)kChunk * sizeof(SampleRec);
-  static constexpr size_t stage_bytes = cell_bytes > rec_bytes ? cell_bytes : rec_bytes;
+  static constexpr size_t stage_bytes = item_bytes > rec_bytes ? item_bytes : rec_bytes;
   static constexpr size_t sorted = stage + stage_bytes;
   static constexpr size_t tag = sorted + (size_t)kChunk * sizeof(SampleRec);
   static constexpr size_t cnt = tag + (size_t)kChunk * 4;
   static constexpr size_t cstart = cnt + (size_t)(kCells + 1) * 4;
-  static constexpr size_t order = cstart + (size_t)(kCells + 1) * 4;
-  static constexpr size_t bytes = order + (size_t)kCells * 4;
+  static constexpr size_t istart = cstart + (size_t)(kCells + 1) * 4;
+  static constexpr size_t items = istart + (size_t)(kCells + 1) * 4;
+  static constexpr size_t sched = items + (size_t)kMaxItems * 4;
+  static constexpr size_t bytes = sched + (size_t)kMaxItems * 4;
 };
+static_assert(kChunk <= 1024, "item packing keeps 10-bit first / length fields");
 
 // Level, batch, head and tile of a bin.  The search runs over compile-time
 // level indices only, so the plan arrays stay in scalar registers instead of
@@ -444,6 +457,95 @@ __device__ inline void load_vec(const void *base, int64_t e, float (&o)[VEC]) {
   }
 }
 
+// ---- wave-wide integer scans and reductions (DPP inside 16-lane rows, then
+// the row totals through readlane)
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111>(x);  // row_shr:1
+  x += dpp_u32<0x112>(x);  // row_shr:2
+  x += dpp_u32<0x114>(x);  // row_shr:4
+  x += dpp_u32<0x118>(x);  // row_shr:8
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
+  const uint32_t row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
+__device__ inline uint32_t wave_sum(uint32_t x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+__device__ inline uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp_u32<kDppQuadXor1>(x));
+  x = max(x, dpp_u32<kDppQuadXor2>(x));
+  x = max(x, dpp_u32<kDppRowHalfMirror>(x));
+  x = max(x, dpp_u32<kDppRowMirror>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+__device__ inline uint32_t ceil_div(uint32_t n, uint32_t d) { return (n + d - 1) / d; }
+
+// Wave 0 of the tile kernel: cell starts (exclusive scan of the per-cell
+// counts), the item table and the schedule.  Lane j holds cells j and j + 64.
+__device__ inline void plan_items(const uint32_t *cnt, uint32_t *cstart, uint32_t *istart,
+                                  uint32_t *items, uint32_t *sched) {
+  const uint32_t c0 = threadIdx.x, c1 = threadIdx.x + 64;
+  const uint32_t n0 = cnt[c0], n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
+  const uint32_t inc0 = wave_incl_scan(n0);
+  const uint32_t total0 = __builtin_amdgcn_readlane(inc0, 63);
+  const uint32_t inc1 = total0 + wave_incl_scan(n1);
+  const uint32_t cs0 = inc0 - n0, cs1 = inc1 - n1;
+  cstart[c0] = cs0;
+  if (c1 <= (uint32_t)kCells) cstart[c1] = cs1;
+  // smallest P = kU * m with at most kMaxItems pieces (m = kChunk / kU leaves
+  // one piece per non-empty cell, at most kCells)
+  uint32_t lo = 1, hi = kChunk / kU;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1, P = kU * mid;
+    if (wave_sum(ceil_div(n0, P) + ceil_div(n1, P)) <= (uint32_t)kMaxItems) hi = mid;
+    else lo = mid + 1;
+  }
+  const uint32_t P = kU * lo;
+  const uint32_t k0 = ceil_div(n0, P), k1 = ceil_div(n1, P);
+  const uint32_t iinc0 = wave_incl_scan(k0);
+  const uint32_t itotal0 = __builtin_amdgcn_readlane(iinc0, 63);
+  const uint32_t iinc1 = itotal0 + wave_incl_scan(k1);
+  const uint32_t is0 = iinc0 - k0, is1 = iinc1 - k1;
+  istart[c0] = is0;
+  if (c1 <= (uint32_t)kCells) istart[c1] = is1;  // istart[kCells] = number of items
+  for (uint32_t j = 0; j < k0; ++j)
+    items[is0 + j] = (cs0 + j * P) | ((min(P, n0 - j * P) - 1) << 10) | (c0 << 20);
+  for (uint32_t j = 0; j < k1; ++j)
+    items[is1 + j] = (cs1 + j * P) | ((min(P, n1 - j * P) - 1) << 10) | (c1 << 20);
+  // schedule: items by decreasing batch count (full pieces have bmax batches,
+  // the last piece of a cell ceil(rest / kU)); order within a count is free
+  const uint32_t bmax = P / kU;
+  const uint32_t lb0 = k0 ? ceil_div(n0 - (k0 - 1) * P, kU) : 0u;
+  const uint32_t lb1 = k1 ? ceil_div(n1 - (k1 - 1) * P, kU) : 0u;
+  uint32_t pos = 0, b = bmax;
+  while (b > 0) {
+    const uint32_t full = b == bmax ? (k0 ? k0 - 1 : 0u) + (k1 ? k1 - 1 : 0u) : 0u;
+    const uint32_t c = full + (lb0 == b ? 1u : 0u) + (lb1 == b ? 1u : 0u);
+    const uint32_t inc = wave_incl_scan(c);
+    uint32_t w = pos + inc - c;
+    if (b == bmax) {
+      for (uint32_t j = 0; j + 1 < k0; ++j) sched[w++] = is0 + j;
+      for (uint32_t j = 0; j + 1 < k1; ++j) sched[w++] = is1 + j;
+    }
+    if (lb0 == b) sched[w++] = is0 + k0 - 1;
+    if (lb1 == b) sched[w++] = is1 + k1 - 1;
+    pos += __builtin_amdgcn_readlane(inc, 63);
+    b = wave_max(max(lb0 < b ? lb0 : 0u, lb1 < b ? lb1 : 0u));
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   using TL = TileLayout<D>;
@@ -463,17 +565,28 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   uint32_t *tag = reinterpret_cast<uint32_t *>(smem + SM::tag);
   uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + SM::cnt);
   uint32_t *cstart = reinterpret_cast<uint32_t *>(smem + SM::cstart);
-  uint32_t *order = reinterpret_cast<uint32_t *>(smem + SM::order);
+  uint32_t *istart = reinterpret_cast<uint32_t *>(smem + SM::istart);
+  uint32_t *items = reinterpret_cast<uint32_t *>(smem + SM::items);
+  uint32_t *sched = reinterpret_cast<uint32_t *>(smem + SM::sched);
 
   const BinPlan &p = a.p;
-  if (blockIdx.x >= *a.w.nchunks) return;
+  // the chunk count, this block's chunk entry and the level starts do not
+  // depend on each other: issue the loads together
+  const uint32_t nchunks = *a.w.nchunks;
   const uint4 ck = a.w.chunks[blockIdx.x];
+  int64_t lstart[kMaxLevels];
+#pragma unroll
+  for (int k = 0; k < kMaxLevels; ++k) lstart[k] = a.starts[min(k, p.L - 1)];
+  if (blockIdx.x >= nchunks) return;
   const int bin = (int)ck.x;
   const uint32_t first = ck.y, count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
   const BinPos bp = decode_bin(p, bin);
   const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
+  int64_t start = lstart[0];
+#pragma unroll
+  for (int k = 1; k < kMaxLevels; ++k)
+    if (k == l) start = lstart[k];
   const int px0 = tx * kTile, py0 = ty * kTile;
-  const int64_t start = a.starts[l];
   const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
   const int grp = threadIdx.x / G, lane = threadIdx.x % G;
 
@@ -534,46 +647,27 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     tag[i] = t;
   }
   __syncthreads();
-  // exclusive scan of the cell counts (one wave, two entries per lane)
-  if (threadIdx.x < 64) {
-    const int i0 = 2 * threadIdx.x, i1 = i0 + 1;
-    const uint32_t c0 = i0 < kCells ? cnt[i0] : 0u, c1 = i1 < kCells ? cnt[i1] : 0u;
-    uint32_t inc = c0 + c1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(inc, off, 64);
-      if ((int)threadIdx.x >= off) inc += v;
-    }
-    const uint32_t exc = inc - c0 - c1;
-    if (i0 <= kCells) cstart[i0] = exc;
-    if (i1 <= kCells) cstart[i1] = exc + c0;
-  }
+  if (threadIdx.x < 64) plan_items(cnt, cstart, istart, items, sched);
   __syncthreads();
-  // scatter the records into cell order; rank the cells by decreasing count
+  // records into cell order (the wave that planned the items is done first)
   for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
     const uint32_t t = tag[i];
     if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
   }
-  if (threadIdx.x < kCells) {
-    const uint32_t c = threadIdx.x, n = cnt[c];
-    uint32_t rank = 0;
-    for (uint32_t o = 0; o < (uint32_t)kCells; ++o) {
-      const uint32_t no = cnt[o];
-      rank += (no > n || (no == n && o < c)) ? 1u : 0u;
-    }
-    order[rank] = c;
-  }
   __syncthreads();
 
-  // ---- cell loop: one group per cell (largest cells first, snaking over the
-  // groups so the groups of a wave get cells of similar size); the cell's
-  // corner rows (fp64) and its four corner sums (fp32) stay in registers
-  for (int round = 0; round * NG < kCells; ++round) {
-    const int rank = round * NG + ((round & 1) ? NG - 1 - grp : grp);
-    if (rank >= kCells) continue;
-    const int cell = (int)order[rank];
-    const int cy = cell / kEdge, cx = cell - (cell / kEdge) * kEdge;
-    const uint32_t s0 = cstart[cell], n = cstart[cell + 1] - s0;
+  // ---- item loop: lane group g takes the schedule's entries g, 2NG-1-g,
+  // 2NG+g, ... (largest items first, snaking so the groups of a wave get items
+  // of similar size); an item's four corner rows (fp64) and its four corner
+  // sums (fp32) stay in registers
+  const uint32_t nitems = istart[kCells];
+  for (int round = 0; round * NG < (int)nitems; ++round) {
+    const int r = round * NG + ((round & 1) ? NG - 1 - grp : grp);
+    if (r >= (int)nitems) continue;
+    const int item = (int)sched[r];
+    const uint32_t desc = items[item];
+    const uint32_t s0 = desc & 0x3ffu, n = ((desc >> 10) & 0x3ffu) + 1, cell = desc >> 20;
+    const int cy = (int)cell / kEdge, cx = (int)cell - ((int)cell / kEdge) * kEdge;
     const double x0 = (double)(px0 + cx - 1), y0 = (double)(py0 + cy - 1);
     double V[4][VEC];
     float acc[4][VEC];
@@ -589,60 +683,158 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
         acc[q][i] = 0.0f;
       }
     }
-    constexpr int U = 4;  // samples whose grad_out rows are loaded together
-    for (uint32_t k0 = 0; k0 < n; k0 += U) {
-      SampleRec rec[U];
-      float g[U][VEC];
+    if constexpr (G == 4) {
+      // transposed batches of kU = 4 samples: slot t of lane j holds sample
+      // k0 + (j ^ t), so after the lane-wise partial dots one quad permutation
+      // per slot hands lane j the full p_c of sample k0 + j, and every lane
+      // does the per-sample work (weights, grad_attn, grad_loc) for its own
+      // sample instead of all four lanes repeating it
+      static_assert(kU == 4, "one sample per lane of a group");
+      uint4 own[1];          // record of the lane's own sample
+      uint32_t ids[1][4];    // sample ids of the four slots
+      float g[1][4][VEC];    // grad_out rows (this lane's channels) of the four slots
+      auto fetch = [&](uint32_t k0, int buf) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        rec[u] = sorted[s0 + min(k0 + u, n - 1)];
-        load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(rec[u].id, p.div_lk) * D + lane * VEC, g[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k0 + u >= n) break;
-        // fp64 partial dot products <g, V_c> over this lane's channels (exact products)
-        double pc[4];
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t pos = s0 + min(k0 + (uint32_t)(lane ^ t), n - 1);
+          if (t == 0) {
+            own[buf] = reinterpret_cast<const uint4 *>(sorted)[pos];
+            ids[buf][0] = own[buf].x;
+          } else {
+            ids[buf][t] = sorted[pos].id;
+          }
+          load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(ids[buf][t], p.div_lk) * D + lane * VEC,
+                           g[buf][t]);
+        }
+      };
+      auto consume = [&](uint32_t k0, int buf) {
+        double P[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          double sum = 0.0;
+          double pd[4];
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) sum = fma((double)g[u][i], V[q][i], sum);
-          pc[q] = sum;
+          for (int t = 0; t < 4; ++t) {
+            double sum = 0.0;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) sum = fma((double)g[buf][t][i], V[q][i], sum);
+            pd[t] = sum;
+          }
+          P[q] = (pd[0] + dpp_move_f64<kDppQuadXor1>(pd[1])) +
+                 (dpp_move_f64<kDppQuadXor2>(pd[2]) + dpp_move_f64<kDppQuadXor3>(pd[3]));
         }
-        const double lx = ((double)rec[u].u * (double)W - 0.5) - x0;
-        const double ly = ((double)rec[u].v * (double)H - 0.5) - y0;
+        const bool valid = k0 + (uint32_t)lane < n;
+        const uint32_t id = own[buf].x;
+        const float av = __uint_as_float(own[buf].y);
+        const double lx = ((double)__uint_as_float(own[buf].z) * (double)W - 0.5) - x0;
+        const double ly = ((double)__uint_as_float(own[buf].w) * (double)H - 0.5) - y0;
         const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
         const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
-        // grad_attn = sum_c w_c p_c ; grad_loc = (A W d/dlx, A H d/dly), all linear in the p_c
-        const double ga = group_sum_f64<G>(w0 * pc[0] + w1 * pc[1] + w2 * pc[2] + w3 * pc[3]);
-        const double gx = group_sum_f64<G>((1.0 - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
-        const double gy = group_sum_f64<G>((1.0 - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
-        const float av = rec[u].a;
-        if (lane == 0) {
-          const uint32_t id = rec[u].id;
-          store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, (float)ga);
-          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id,
-                          (float)((double)av * (double)W * gx));
-          store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)id + 1,
-                          (float)((double)av * (double)H * gy));
+        if (valid) {
+          const double ga = w0 * P[0] + w1 * P[1] + w2 * P[2] + w3 * P[3];
+          const double gx = (1.0 - ly) * (P[1] - P[0]) + ly * (P[3] - P[2]);
+          const double gy = (1.0 - lx) * (P[2] - P[0]) + lx * (P[3] - P[1]);
+          // the record has been read for good: it now holds the sample's results
+          reinterpret_cast<uint4 *>(sorted)[s0 + k0 + lane] =
+              make_uint4(id, __float_as_uint((float)ga),
+                         __float_as_uint((float)((double)av * (double)W * gx)),
+                         __float_as_uint((float)((double)av * (double)H * gy)));
         }
-        const float aw[4] = {av * (float)w0, av * (float)w1, av * (float)w2, av * (float)w3};
+        const float as = valid ? av : 0.0f;
+        const float aw[4] = {as * (float)w0, as * (float)w1, as * (float)w2, as * (float)w3};
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q) {
+          const float at[4] = {aw[q], dpp_move<kDppQuadXor1>(aw[q]), dpp_move<kDppQuadXor2>(aw[q]),
+                               dpp_move<kDppQuadXor3>(aw[q])};
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw[q], g[u][i], acc[q][i]);
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(at[t], g[buf][t][i], acc[q][i]);
+        }
+      };
+      for (uint32_t k0 = 0; k0 < n; k0 += kU) {
+        fetch(k0, 0);
+        consume(k0, 0);
+      }
+    } else {
+      // batches of kU samples; the records and grad_out rows of the next batch
+      // are loaded before the current one is processed
+      SampleRec rec[2][kU];
+      float g[2][kU][VEC];
+      auto fetch = [&](uint32_t k0, int buf) {
+  #pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          rec[buf][u] = sorted[s0 + min(k0 + u, n - 1)];
+          load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(rec[buf][u].id, p.div_lk) * D + lane * VEC,
+                           g[buf][u]);
+        }
+      };
+      auto consume = [&](uint32_t k0, int buf) {
+  #pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (k0 + u >= n) break;
+          const SampleRec &sr = rec[buf][u];
+          const float(&gu)[VEC] = g[buf][u];
+          // fp64 partial dot products <g, V_c> over this lane's channels (exact products)
+          double pc[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            double sum = 0.0;
+  #pragma unroll
+            for (int i = 0; i < VEC; ++i) sum = fma((double)gu[i], V[q][i], sum);
+            pc[q] = sum;
+          }
+          const double lx = ((double)sr.u * (double)W - 0.5) - x0;
+          const double ly = ((double)sr.v * (double)H - 0.5) - y0;
+          const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
+          const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
+          // grad_attn = sum_c w_c p_c ; grad_loc = (A W d/dlx, A H d/dly), all linear in the p_c
+          const double ga = group_sum_f64<G>(w0 * pc[0] + w1 * pc[1] + w2 * pc[2] + w3 * pc[3]);
+          const double gx = group_sum_f64<G>((1.0 - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
+          const double gy = group_sum_f64<G>((1.0 - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
+          const float av = sr.a;
+          if (lane == 0)
+            reinterpret_cast<uint4 *>(sorted)[s0 + k0 + u] =
+                make_uint4(sr.id, __float_as_uint((float)ga),
+                           __float_as_uint((float)((double)av * (double)W * gx)),
+                           __float_as_uint((float)((double)av * (double)H * gy)));
+          const float aw[4] = {av * (float)w0, av * (float)w1, av * (float)w2, av * (float)w3};
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+  #pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw[q], gu[i], acc[q][i]);
+        }
+      };
+      fetch(0, 0);
+      for (uint32_t k0 = 0; k0 < n; k0 += 2 * kU) {
+        if (k0 + kU < n) fetch(k0 + kU, 1);
+        consume(k0, 0);
+        if (k0 + kU >= n) break;
+        if (k0 + 2 * kU < n) fetch(k0 + 2 * kU, 0);
+        consume(k0 + kU, 1);
       }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) stage[(cell * 4 + q) * RS + lane * VEC + i] = acc[q][i];
+      for (int i = 0; i < VEC; ++i) stage[(item * 4 + q) * RS + lane * VEC + i] = acc[q][i];
   }
   __syncthreads();
 
-  // ---- every pixel of the tile and its rim sums the cells it is a corner of, then
-  // goes to grad_value (interior), the rim (edge / halo) or the chunk's slot
+  // ---- per-sample results back in record order: the scatter pass wrote a
+  // bin's records in sample order, so neighbouring lanes store neighbouring
+  // ids and the stores of a sample's points merge
+  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+    const uint32_t t = tag[i];
+    if (t == kDropped) continue;
+    const uint4 r = reinterpret_cast<const uint4 *>(sorted)[cstart[t & 0xffu] + (t >> 8)];
+    store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + r.x, __uint_as_float(r.y));
+    store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)r.x, __uint_as_float(r.z),
+                  __uint_as_float(r.w));
+  }
+
+  // ---- every pixel of the tile and its rim sums the items of the cells it is
+  // a corner of, then goes to grad_value (interior), the rim (edge / halo) or
+  // the chunk's slot
   for (int r = grp; r < NROWS; r += NG) {
     const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
     const int py = py0 + iy, px = px0 + ix;
@@ -655,9 +847,12 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int cy = iy + 1 - (q >> 1), cx = ix + 1 - (q & 1);
       if (cy >= kEdge || cx >= kEdge) continue;
-      const float *src = stage + ((cy * kEdge + cx) * 4 + q) * RS + lane * VEC;
+      const int c = cy * kEdge + cx;
+      for (uint32_t it = istart[c]; it < istart[c + 1]; ++it) {
+        const float *src = stage + (it * 4 + q) * RS + lane * VEC;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] += src[i];
+        for (int i = 0; i < VEC; ++i) v[i] += src[i];
+      }
     }
     if (slot != kNoSlot) {
       float *dst = a.w.slots + ((int64_t)slot * NROWS + r) * D + lane * VEC;

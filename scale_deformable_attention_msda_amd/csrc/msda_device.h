@@ -143,6 +143,18 @@ __device__ inline void store_scalar<bf16_t>(bf16_t *p, float x) {
   p->bits = (uint16_t)bf16_bits_rne(x);
 }
 
+// Two consecutive elements (p 8-byte aligned for fp32, 4-byte aligned for bf16).
+template <typename T>
+__device__ inline void store_pair(T *p, float x, float y);
+template <>
+__device__ inline void store_pair<float>(float *p, float x, float y) {
+  *reinterpret_cast<float2 *>(p) = make_float2(x, y);
+}
+template <>
+__device__ inline void store_pair<bf16_t>(bf16_t *p, float x, float y) {
+  *reinterpret_cast<uint32_t *>(p) = bf16_bits_rne(x) | (bf16_bits_rne(y) << 16);
+}
+
 // Unpack the 32-bit words of a row slice into fp32 channels.
 template <typename T, int WORDS>
 __device__ inline void unpack(const uint32_t (&w)[WORDS], float *out);
@@ -239,12 +251,13 @@ __device__ inline void pack(const float *x, uint32_t (&w)[WORDS]) {
 // DPP lane moves inside a 16-lane row (gfx9 encodings of dpp_ctrl).
 constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor3 = 0x1B;       // quad_perm [3,2,1,0]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8
 constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within 16
 
 template <int CTRL>
 __device__ inline float dpp_move(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over an aligned group of G (4, 8 or 16) lanes; every lane of the group
@@ -262,8 +275,8 @@ __device__ inline float group_sum(float x) {
 template <int CTRL>
 __device__ inline double dpp_move_f64(double x) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
   return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
