@@ -188,84 +188,156 @@ __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   }
 }
 
+// ---- wave-wide integer scans and reductions (DPP inside 16-lane rows, then
+// the row totals through readlane)
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111>(x);  // row_shr:1
+  x += dpp_u32<0x112>(x);  // row_shr:2
+  x += dpp_u32<0x114>(x);  // row_shr:4
+  x += dpp_u32<0x118>(x);  // row_shr:8
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
+  const uint32_t row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
+__device__ inline uint32_t wave_sum(uint32_t x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+__device__ inline uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp_u32<kDppQuadXor1>(x));
+  x = max(x, dpp_u32<kDppQuadXor2>(x));
+  x = max(x, dpp_u32<kDppRowHalfMirror>(x));
+  x = max(x, dpp_u32<kDppRowMirror>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+__device__ inline uint32_t ceil_div(uint32_t n, uint32_t d) { return (n + d - 1) / d; }
+
 // ---------------------------------------------------------------- plan pass
 
-// Counts of bin i, one per stripe.
-__device__ inline void load_stripes(const BinArgs &a, int i, uint32_t (&c)[kStripes]) {
-  const uint4 *src = reinterpret_cast<const uint4 *>(a.w.counts + (size_t)i * kStripes);
+constexpr int kPlanThreads = 1024;
+
+// Position j of the chunk order is a bin: (batch, head) major, then the
+// levels coarsest first, then the tiles of a level row-major, so that the
+// chunks running at one time share the grad_out rows of one head of one image.
+struct OrderTab {
+  int tile_off, ntiles, bin_base;
+};
+
+__device__ inline int bin_of_order(const BinPlan &p, const OrderTab *ot, int j) {
+  const int bm = j / p.tiles_bm;
+  const int off = j - bm * p.tiles_bm;
+  int k = 0;
+  while (k + 1 < p.L && !(off >= ot[k].tile_off && off < ot[k].tile_off + ot[k].ntiles)) ++k;
+  return ot[k].bin_base + bm * ot[k].ntiles + (off - ot[k].tile_off);
+}
+
+__device__ inline uint32_t chunks_of(const BinPlan &p, uint32_t c) {
+  return c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
+}
+
+// Exclusive scan of three per-thread values over the block (wave scans, then
+// the wave totals through LDS); tot receives the block totals.
+__device__ inline void block_scan3(uint32_t (&v)[3], uint32_t (&tot)[3], uint32_t *wsum) {
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t inc[3];
 #pragma unroll
-  for (int k = 0; k < kStripes / 4; ++k) {
-    const uint4 v = src[k];
-    c[4 * k] = v.x; c[4 * k + 1] = v.y; c[4 * k + 2] = v.z; c[4 * k + 3] = v.w;
+  for (int k = 0; k < 3; ++k) inc[k] = wave_incl_scan(v[k]);
+  if ((threadIdx.x & 63) == 63)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) wsum[w * 3 + k] = inc[k];
+  __syncthreads();
+  uint32_t before[3] = {0, 0, 0}, all[3] = {0, 0, 0};
+  for (int i = 0; i < nw; ++i)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t t = wsum[i * 3 + k];
+      before[k] += i < w ? t : 0u;
+      all[k] += t;
+    }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    v[k] = before[k] + inc[k] - v[k];
+    tot[k] = all[k];
   }
 }
 
-// One block of 1024 threads: exclusive scans of the bin counts, chunk counts
-// and split-bin slot counts; then each bin's start, its stripe cursors (each
-// stripe's first sorted position) and its chunk-table entries.
-__global__ __launch_bounds__(1024) void plan_kernel(BinArgs a) {
-  __shared__ uint32_t part[3][1024];
+// One block walks the chunk order in rounds of one bin per thread: exclusive
+// scans of the sample, chunk and split-bin slot counts give each bin its
+// first sorted position, its stripe cursors (each stripe's first position)
+// and its chunk entries; neighbouring threads write neighbouring entries.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(BinArgs a) {
+  __shared__ uint32_t wsum[(kPlanThreads / 64) * 3];
+  __shared__ OrderTab ot[kMaxLevels];
   const BinPlan &p = a.p;
+  if (threadIdx.x < (unsigned)p.L) {
+    const int l = threadIdx.x;
+    ot[l] = OrderTab{p.tile_off[l], p.ntiles[l], p.bin_base[l]};
+  }
+  __syncthreads();
   const int n = p.nbins;
-  const int per = (n + blockDim.x - 1) / blockDim.x;
-  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
-  uint32_t s_cnt = 0, s_ch = 0, s_slot = 0;
-  for (int i = lo; i < hi; ++i) {
+  // the next round's bin and counts are loaded while the current one is scanned
+  auto fetch = [&](int j, int &bin, uint4 (&raw)[kStripes / 4]) {
+    bin = bin_of_order(p, ot, min(j, n - 1));
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.w.counts + (size_t)bin * kStripes);
+#pragma unroll
+    for (int k = 0; k < kStripes / 4; ++k) raw[k] = src[k];
+  };
+  int next_bin;
+  uint4 next_raw[kStripes / 4];
+  fetch((int)threadIdx.x, next_bin, next_raw);
+  uint32_t carry[3] = {0, 0, 0};  // samples, chunks, slots of the earlier rounds
+  for (int j0 = 0; j0 < n; j0 += kPlanThreads) {
+    const int j = j0 + (int)threadIdx.x;
+    const bool live = j < n;
+    const int i = next_bin;
     uint32_t cs[kStripes];
-    load_stripes(a, i, cs);
+#pragma unroll
+    for (int k = 0; k < kStripes / 4; ++k) {
+      const uint4 v = next_raw[k];
+      cs[4 * k] = v.x; cs[4 * k + 1] = v.y; cs[4 * k + 2] = v.z; cs[4 * k + 3] = v.w;
+    }
+    if (j0 + kPlanThreads < n) fetch(j + kPlanThreads, next_bin, next_raw);
     uint32_t c = 0;
 #pragma unroll
     for (int k = 0; k < kStripes; ++k) c += cs[k];
-    const uint32_t nch = c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
-    s_cnt += c;
-    s_ch += nch;
-    s_slot += nch > 1 ? nch : 0;
-  }
-  // inclusive Hillis-Steele scan of the three per-thread totals
-  part[0][threadIdx.x] = s_cnt;
-  part[1][threadIdx.x] = s_ch;
-  part[2][threadIdx.x] = s_slot;
-  __syncthreads();
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-    uint32_t v0 = 0, v1 = 0, v2 = 0;
-    if ((int)threadIdx.x >= off) {
-      v0 = part[0][threadIdx.x - off];
-      v1 = part[1][threadIdx.x - off];
-      v2 = part[2][threadIdx.x - off];
-    }
-    __syncthreads();
-    part[0][threadIdx.x] += v0;
-    part[1][threadIdx.x] += v1;
-    part[2][threadIdx.x] += v2;
-    __syncthreads();
-  }
-  if (threadIdx.x == blockDim.x - 1) *a.w.nchunks = part[1][threadIdx.x];
-  uint32_t pos = part[0][threadIdx.x] - s_cnt, ch = part[1][threadIdx.x] - s_ch;
-  uint32_t slot = part[2][threadIdx.x] - s_slot;
-  for (int i = lo; i < hi; ++i) {
-    uint32_t cs[kStripes];
-    load_stripes(a, i, cs);
-    uint32_t c = 0;
-    uint4 *cur = reinterpret_cast<uint4 *>(a.w.cursor + (size_t)i * kStripes);
+    const uint32_t nch = live ? chunks_of(p, c) : 0u;
+    uint32_t v[3] = {live ? c : 0u, nch, nch > 1 ? nch : 0u}, tot[3];
+    block_scan3(v, tot, wsum);
+    if (live) {
+      const uint32_t pos = carry[0] + v[0], ch = carry[1] + v[1], slot = carry[2] + v[2];
+      uint4 *cur = reinterpret_cast<uint4 *>(a.w.cursor + (size_t)i * kStripes);
+      uint32_t run = pos;
 #pragma unroll
-    for (int k = 0; k < kStripes; k += 4) {
-      const uint32_t c0 = pos + c, c1 = c0 + cs[k], c2 = c1 + cs[k + 1], c3 = c2 + cs[k + 2];
-      cur[k / 4] = make_uint4(c0, c1, c2, c3);
-      c += cs[k] + cs[k + 1] + cs[k + 2] + cs[k + 3];
+      for (int k = 0; k < kStripes; k += 4) {
+        const uint32_t c0 = run, c1 = c0 + cs[k], c2 = c1 + cs[k + 1], c3 = c2 + cs[k + 2];
+        cur[k / 4] = make_uint4(c0, c1, c2, c3);
+        run = c3 + cs[k + 3];
+      }
+      a.w.bin_start[i] = pos;
+      a.w.bin_nch[i] = nch;
+      a.w.bin_slot0[i] = nch > 1 ? slot : kNoSlot;
+      for (uint32_t k = 0; k < nch; ++k) {
+        const uint32_t first = k * (uint32_t)p.chunk;
+        const uint32_t cnt = c > first ? min((uint32_t)p.chunk, c - first) : 0u;
+        a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
+      }
     }
-    const uint32_t nch = c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
-    a.w.bin_start[i] = pos;
-    a.w.bin_nch[i] = nch;
-    a.w.bin_slot0[i] = nch > 1 ? slot : kNoSlot;
-    for (uint32_t k = 0; k < nch; ++k) {
-      const uint32_t first = k * (uint32_t)p.chunk;
-      const uint32_t cnt = c > first ? min((uint32_t)p.chunk, c - first) : 0u;
-      a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
-    }
-    pos += c;
-    ch += nch;
-    slot += nch > 1 ? nch : 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) carry[k] += tot[k];
+    __syncthreads();  // wsum is reused by the next round
   }
+  if (threadIdx.x == 0) *a.w.nchunks = carry[1];
 }
 
 // ------------------------------------------------------------- scatter pass
@@ -457,63 +529,59 @@ __device__ inline void load_vec(const void *base, int64_t e, float (&o)[VEC]) {
   }
 }
 
-// ---- wave-wide integer scans and reductions (DPP inside 16-lane rows, then
-// the row totals through readlane)
-template <int CTRL>
-__device__ inline uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+// ceil(n / d) for n <= 2^12 and 1 <= d <= 2^12, rd ~ 1/d within a few ulp: the
+// float quotient is off by less than 2^-10 from n / d, so at most the floor of
+// an exact integer quotient comes out one low, and one integer check fixes it.
+__device__ inline uint32_t ceil_div_small(uint32_t n, uint32_t d, float rd) {
+  uint32_t q = (uint32_t)((float)n * rd);
+  q += (q + 1) * d <= n ? 1u : 0u;  // exact floor(n / d)
+  return q + (q * d < n ? 1u : 0u);
 }
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ inline uint32_t wave_incl_scan(uint32_t x) {
-  x += dpp_u32<0x111>(x);  // row_shr:1
-  x += dpp_u32<0x112>(x);  // row_shr:2
-  x += dpp_u32<0x114>(x);  // row_shr:4
-  x += dpp_u32<0x118>(x);  // row_shr:8
-  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
-  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
-  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
-  const uint32_t row = (threadIdx.x & 63) >> 4;
-  return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
-}
-
-__device__ inline uint32_t wave_sum(uint32_t x) {
-  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
-}
-
-__device__ inline uint32_t wave_max(uint32_t x) {
-  x = max(x, dpp_u32<kDppQuadXor1>(x));
-  x = max(x, dpp_u32<kDppQuadXor2>(x));
-  x = max(x, dpp_u32<kDppRowHalfMirror>(x));
-  x = max(x, dpp_u32<kDppRowMirror>(x));
-  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
-             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
-}
-
-__device__ inline uint32_t ceil_div(uint32_t n, uint32_t d) { return (n + d - 1) / d; }
-
-// Wave 0 of the tile kernel: cell starts (exclusive scan of the per-cell
-// counts), the item table and the schedule.  Lane j holds cells j and j + 64.
-__device__ inline void plan_items(const uint32_t *cnt, uint32_t *cstart, uint32_t *istart,
-                                  uint32_t *items, uint32_t *sched) {
+// Wave 0 of the tile kernel, step 1: cell starts (exclusive scan of the
+// per-cell counts, cstart[kCells] = live samples).  Lane j holds cells j and j + 64.
+__device__ inline void cell_starts(const uint32_t *cnt, uint32_t *cstart) {
   const uint32_t c0 = threadIdx.x, c1 = threadIdx.x + 64;
   const uint32_t n0 = cnt[c0], n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
   const uint32_t inc0 = wave_incl_scan(n0);
   const uint32_t total0 = __builtin_amdgcn_readlane(inc0, 63);
   const uint32_t inc1 = total0 + wave_incl_scan(n1);
-  const uint32_t cs0 = inc0 - n0, cs1 = inc1 - n1;
-  cstart[c0] = cs0;
-  if (c1 <= (uint32_t)kCells) cstart[c1] = cs1;
-  // smallest P = kU * m with at most kMaxItems pieces (m = kChunk / kU leaves
-  // one piece per non-empty cell, at most kCells)
-  uint32_t lo = 1, hi = kChunk / kU;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1, P = kU * mid;
-    if (wave_sum(ceil_div(n0, P) + ceil_div(n1, P)) <= (uint32_t)kMaxItems) hi = mid;
-    else lo = mid + 1;
+  cstart[c0] = inc0 - n0;
+  if (c1 <= (uint32_t)kCells) cstart[c1] = inc1 - n1;
+}
+
+// Wave 0 of the tile kernel, step 2: the item table and the schedule.
+__device__ inline void plan_items(const uint32_t *cnt, const uint32_t *cstart, uint32_t *istart,
+                                  uint32_t *items, uint32_t *sched) {
+  const uint32_t c0 = threadIdx.x, c1 = threadIdx.x + 64;
+  const uint32_t n0 = cnt[c0], n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
+  const uint32_t cs0 = cstart[c0], cs1 = c1 < (uint32_t)kCells ? cstart[c1] : 0u;
+  const uint32_t total = cstart[kCells];
+  // smallest P = kU * m with at most kMaxItems pieces: linear steps up from
+  // the lower bound total / kMaxItems, then a binary search if that is slow
+  // (m = kChunk / kU leaves one piece per non-empty cell, at most kCells)
+  auto pieces = [&](uint32_t P) {
+    const float rp = __builtin_amdgcn_rcpf((float)P);
+    return wave_sum(ceil_div_small(n0, P, rp) + ceil_div_small(n1, P, rp));
+  };
+  uint32_t m = max(1u, ceil_div(total, kU * kMaxItems));
+  for (int step = 0; pieces(kU * m) > (uint32_t)kMaxItems; ++step) {
+    if (step < 3) {
+      ++m;
+      continue;
+    }
+    uint32_t lo = m + 1, hi = kChunk / kU;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (pieces(kU * mid) <= (uint32_t)kMaxItems) hi = mid;
+      else lo = mid + 1;
+    }
+    m = lo;
+    break;
   }
-  const uint32_t P = kU * lo;
-  const uint32_t k0 = ceil_div(n0, P), k1 = ceil_div(n1, P);
+  const uint32_t P = kU * m;
+  const float rp = __builtin_amdgcn_rcpf((float)P);
+  const uint32_t k0 = ceil_div_small(n0, P, rp), k1 = ceil_div_small(n1, P, rp);
   const uint32_t iinc0 = wave_incl_scan(k0);
   const uint32_t itotal0 = __builtin_amdgcn_readlane(iinc0, 63);
   const uint32_t iinc1 = itotal0 + wave_incl_scan(k1);
@@ -524,18 +592,17 @@ __device__ inline void plan_items(const uint32_t *cnt, uint32_t *cstart, uint32_
     items[is0 + j] = (cs0 + j * P) | ((min(P, n0 - j * P) - 1) << 10) | (c0 << 20);
   for (uint32_t j = 0; j < k1; ++j)
     items[is1 + j] = (cs1 + j * P) | ((min(P, n1 - j * P) - 1) << 10) | (c1 << 20);
-  // schedule: items by decreasing batch count (full pieces have bmax batches,
+  // schedule: items by decreasing batch count (full pieces have m batches,
   // the last piece of a cell ceil(rest / kU)); order within a count is free
-  const uint32_t bmax = P / kU;
-  const uint32_t lb0 = k0 ? ceil_div(n0 - (k0 - 1) * P, kU) : 0u;
-  const uint32_t lb1 = k1 ? ceil_div(n1 - (k1 - 1) * P, kU) : 0u;
-  uint32_t pos = 0, b = bmax;
+  const uint32_t lb0 = k0 ? (n0 - (k0 - 1) * P + kU - 1) / kU : 0u;
+  const uint32_t lb1 = k1 ? (n1 - (k1 - 1) * P + kU - 1) / kU : 0u;
+  uint32_t pos = 0, b = m;
   while (b > 0) {
-    const uint32_t full = b == bmax ? (k0 ? k0 - 1 : 0u) + (k1 ? k1 - 1 : 0u) : 0u;
+    const uint32_t full = b == m ? (k0 ? k0 - 1 : 0u) + (k1 ? k1 - 1 : 0u) : 0u;
     const uint32_t c = full + (lb0 == b ? 1u : 0u) + (lb1 == b ? 1u : 0u);
     const uint32_t inc = wave_incl_scan(c);
     uint32_t w = pos + inc - c;
-    if (b == bmax) {
+    if (b == m) {
       for (uint32_t j = 0; j + 1 < k0; ++j) sched[w++] = is0 + j;
       for (uint32_t j = 0; j + 1 < k1; ++j) sched[w++] = is1 + j;
     }
@@ -647,12 +714,16 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     tag[i] = t;
   }
   __syncthreads();
-  if (threadIdx.x < 64) plan_items(cnt, cstart, istart, items, sched);
+  if (threadIdx.x < 64) cell_starts(cnt, cstart);
   __syncthreads();
-  // records into cell order (the wave that planned the items is done first)
-  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
-    const uint32_t t = tag[i];
-    if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
+  // wave 0 plans the items while the other waves put the records in cell order
+  if (threadIdx.x < 64) {
+    plan_items(cnt, cstart, istart, items, sched);
+  } else {
+    for (uint32_t i = threadIdx.x - 64; i < count; i += blockDim.x - 64) {
+      const uint32_t t = tag[i];
+      if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
+    }
   }
   __syncthreads();
 
@@ -1079,13 +1150,16 @@ bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, in
   p.nbins = (int)nbins;
   p.hist_size = (int)(M * tiles);
   // coarsest level (highest index) first
-  int run_bins = 0, run_hist = 0;
+  int run_bins = 0, run_hist = 0, run_tiles = 0;
   for (int l = L - 1; l >= 0; --l) {
     p.bin_base[l] = run_bins;
     p.hist_base[l] = run_hist;
+    p.tile_off[l] = run_tiles;
     run_bins += (int)(B * M) * p.ntiles[l];
     run_hist += M * p.ntiles[l];
+    run_tiles += p.ntiles[l];
   }
+  p.tiles_bm = run_tiles;
   const int64_t extra = (total + kChunk - 1) / kChunk;
   p.max_chunks = (int)(nbins + extra);
   p.max_slots = (int)(2 * extra);

@@ -47,6 +47,9 @@ struct BinPlan {
   int ntiles[kMaxLevels];      // tiles of level l (per batch and head)
   int bin_base[kMaxLevels];    // first bin of level l
   int hist_base[kMaxLevels];   // first per-batch histogram slot of level l
+  int tile_off[kMaxLevels];    // first tile of level l among the tiles of one (batch, head),
+                               // coarsest level first
+  int tiles_bm;                // tiles of all levels of one (batch, head)
   int nbins;                   // B * M * (tiles of all levels)
   int hist_size;               // M * (tiles of all levels): one batch's bins
   int max_chunks;              // nbins + ceil(total / chunk)
@@ -65,7 +68,7 @@ struct BinScratch {
   uint32_t *bin_nch;    // [nbins] chunks of a bin
   uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
   uint32_t *nchunks;    // [1] chunks in use
-  uint4 *chunks;        // [max_chunks] (bin, first position, count, slot or ~0)
+  uint4 *chunks;        // [max_chunks] (bin, first position, count, slot or ~0) in chunk order
   uint4 *recs;          // [total] (id, u, v, A) of every live sample, sorted by bin
   float *rim;           // [nbins][4*tile][D] edge rows and halo of single-chunk tiles
   float *slots;         // [max_slots][(tile+1)^2][D] whole partial tiles of split bins
