@@ -79,12 +79,6 @@ __device__ inline bool cell_of(float u, float v, int H, int W, Cell &c) {
   return true;
 }
 
-// Tile of a cell: the one holding its top-left corner, clamped into the map.
-__device__ inline int tile_of(int ntx, const Cell &c) {
-  const int x = max(c.x0, 0), y = max(c.y0, 0);
-  return (y / kTile) * ntx + (x / kTile);
-}
-
 template <typename T>
 __device__ inline float ldf(const void *base, int64_t i) {
   return to_float<T>(reinterpret_cast<const T *>(base)[i]);
@@ -113,17 +107,44 @@ __device__ inline int bin_of_slot(const BinPlan &p, const LevelTab *lt, int b, i
   return lt[l].bin_base + (b * p.M + m) * lt[l].ntiles + t;
 }
 
-// Histogram slot of batch-local sample s (< 2^32) at normalised (u, v), or -1
-// for a dead sample (no corner inside its level).
-__device__ inline int slot_of_sample(const BinPlan &p, const LevelTab *lt, uint32_t s, float u,
-                                     float v) {
-  const uint32_t hq = fdiv(s, p.div_lk);
-  const uint32_t j = s - hq * (uint32_t)(p.L * p.K);
-  const uint32_t m = hq - fdiv(hq, p.div_m) * (uint32_t)p.M;
-  const LevelTab t = lt[fdiv(j, p.div_k)];
+// A thread's samples s0 + r * 256 (r = 0, 1, ...) inside one batch: the
+// head-query hq = s / (L K), the point j = s % (L K) and the head m = hq % M
+// advance by fixed steps instead of being divided out for every sample.
+struct SampleWalk {
+  uint32_t hq, j, m;
+};
+
+__device__ inline SampleWalk walk_start(const BinPlan &p, uint32_t s) {
+  SampleWalk w;
+  w.hq = fdiv(s, p.div_lk);
+  w.j = s - w.hq * (uint32_t)(p.L * p.K);
+  w.m = w.hq - fdiv(w.hq, p.div_m) * (uint32_t)p.M;
+  return w;
+}
+
+__device__ inline void walk_step(const BinPlan &p, SampleWalk &w) {
+  w.j += p.step_j;
+  w.hq += p.step_hq;
+  w.m += p.step_m;  // step_m < M, plus at most one carry: one subtraction wraps m
+  if (w.j >= (uint32_t)(p.L * p.K)) {
+    w.j -= (uint32_t)(p.L * p.K);
+    ++w.hq;
+    ++w.m;
+  }
+  if (w.m >= (uint32_t)p.M) w.m -= (uint32_t)p.M;
+}
+
+// Histogram slot of the walk's current sample at normalised (u, v), or -1 for
+// a dead sample (no corner inside its level).  The level is j / K through a
+// 16-bit fixed-point reciprocal (exact for j < L K <= 64).
+__device__ inline int slot_of_sample(const BinPlan &p, const LevelTab *lt, const SampleWalk &w,
+                                     float u, float v) {
+  const LevelTab t = lt[__umul24(w.j, p.magic_k) >> 16];
   Cell c;
   if (!cell_of(u, v, t.H, t.W, c)) return -1;
-  return t.hist_base + (int)m * t.ntiles + tile_of(t.ntx, c);
+  const uint32_t x = (uint32_t)max(c.x0, 0), y = (uint32_t)max(c.y0, 0);
+  return t.hist_base + (int)__umul24(w.m, (uint32_t)t.ntiles) +
+         (int)(__umul24(y / kTile, (uint32_t)t.ntx) + x / kTile);
 }
 
 // Sampling location of sample `id` (both coordinates in one load).
@@ -154,31 +175,34 @@ __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
   __shared__ LevelTab lt[kMaxLevels];
   stage_level_tab(p, lt);
-  const int64_t per_b = a.p.Q * p.M * p.L * p.K;
-  const int64_t s0 = (int64_t)blockIdx.x * kCountSamples;
+  const uint32_t per_b = p.total / (uint32_t)p.B;      // samples of one batch (< 2^32)
+  const uint32_t s0 = blockIdx.x * kCountSamples + threadIdx.x;
+  const uint32_t id0 = (uint32_t)b * per_b;
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
-  // branch-free loads (clamped index) so all kPer loads are in flight together
+  __syncthreads();
+  // branch-free loads (clamped index) so all kPer loads are in flight together;
+  // each sample is binned as soon as its own load has arrived
   float u[kPer], v[kPer];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int64_t s = min(s0 + r * 256 + (int64_t)threadIdx.x, per_b - 1);
-    load_loc<T>(a.loc, b * per_b + s, u[r], v[r]);
-  }
-  __syncthreads();
+  for (int r = 0; r < kPer; ++r)
+    load_loc<T>(a.loc, id0 + min(s0 + r * 256, per_b - 1), u[r], v[r]);
+  SampleWalk w = walk_start(p, s0);
+  uint32_t dead = 0;  // bit r: sample r has no corner inside its level
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const int64_t s = s0 + r * 256 + threadIdx.x;
-    if (s >= per_b) break;
-    const int64_t id = b * per_b + s;
-    const int e = slot_of_sample(p, lt, (uint32_t)s, u[r], v[r]);
-    if (e < 0) {
-      // no corner inside its level: zero gradients, never binned
-      store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, 0.0f);
-      store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * id, 0.0f);
-      store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * id + 1, 0.0f);
-      continue;
-    }
-    __hip_atomic_fetch_add(&hist[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (s0 + r * 256 >= per_b) break;
+    const int e = slot_of_sample(p, lt, w, u[r], v[r]);
+    if (e < 0) dead |= 1u << r;
+    else __hip_atomic_fetch_add(&hist[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    walk_step(p, w);
+  }
+  // dead samples get zero gradients here and are never binned
+  while (dead) {
+    const int r = __builtin_ctz(dead);
+    dead &= dead - 1;
+    const int64_t id = id0 + s0 + r * 256;
+    store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, 0.0f);
+    store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * id, 0.0f, 0.0f);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
@@ -350,55 +374,65 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
   const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
   __shared__ LevelTab lt[kMaxLevels];
   stage_level_tab(p, lt);
-  const int64_t per_b = a.p.Q * p.M * p.L * p.K;
-  const int64_t s0 = (int64_t)blockIdx.x * kCountSamples;
+  const uint32_t per_b = p.total / (uint32_t)p.B;      // samples of one batch (< 2^32)
+  const uint32_t s0 = blockIdx.x * kCountSamples + threadIdx.x;
+  const uint32_t id0 = (uint32_t)b * per_b;
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
-  // branch-free loads (clamped index) so all kPer loads are in flight together
-  float u[kPer], v[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int64_t s = min(s0 + r * 256 + (int64_t)threadIdx.x, per_b - 1);
-    load_loc<T>(a.loc, b * per_b + s, u[r], v[r]);
-  }
   __syncthreads();
-  float aw[kPer];
+  // branch-free loads (clamped index) so all loads are in flight together;
+  // each sample is ranked as soon as its own location has arrived
+  float u[kPer], v[kPer], aw[kPer];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int64_t s = min(s0 + r * 256 + (int64_t)threadIdx.x, per_b - 1);
-    aw[r] = ldf<T>(a.attn, b * per_b + s);
-  }
+  for (int r = 0; r < kPer; ++r)
+    load_loc<T>(a.loc, id0 + min(s0 + r * 256, per_b - 1), u[r], v[r]);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) aw[r] = ldf<T>(a.attn, id0 + min(s0 + r * 256, per_b - 1));
   int slot[kPer];
   uint32_t rank[kPer];
+  SampleWalk w = walk_start(p, s0);
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const int64_t s = s0 + r * 256 + threadIdx.x;
     slot[r] = -1;
     rank[r] = 0;
-    if (s < per_b) {
-      slot[r] = slot_of_sample(p, lt, (uint32_t)s, u[r], v[r]);
+    if (s0 + r * 256 < per_b) {
+      slot[r] = slot_of_sample(p, lt, w, u[r], v[r]);
       if (slot[r] >= 0)
         rank[r] = __hip_atomic_fetch_add(&hist[slot[r]], 1u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    walk_step(p, w);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
-    const uint32_t n = hist[e];
-    if (n) {
-      // the cursor of (bin, stripe) starts at that stripe's first sorted position
-      const int bin = bin_of_slot(p, lt, b, e);
-      hist[e] = __hip_atomic_fetch_add(&a.w.cursor[bin * kStripes + stripe], n, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+  // reserve every touched bin's range: the cursor of (bin, stripe) starts at
+  // that stripe's first sorted position; kReserve returning atomics per
+  // thread are in flight together
+  constexpr int kReserve = 8;
+  for (int e0 = 0; e0 < p.hist_size; e0 += 256 * kReserve) {
+    uint32_t n[kReserve], got[kReserve];
+#pragma unroll
+    for (int k = 0; k < kReserve; ++k) {
+      const int e = e0 + k * 256 + (int)threadIdx.x;
+      n[k] = e < p.hist_size ? hist[e] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kReserve; ++k) {
+      const int e = e0 + k * 256 + (int)threadIdx.x;
+      got[k] = n[k] ? __hip_atomic_fetch_add(&a.w.cursor[bin_of_slot(p, lt, b, e) * kStripes + stripe],
+                                             n[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kReserve; ++k) {
+      const int e = e0 + k * 256 + (int)threadIdx.x;
+      if (n[k]) hist[e] = got[k];
     }
   }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    if (slot[r] >= 0) {
-      const int64_t s = s0 + r * 256 + threadIdx.x;
-      a.w.recs[hist[slot[r]] + rank[r]] = make_uint4((uint32_t)(b * per_b + s), __float_as_uint(u[r]),
+    if (slot[r] >= 0)
+      a.w.recs[hist[slot[r]] + rank[r]] = make_uint4(id0 + s0 + r * 256, __float_as_uint(u[r]),
                                                      __float_as_uint(v[r]), __float_as_uint(aw[r]));
-    }
   }
 }
 
@@ -1147,6 +1181,10 @@ bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, in
   p.div_lk = make_fastdiv((uint32_t)(L * K));
   p.div_k = make_fastdiv((uint32_t)K);
   p.div_m = make_fastdiv((uint32_t)M);
+  p.step_hq = 256u / (uint32_t)(L * K);
+  p.step_j = 256u % (uint32_t)(L * K);
+  p.step_m = p.step_hq % (uint32_t)M;
+  p.magic_k = ((1u << 16) + (uint32_t)K - 1) / (uint32_t)K;
   p.nbins = (int)nbins;
   p.hist_size = (int)(M * tiles);
   // coarsest level (highest index) first

@@ -57,6 +57,10 @@ struct BinPlan {
   int64_t pyramid_rows;        // sum_l H_l * W_l
   uint32_t total;              // B*Q*M*L*K samples
   FastDiv div_lk, div_k, div_m;  // by L*K, K and M
+  // a stride of 256 samples inside one batch: whole head-queries, points and
+  // heads it advances (256 / (L K), 256 % (L K), (256 / (L K)) % M)
+  uint32_t step_hq, step_j, step_m;
+  uint32_t magic_k;              // ceil(2^16 / K): j / K = (j * magic_k) >> 16 for j < L K
 };
 
 // Device scratch carved out of the caller's workspace (byte offsets into it
