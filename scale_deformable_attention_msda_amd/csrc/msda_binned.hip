@@ -248,8 +248,15 @@ __device__ inline uint32_t wave_max(uint32_t x) {
 __device__ inline uint32_t ceil_div(uint32_t n, uint32_t d) { return (n + d - 1) / d; }
 
 // ---------------------------------------------------------------- plan pass
+//
+// Many blocks of kPlanBlock bins each, in chunk order, one bin per thread.
+// Positions are exclusive scans over the chunk order of three counts per bin
+// (samples, chunks, split-bin slots): a block scans its own bins, publishes
+// its totals, and adds the totals every earlier block has published
+// (decoupled look-back).  A block only ever waits for lower-numbered blocks,
+// which are dispatched before it and wait for nobody later, so the waits end.
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanBlock = 256;
 
 // Position j of the chunk order is a bin: (batch, head) major, then the
 // levels coarsest first, then the tiles of a level row-major, so that the
@@ -270,98 +277,106 @@ __device__ inline uint32_t chunks_of(const BinPlan &p, uint32_t c) {
   return c == 0 ? 1u : (c + p.chunk - 1) / p.chunk;
 }
 
-// Exclusive scan of three per-thread values over the block (wave scans, then
-// the wave totals through LDS); tot receives the block totals.
+// Exclusive scans over the block of three per-thread values: wave scans
+// (DPP), then the kPlanBlock / 64 wave totals through LDS.  tot receives the
+// block totals.  wsum holds 3 * (kPlanBlock / 64) words.
 __device__ inline void block_scan3(uint32_t (&v)[3], uint32_t (&tot)[3], uint32_t *wsum) {
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  constexpr int kWaves = kPlanBlock / 64;
+  const int w = threadIdx.x >> 6;
   uint32_t inc[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) inc[k] = wave_incl_scan(v[k]);
   if ((threadIdx.x & 63) == 63)
 #pragma unroll
-    for (int k = 0; k < 3; ++k) wsum[w * 3 + k] = inc[k];
-  __syncthreads();
-  uint32_t before[3] = {0, 0, 0}, all[3] = {0, 0, 0};
-  for (int i = 0; i < nw; ++i)
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const uint32_t t = wsum[i * 3 + k];
-      before[k] += i < w ? t : 0u;
-      all[k] += t;
-    }
+    for (int k = 0; k < 3; ++k) wsum[k * kWaves + w] = inc[k];
+  lds_barrier();
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
-    v[k] = before[k] + inc[k] - v[k];
-    tot[k] = all[k];
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const uint32_t t = wsum[k * kWaves + i];
+      before += i < w ? t : 0u;
+      all += t;
+    }
+    v[k] = before + inc[k] - v[k];
+    tot[k] = all;
   }
+  lds_barrier();  // wsum may be reused right away
 }
 
-// One block walks the chunk order in rounds of one bin per thread: exclusive
-// scans of the sample, chunk and split-bin slot counts give each bin its
-// first sorted position, its stripe cursors (each stripe's first position)
-// and its chunk entries; neighbouring threads write neighbouring entries.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(BinArgs a) {
-  __shared__ uint32_t wsum[(kPlanThreads / 64) * 3];
+// Bound on the polls of one predecessor's published totals.  Predecessors
+// always publish (see above); the bound only guarantees that every wave ends.
+constexpr uint32_t kPlanSpinLimit = 1u << 24;
+
+__global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
+  __shared__ uint32_t wsum[3 * (kPlanBlock / 64)];
   __shared__ OrderTab ot[kMaxLevels];
   const BinPlan &p = a.p;
   if (threadIdx.x < (unsigned)p.L) {
     const int l = threadIdx.x;
     ot[l] = OrderTab{p.tile_off[l], p.ntiles[l], p.bin_base[l]};
   }
-  __syncthreads();
+  lds_barrier();
   const int n = p.nbins;
-  // the next round's bin and counts are loaded while the current one is scanned
-  auto fetch = [&](int j, int &bin, uint4 (&raw)[kStripes / 4]) {
-    bin = bin_of_order(p, ot, min(j, n - 1));
-    const uint4 *src = reinterpret_cast<const uint4 *>(a.w.counts + (size_t)bin * kStripes);
+  const int j = (int)blockIdx.x * kPlanBlock + (int)threadIdx.x;
+  const bool live = j < n;
+  const int i = bin_of_order(p, ot, min(j, n - 1));
+  uint32_t cs[kStripes];
+  const uint4 *src = reinterpret_cast<const uint4 *>(a.w.counts + (size_t)i * kStripes);
 #pragma unroll
-    for (int k = 0; k < kStripes / 4; ++k) raw[k] = src[k];
-  };
-  int next_bin;
-  uint4 next_raw[kStripes / 4];
-  fetch((int)threadIdx.x, next_bin, next_raw);
-  uint32_t carry[3] = {0, 0, 0};  // samples, chunks, slots of the earlier rounds
-  for (int j0 = 0; j0 < n; j0 += kPlanThreads) {
-    const int j = j0 + (int)threadIdx.x;
-    const bool live = j < n;
-    const int i = next_bin;
-    uint32_t cs[kStripes];
-#pragma unroll
-    for (int k = 0; k < kStripes / 4; ++k) {
-      const uint4 v = next_raw[k];
-      cs[4 * k] = v.x; cs[4 * k + 1] = v.y; cs[4 * k + 2] = v.z; cs[4 * k + 3] = v.w;
-    }
-    if (j0 + kPlanThreads < n) fetch(j + kPlanThreads, next_bin, next_raw);
-    uint32_t c = 0;
-#pragma unroll
-    for (int k = 0; k < kStripes; ++k) c += cs[k];
-    const uint32_t nch = live ? chunks_of(p, c) : 0u;
-    uint32_t v[3] = {live ? c : 0u, nch, nch > 1 ? nch : 0u}, tot[3];
-    block_scan3(v, tot, wsum);
-    if (live) {
-      const uint32_t pos = carry[0] + v[0], ch = carry[1] + v[1], slot = carry[2] + v[2];
-      uint4 *cur = reinterpret_cast<uint4 *>(a.w.cursor + (size_t)i * kStripes);
-      uint32_t run = pos;
-#pragma unroll
-      for (int k = 0; k < kStripes; k += 4) {
-        const uint32_t c0 = run, c1 = c0 + cs[k], c2 = c1 + cs[k + 1], c3 = c2 + cs[k + 2];
-        cur[k / 4] = make_uint4(c0, c1, c2, c3);
-        run = c3 + cs[k + 3];
-      }
-      a.w.bin_start[i] = pos;
-      a.w.bin_nch[i] = nch;
-      a.w.bin_slot0[i] = nch > 1 ? slot : kNoSlot;
-      for (uint32_t k = 0; k < nch; ++k) {
-        const uint32_t first = k * (uint32_t)p.chunk;
-        const uint32_t cnt = c > first ? min((uint32_t)p.chunk, c - first) : 0u;
-        a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 3; ++k) carry[k] += tot[k];
-    __syncthreads();  // wsum is reused by the next round
+  for (int k = 0; k < kStripes / 4; ++k) {
+    const uint4 x = src[k];
+    cs[4 * k] = x.x; cs[4 * k + 1] = x.y; cs[4 * k + 2] = x.z; cs[4 * k + 3] = x.w;
   }
-  if (threadIdx.x == 0) *a.w.nchunks = carry[1];
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < kStripes; ++k) c += cs[k];
+  const uint32_t nch = live ? chunks_of(p, c) : 0u;
+  uint32_t v[3] = {live ? c : 0u, nch, nch > 1 ? nch : 0u}, tot[3];
+  block_scan3(v, tot, wsum);
+  // publish this block's totals: value << 1 | 1, so a zero word means "not yet"
+  unsigned long long *status = a.w.plan_status;
+  if (threadIdx.x == 0)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      __hip_atomic_store(&status[3 * blockIdx.x + k], ((unsigned long long)tot[k] << 1) | 1ull,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // add the totals of all earlier blocks
+  uint32_t pre[3] = {0, 0, 0};
+  for (int b = threadIdx.x; b < (int)blockIdx.x; b += kPlanBlock)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      unsigned long long x = 0;
+      for (uint32_t spin = 0; spin < kPlanSpinLimit; ++spin) {
+        x = __hip_atomic_load(&status[3 * b + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (x & 1ull) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      pre[k] += (uint32_t)(x >> 1);
+    }
+  uint32_t pre_tot[3];
+  block_scan3(pre, pre_tot, wsum);
+  if (live) {
+    const uint32_t pos = pre_tot[0] + v[0], ch = pre_tot[1] + v[1], slot = pre_tot[2] + v[2];
+    uint4 *cur = reinterpret_cast<uint4 *>(a.w.cursor + (size_t)i * kStripes);
+    uint32_t run = pos;
+#pragma unroll
+    for (int k = 0; k < kStripes; k += 4) {
+      const uint32_t c0 = run, c1 = c0 + cs[k], c2 = c1 + cs[k + 1], c3 = c2 + cs[k + 2];
+      cur[k / 4] = make_uint4(c0, c1, c2, c3);
+      run = c3 + cs[k + 3];
+    }
+    a.w.bin_start[i] = pos;
+    a.w.bin_nch[i] = nch;
+    a.w.bin_slot0[i] = nch > 1 ? slot : kNoSlot;
+    for (uint32_t k = 0; k < nch; ++k) {
+      const uint32_t first = k * (uint32_t)p.chunk;
+      const uint32_t cnt = c > first ? min((uint32_t)p.chunk, c - first) : 0u;
+      a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
+    }
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *a.w.nchunks = pre_tot[1] + tot[1];
 }
 
 // ------------------------------------------------------------- scatter pass
@@ -1091,12 +1106,24 @@ hipError_t launch_tile_and_merge(const BinArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The striped bin counts and, after them, the plan blocks' published totals
+// (3 words each): one region, cleared by one fill before the count pass.
+size_t status_offset(const BinPlan &p) {
+  return align256((size_t)p.nbins * kStripes * sizeof(uint32_t));
+}
+size_t counts_and_status_bytes(const BinPlan &p) {
+  const size_t blocks = ((size_t)p.nbins + kPlanBlock - 1) / kPlanBlock;
+  return align256(status_offset(p) + blocks * 3 * sizeof(unsigned long long));
+}
+
 template <typename T>
 hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   const BinPlan &p = a.p;
   hipError_t e;
   // the striped counts start at zero; the plan writes the cursors
-  e = launch_zero(a.w.counts, (size_t)p.nbins * kStripes * sizeof(uint32_t), s);
+  e = launch_zero(a.w.counts, counts_and_status_bytes(p), s);
   if (e != hipSuccess) return e;
   if (p.S > p.pyramid_rows) {
     prof_begin(s);
@@ -1112,7 +1139,8 @@ hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   prof_end(s, "bin_count");
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(s);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)((p.nbins + kPlanBlock - 1) / kPlanBlock)),
+                     dim3(kPlanBlock), 0, s, a);
   prof_end(s, "bin_plan");
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin(s);
@@ -1128,7 +1156,6 @@ hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
@@ -1213,7 +1240,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
     return base ? base + o : nullptr;
   };
   const size_t nb4 = (size_t)(p.nbins + 3) / 4 * 4;
-  char *cc = take((size_t)p.nbins * kStripes * sizeof(uint32_t));
+  char *cc = take(counts_and_status_bytes(p));
   char *cu = take((size_t)p.nbins * kStripes * sizeof(uint32_t));
   char *bs = take(nb4 * sizeof(uint32_t));
   char *bn = take(nb4 * sizeof(uint32_t));
@@ -1225,6 +1252,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
   char *sl = take((size_t)p.max_slots * E * E * p.D * sizeof(float));
   if (w) {
     w->counts = reinterpret_cast<uint32_t *>(cc);
+    w->plan_status = reinterpret_cast<unsigned long long *>(cc + status_offset(p));
     w->cursor = reinterpret_cast<uint32_t *>(cu);
     w->bin_start = reinterpret_cast<uint32_t *>(bs);
     w->bin_nch = reinterpret_cast<uint32_t *>(bn);

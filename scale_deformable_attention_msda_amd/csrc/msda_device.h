@@ -248,6 +248,14 @@ __device__ inline void pack(const float *x, uint32_t (&w)[WORDS]) {
 
 // ------------------------------------------------------------ reductions
 
+// Workgroup barrier for data handed between waves through LDS only: unlike
+// __syncthreads() it does not wait for the wave's outstanding global stores.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // DPP lane moves inside a 16-lane row (gfx9 encodings of dpp_ctrl).
 constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]

@@ -80,7 +80,10 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   using RL = RowLayout<T, D>;
   constexpr int G = RL::G;
   __shared__ Level lv[kMaxLevels];
-  extern __shared__ Corners geo[];  // [L*K][hqb]
+  // [L*K][hqb + 1]: the odd row stride (in 32-byte entries) spreads the
+  // phase-1 stores of consecutive samples (consecutive j) over all LDS banks
+  extern __shared__ Corners geo[];
+  const int gs_stride = hqb + 1;
 
   const int K = (int)a.K, LK = (int)(a.L * a.K), M = (int)a.M;
   const int64_t total_hq = a.nb * a.Q * a.M;
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
                    (uint32_t)(m * D * (int)sizeof(T)), cs, lx, ly);
 #pragma unroll
     for (int c = 0; c < 4; ++c) cs.w[c] *= w;
-    geo[j * hqb + hl] = cs;
+    geo[j * gs_stride + hl] = cs;
   }
   __syncthreads();
 
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   for (int i = 0; i < RL::VEC; ++i) acc[i] = 0.0f;
 #pragma unroll 2
   for (int j = 0; j < LK; ++j) {
-    const Corners cs = geo[j * hqb + grp];
+    const Corners cs = geo[j * gs_stride + grp];
     uint32_t raw[4][RL::WORDS];
 #pragma unroll
     for (int c = 0; c < 4; ++c) buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[c]);
@@ -176,9 +179,11 @@ __global__ __launch_bounds__(kMaxBlock) void bwd_kernel(LaunchArgs a, int hqb) {
   extern __shared__ char smem[];
 
   const int K = (int)a.K, LK = (int)(a.L * a.K), M = (int)a.M;
-  Corners *geo = reinterpret_cast<Corners *>(smem);            // [LK][hqb]
-  SampleAux *aux = reinterpret_cast<SampleAux *>(geo + LK * hqb);  // [LK][hqb]
-  float *res = reinterpret_cast<float *>(aux + LK * hqb);      // [hqb*LK][3] in sample order
+  // [LK][hqb + 1]: odd row strides spread the phase-1 stores over all banks
+  const int gs_stride = hqb + 1;
+  Corners *geo = reinterpret_cast<Corners *>(smem);                      // [LK][hqb + 1]
+  SampleAux *aux = reinterpret_cast<SampleAux *>(geo + LK * gs_stride);  // [LK][hqb + 1]
+  float *res = reinterpret_cast<float *>(aux + LK * gs_stride);          // [hqb*LK][3] in sample order
 
   const int64_t total_hq = a.nb * a.Q * a.M;
   const int64_t hq0 = logical_block() * hqb;
@@ -207,8 +212,8 @@ __global__ __launch_bounds__(kMaxBlock) void bwd_kernel(LaunchArgs a, int hqb) {
     ax.u = u;
     ax.v = v;
     ax.l = j / K;
-    geo[j * hqb + hl] = cs;
-    aux[j * hqb + hl] = ax;
+    geo[j * gs_stride + hl] = cs;
+    aux[j * gs_stride + hl] = ax;
   }
   __syncthreads();
 
@@ -228,8 +233,8 @@ __global__ __launch_bounds__(kMaxBlock) void bwd_kernel(LaunchArgs a, int hqb) {
       unpack<T, RL::WORDS>(gw, g);
     }
     for (int j = 0; j < LK; ++j) {
-      const Corners cs = geo[j * hqb + grp];
-      const SampleAux ax = aux[j * hqb + grp];
+      const Corners cs = geo[j * gs_stride + grp];
+      const SampleAux ax = aux[j * gs_stride + grp];
       uint32_t raw[4][RL::WORDS];
 #pragma unroll
       for (int c = 0; c < 4; ++c) buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[c]);
@@ -314,7 +319,7 @@ hipError_t fwd_launch(const LaunchArgs &a, hipStream_t stream) {
   const int64_t total_hq = a.nb * a.Q * a.M;
   const int64_t blocks = padded_grid((total_hq + hqb - 1) / hqb);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)LK * hqb * sizeof(Corners);
+  const size_t lds = (size_t)LK * (hqb + 1) * sizeof(Corners);
   prof_begin(stream);
   hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds, stream,
                      a, hqb);
@@ -331,7 +336,8 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
   const int64_t total_hq = a.nb * a.Q * a.M;
   const int64_t blocks = padded_grid((total_hq + hqb - 1) / hqb);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)LK * hqb * per_sample;
+  const size_t lds = (size_t)LK * (hqb + 1) * (sizeof(Corners) + sizeof(SampleAux)) +
+                    (size_t)LK * hqb * 3 * sizeof(float);
   prof_begin(stream);
   hipLaunchKernelGGL((bwd_kernel<T, D, AccT>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
                      stream, a, hqb);

@@ -67,6 +67,7 @@ struct BinPlan {
 // are fixed by binned_layout()).
 struct BinScratch {
   uint32_t *counts;     // [nbins][stripes] samples per bin, per block stripe
+  unsigned long long *plan_status;  // [plan blocks][3] published totals (value << 1 | 1)
   uint32_t *cursor;     // [nbins][stripes] fill cursor of the id scatter
   uint32_t *bin_start;  // [nbins] first sorted position of a bin
   uint32_t *bin_nch;    // [nbins] chunks of a bin
