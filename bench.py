@@ -39,14 +39,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def bytes_model(wl: workloads.Workload) -> dict:
+def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
     """Algorithmic (compulsory) HBM bytes per launch of each kernel, each tensor once.
 
     For the encoder workloads every pyramid pixel is the reference point of a
     query and offsets are a few pixels, so every value row is touched and the
     whole value tensor counts.  Per-sample figures: loc 2 elements, attn 1
     element; the binned path also writes and reads one 16-byte record
-    (id, location, weight) per sample."""
+    (id, location, weight) per sample.  The fill kernel clears the grad_value
+    accumulator on the atomic path and the per-bin counters (8 stripes of
+    4 bytes per 8x8 tile of every batch and head, plus 24 bytes per 256 bins of
+    plan status) on the binned path."""
     elt = 4 if wl.dtype == "fp32" else 2
     B, S, Q, M, D, L, K = wl.B, wl.S, wl.num_queries, wl.M, wl.D, wl.L, wl.K
     n = B * Q * M * L * K
@@ -55,13 +58,15 @@ def bytes_model(wl: workloads.Workload) -> dict:
     attn = n * elt
     out = B * Q * M * D * elt
     recs = n * 16
+    nbins = B * M * sum(-(-h // 8) * -(-w // 8) for h, w in wl.shapes)
+    counters = nbins * 8 * 4 + -(-nbins // 256) * 24
     return {
         "samples": n,
         # forward: gather value, read loc / attn, write out
         "fwd": value + loc + attn + out,
         # atomic backward: value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written
         "bwd_atomic": value + loc + attn + out + value + loc + attn,
-        "zero": value,
+        "zero": value if scatter == "atomic" else counters,
         # binned passes
         "bin_count": loc,
         "bin_scatter": loc + attn + recs,
@@ -224,7 +229,7 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - w0
     records = msda.msda_profile_stop(64 * args.steps)
 
-    bm = bytes_model(wl)
+    bm = bytes_model(wl, args.scatter)
     per_kernel = {}
     for name, ms in records:
         per_kernel.setdefault(name, []).append(ms)
