@@ -47,9 +47,9 @@ def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
     whole value tensor counts.  Per-sample figures: loc 2 elements, attn 1
     element; the binned path also writes and reads one 16-byte record
     (id, location, weight) per sample.  The fill kernel clears the grad_value
-    accumulator on the atomic path and the per-bin counters (8 stripes of
-    4 bytes per 8x8 tile of every batch and head, plus 24 bytes per 256 bins of
-    plan status) on the binned path."""
+    accumulator on the atomic path and the per-bin counters (8 stripes, one
+    64-byte line each, per 8x8 tile of every batch and head, plus 24 bytes per
+    256 bins of plan status) on the binned path."""
     elt = 4 if wl.dtype == "fp32" else 2
     B, S, Q, M, D, L, K = wl.B, wl.S, wl.num_queries, wl.M, wl.D, wl.L, wl.K
     n = B * Q * M * L * K
@@ -59,7 +59,7 @@ def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
     out = B * Q * M * D * elt
     recs = n * 16
     nbins = B * M * sum(-(-h // 8) * -(-w // 8) for h, w in wl.shapes)
-    counters = nbins * 8 * 4 + -(-nbins // 256) * 24
+    counters = nbins * 8 * 64 + -(-nbins // 256) * 24
     return {
         "samples": n,
         # forward: gather value, read loc / attn, write out

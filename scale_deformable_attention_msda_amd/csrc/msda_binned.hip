@@ -54,6 +54,13 @@ constexpr int kHistLdsBytes = 48 * 1024;
 // kStripes): a coarse-level bin collects counts from ~100 blocks, and integer
 // atomics on one address from many blocks serialize.
 constexpr int kStripes = 8;
+// Every (bin, stripe) counter sits on a 64-byte line of its own: device-scope
+// atomics execute at the memory side one line at a time, so counters sharing
+// a line would serialize the blocks that update different ones.
+constexpr int kCounterWords = 16;
+__host__ __device__ inline size_t counter_index(int bin, int stripe) {
+  return ((size_t)bin * kStripes + stripe) * kCounterWords;
+}
 constexpr uint32_t kNoSlot = 0xffffffffu;
 
 // -------------------------------------------------------------- geometry
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   __syncthreads();
   for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
     const uint32_t n = hist[e];
-    if (n) __hip_atomic_fetch_add(&a.w.counts[bin_of_slot(p, lt, b, e) * kStripes + stripe], n,
+    if (n) __hip_atomic_fetch_add(&a.w.counts[counter_index(bin_of_slot(p, lt, b, e), stripe)], n,
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -323,12 +330,8 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
   const bool live = j < n;
   const int i = bin_of_order(p, ot, min(j, n - 1));
   uint32_t cs[kStripes];
-  const uint4 *src = reinterpret_cast<const uint4 *>(a.w.counts + (size_t)i * kStripes);
 #pragma unroll
-  for (int k = 0; k < kStripes / 4; ++k) {
-    const uint4 x = src[k];
-    cs[4 * k] = x.x; cs[4 * k + 1] = x.y; cs[4 * k + 2] = x.z; cs[4 * k + 3] = x.w;
-  }
+  for (int k = 0; k < kStripes; ++k) cs[k] = a.w.counts[counter_index(i, k)];
   uint32_t c = 0;
 #pragma unroll
   for (int k = 0; k < kStripes; ++k) c += cs[k];
@@ -359,13 +362,11 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
   block_scan3(pre, pre_tot, wsum);
   if (live) {
     const uint32_t pos = pre_tot[0] + v[0], ch = pre_tot[1] + v[1], slot = pre_tot[2] + v[2];
-    uint4 *cur = reinterpret_cast<uint4 *>(a.w.cursor + (size_t)i * kStripes);
     uint32_t run = pos;
 #pragma unroll
-    for (int k = 0; k < kStripes; k += 4) {
-      const uint32_t c0 = run, c1 = c0 + cs[k], c2 = c1 + cs[k + 1], c3 = c2 + cs[k + 2];
-      cur[k / 4] = make_uint4(c0, c1, c2, c3);
-      run = c3 + cs[k + 3];
+    for (int k = 0; k < kStripes; ++k) {
+      a.w.cursor[counter_index(i, k)] = run;
+      run += cs[k];
     }
     a.w.bin_start[i] = pos;
     a.w.bin_nch[i] = nch;
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
 #pragma unroll
     for (int k = 0; k < kReserve; ++k) {
       const int e = e0 + k * 256 + (int)threadIdx.x;
-      got[k] = n[k] ? __hip_atomic_fetch_add(&a.w.cursor[bin_of_slot(p, lt, b, e) * kStripes + stripe],
+      got[k] = n[k] ? __hip_atomic_fetch_add(&a.w.cursor[counter_index(bin_of_slot(p, lt, b, e), stripe)],
                                              n[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                     : 0u;
     }
@@ -1111,7 +1112,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // The striped bin counts and, after them, the plan blocks' published totals
 // (3 words each): one region, cleared by one fill before the count pass.
 size_t status_offset(const BinPlan &p) {
-  return align256((size_t)p.nbins * kStripes * sizeof(uint32_t));
+  return align256(counter_index(p.nbins, 0) * sizeof(uint32_t));
 }
 size_t counts_and_status_bytes(const BinPlan &p) {
   const size_t blocks = ((size_t)p.nbins + kPlanBlock - 1) / kPlanBlock;
@@ -1241,7 +1242,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
   };
   const size_t nb4 = (size_t)(p.nbins + 3) / 4 * 4;
   char *cc = take(counts_and_status_bytes(p));
-  char *cu = take((size_t)p.nbins * kStripes * sizeof(uint32_t));
+  char *cu = take(counter_index(p.nbins, 0) * sizeof(uint32_t));
   char *bs = take(nb4 * sizeof(uint32_t));
   char *bn = take(nb4 * sizeof(uint32_t));
   char *b0 = take(nb4 * sizeof(uint32_t));

@@ -66,9 +66,9 @@ struct BinPlan {
 // Device scratch carved out of the caller's workspace (byte offsets into it
 // are fixed by binned_layout()).
 struct BinScratch {
-  uint32_t *counts;     // [nbins][stripes] samples per bin, per block stripe
+  uint32_t *counts;     // [nbins][stripes] samples per bin, per block stripe, one 64-byte line each
   unsigned long long *plan_status;  // [plan blocks][3] published totals (value << 1 | 1)
-  uint32_t *cursor;     // [nbins][stripes] fill cursor of the id scatter
+  uint32_t *cursor;     // [nbins][stripes] fill cursor of the record scatter, one 64-byte line each
   uint32_t *bin_start;  // [nbins] first sorted position of a bin
   uint32_t *bin_nch;    // [nbins] chunks of a bin
   uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
