@@ -147,6 +147,8 @@ size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
  * scatter / accum_dtype:
  *   BINNED: accum_dtype must be FP32; spatial_shapes_host ([L,2] int64 on
  *           the host, the same values as spatial_shapes) plans the tiles.
+ *           Limits (else MSDA_ERR_UNSUPPORTED): at most 12288 8x8 tiles over
+ *           all levels, B*M <= 65535, B*Q*M*L*K < 2^32 - 1.
  *   ATOMIC: FP32 data -> accum FP32 (fp32 atomics into grad_value);
  *           BF16 data -> accum FP32 (atomics into an fp32 workspace, then one
  *           rounding to bf16) or accum BF16 (packed-bf16 atomics straight

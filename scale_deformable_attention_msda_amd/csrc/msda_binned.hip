@@ -95,63 +95,61 @@ __device__ inline float ldf(const void *base, int64_t i) {
 // argument's arrays with a per-sample level would turn every access into a
 // dependent load from the argument segment.
 struct LevelTab {
-  int H, W, ntx, ntiles, hist_base, bin_base;
+  int H, W, ntx, ntiles, tile_off, bin_base;
 };
 
 __device__ inline void stage_level_tab(const BinPlan &p, LevelTab *t) {
   if (threadIdx.x < (unsigned)p.L) {
     const int l = threadIdx.x;
-    t[l] = LevelTab{p.H[l], p.W[l], p.ntx[l], p.ntiles[l], p.hist_base[l], p.bin_base[l]};
+    t[l] = LevelTab{p.H[l], p.W[l], p.ntx[l], p.ntiles[l], p.tile_off[l], p.bin_base[l]};
   }
 }
 
-// Global bin of batch-local histogram slot e of batch b.
-__device__ inline int bin_of_slot(const BinPlan &p, const LevelTab *lt, int b, int e) {
+// Global bin of histogram slot e (a tile of one head, levels coarsest first)
+// of batch b, head m.
+__device__ inline int bin_of_slot(const BinPlan &p, const LevelTab *lt, int bm, int e) {
   int l = 0;
-  while (l + 1 < p.L && !(e >= lt[l].hist_base && e < lt[l].hist_base + p.M * lt[l].ntiles)) ++l;
-  const int rem = e - lt[l].hist_base;
-  const int m = rem / lt[l].ntiles, t = rem - m * lt[l].ntiles;
-  return lt[l].bin_base + (b * p.M + m) * lt[l].ntiles + t;
+  while (l + 1 < p.L && !(e >= lt[l].tile_off && e < lt[l].tile_off + lt[l].ntiles)) ++l;
+  return lt[l].bin_base + bm * lt[l].ntiles + (e - lt[l].tile_off);
 }
 
-// A thread's samples s0 + r * 256 (r = 0, 1, ...) inside one batch: the
-// head-query hq = s / (L K), the point j = s % (L K) and the head m = hq % M
-// advance by fixed steps instead of being divided out for every sample.
+// The count and scatter passes walk the samples of one (batch b, head m):
+// t = q * (L K) + j over the queries q and points j, sample id
+// ((b Q + q) M + m) (L K) + j.  A thread's samples t0 + 256 r (r = 0, 1, ...)
+// advance j and the id by fixed steps instead of dividing t for every sample.
 struct SampleWalk {
-  uint32_t hq, j, m;
+  uint32_t j, id;
 };
 
-__device__ inline SampleWalk walk_start(const BinPlan &p, uint32_t s) {
+__device__ inline SampleWalk walk_start(const BinPlan &p, int b, int m, uint32_t t) {
+  const uint32_t LK = (uint32_t)(p.L * p.K);
+  const uint32_t q = fdiv(t, p.div_lk);
   SampleWalk w;
-  w.hq = fdiv(s, p.div_lk);
-  w.j = s - w.hq * (uint32_t)(p.L * p.K);
-  w.m = w.hq - fdiv(w.hq, p.div_m) * (uint32_t)p.M;
+  w.j = t - q * LK;
+  w.id = (((uint32_t)b * (uint32_t)p.Q + q) * (uint32_t)p.M + (uint32_t)m) * LK + w.j;
   return w;
 }
 
 __device__ inline void walk_step(const BinPlan &p, SampleWalk &w) {
   w.j += p.step_j;
-  w.hq += p.step_hq;
-  w.m += p.step_m;  // step_m < M, plus at most one carry: one subtraction wraps m
-  if (w.j >= (uint32_t)(p.L * p.K)) {
+  w.id += p.step_id;
+  if (w.j >= (uint32_t)(p.L * p.K)) {  // one more query: j wraps, the id skips the other heads
     w.j -= (uint32_t)(p.L * p.K);
-    ++w.hq;
-    ++w.m;
+    w.id += p.wrap_id;
   }
-  if (w.m >= (uint32_t)p.M) w.m -= (uint32_t)p.M;
 }
 
-// Histogram slot of the walk's current sample at normalised (u, v), or -1 for
-// a dead sample (no corner inside its level).  The level is j / K through a
-// 16-bit fixed-point reciprocal (exact for j < L K <= 64).
+// Histogram slot (tile of the head, levels coarsest first) of the walk's
+// current sample at normalised (u, v), or -1 for a dead sample (no corner
+// inside its level).  The level is j / K through a 16-bit fixed-point
+// reciprocal (exact for j < L K <= 64).
 __device__ inline int slot_of_sample(const BinPlan &p, const LevelTab *lt, const SampleWalk &w,
                                      float u, float v) {
   const LevelTab t = lt[__umul24(w.j, p.magic_k) >> 16];
   Cell c;
   if (!cell_of(u, v, t.H, t.W, c)) return -1;
   const uint32_t x = (uint32_t)max(c.x0, 0), y = (uint32_t)max(c.y0, 0);
-  return t.hist_base + (int)__umul24(w.m, (uint32_t)t.ntiles) +
-         (int)(__umul24(y / kTile, (uint32_t)t.ntx) + x / kTile);
+  return t.tile_off + (int)(__umul24(y / kTile, (uint32_t)t.ntx) + x / kTile);
 }
 
 // Sampling location of sample `id` (both coordinates in one load).
@@ -170,7 +168,7 @@ __device__ inline void load_loc(const void *loc, int64_t id, float &u, float &v)
 
 // --------------------------------------------------------------- count pass
 
-// Every thread owns kPer samples s0 + r*256 + threadIdx.x; all their locations
+// Every thread owns kPer samples t0 + r*256 of its block's (batch, head); all their locations
 // are loaded before any is used, so the loads overlap.
 constexpr int kPer = kCountSamples / 256;
 
@@ -178,26 +176,33 @@ template <typename T>
 __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   extern __shared__ uint32_t hist[];
   const BinPlan &p = a.p;
-  const int b = blockIdx.y;
+  const int bm = blockIdx.y;  // batch * M + head
+  const int b = bm / p.M, m = bm - b * p.M;
   const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
   __shared__ LevelTab lt[kMaxLevels];
   stage_level_tab(p, lt);
-  const uint32_t per_b = p.total / (uint32_t)p.B;      // samples of one batch (< 2^32)
-  const uint32_t s0 = blockIdx.x * kCountSamples + threadIdx.x;
-  const uint32_t id0 = (uint32_t)b * per_b;
-  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
+  const uint32_t per_head = (uint32_t)p.Q * (uint32_t)(p.L * p.K);  // samples of one (batch, head)
+  const uint32_t t0 = blockIdx.x * kCountSamples + threadIdx.x;
+  for (int e = threadIdx.x; e < p.tiles_bm; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  // branch-free loads (clamped index) so all kPer loads are in flight together;
-  // each sample is binned as soon as its own load has arrived
+  // all kPer loads in flight together (samples past the head's end reload its
+  // first one); each sample is binned as soon as its own load has arrived
+  const uint32_t first_id = ((uint32_t)b * (uint32_t)p.Q * (uint32_t)p.M + (uint32_t)m) *
+                            (uint32_t)(p.L * p.K);
   float u[kPer], v[kPer];
+  {
+    SampleWalk w = walk_start(p, b, m, t0);
 #pragma unroll
-  for (int r = 0; r < kPer; ++r)
-    load_loc<T>(a.loc, id0 + min(s0 + r * 256, per_b - 1), u[r], v[r]);
-  SampleWalk w = walk_start(p, s0);
+    for (int r = 0; r < kPer; ++r) {
+      load_loc<T>(a.loc, t0 + r * 256 < per_head ? w.id : first_id, u[r], v[r]);
+      walk_step(p, w);
+    }
+  }
+  SampleWalk w = walk_start(p, b, m, t0);
   uint32_t dead = 0;  // bit r: sample r has no corner inside its level
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    if (s0 + r * 256 >= per_b) break;
+    if (t0 + r * 256 >= per_head) break;
     const int e = slot_of_sample(p, lt, w, u[r], v[r]);
     if (e < 0) dead |= 1u << r;
     else __hip_atomic_fetch_add(&hist[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -207,14 +212,14 @@ __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   while (dead) {
     const int r = __builtin_ctz(dead);
     dead &= dead - 1;
-    const int64_t id = id0 + s0 + r * 256;
+    const int64_t id = walk_start(p, b, m, t0 + r * 256).id;
     store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + id, 0.0f);
     store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * id, 0.0f, 0.0f);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) {
+  for (int e = threadIdx.x; e < p.tiles_bm; e += blockDim.x) {
     const uint32_t n = hist[e];
-    if (n) __hip_atomic_fetch_add(&a.w.counts[counter_index(bin_of_slot(p, lt, b, e), stripe)], n,
+    if (n) __hip_atomic_fetch_add(&a.w.counts[counter_index(bin_of_slot(p, lt, bm, e), stripe)], n,
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -386,31 +391,41 @@ template <typename T>
 __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
   extern __shared__ uint32_t hist[];
   const BinPlan &p = a.p;
-  const int b = blockIdx.y;
+  const int bm = blockIdx.y;  // batch * M + head
+  const int b = bm / p.M, m = bm - b * p.M;
   const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
   __shared__ LevelTab lt[kMaxLevels];
   stage_level_tab(p, lt);
-  const uint32_t per_b = p.total / (uint32_t)p.B;      // samples of one batch (< 2^32)
-  const uint32_t s0 = blockIdx.x * kCountSamples + threadIdx.x;
-  const uint32_t id0 = (uint32_t)b * per_b;
-  for (int e = threadIdx.x; e < p.hist_size; e += blockDim.x) hist[e] = 0;
+  const uint32_t per_head = (uint32_t)p.Q * (uint32_t)(p.L * p.K);
+  const uint32_t t0 = blockIdx.x * kCountSamples + threadIdx.x;
+  const uint32_t first_id = ((uint32_t)b * (uint32_t)p.Q * (uint32_t)p.M + (uint32_t)m) *
+                            (uint32_t)(p.L * p.K);
+  for (int e = threadIdx.x; e < p.tiles_bm; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  // branch-free loads (clamped index) so all loads are in flight together;
-  // each sample is ranked as soon as its own location has arrived
+  // all loads in flight together (samples past the head's end reload its
+  // first one); each sample is ranked as soon as its own location has arrived
   float u[kPer], v[kPer], aw[kPer];
+  uint32_t sid[kPer];
+  {
+    SampleWalk w = walk_start(p, b, m, t0);
 #pragma unroll
-  for (int r = 0; r < kPer; ++r)
-    load_loc<T>(a.loc, id0 + min(s0 + r * 256, per_b - 1), u[r], v[r]);
+    for (int r = 0; r < kPer; ++r) {
+      sid[r] = t0 + r * 256 < per_head ? w.id : first_id;
+      walk_step(p, w);
+    }
+  }
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) aw[r] = ldf<T>(a.attn, id0 + min(s0 + r * 256, per_b - 1));
+  for (int r = 0; r < kPer; ++r) load_loc<T>(a.loc, sid[r], u[r], v[r]);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) aw[r] = ldf<T>(a.attn, sid[r]);
   int slot[kPer];
   uint32_t rank[kPer];
-  SampleWalk w = walk_start(p, s0);
+  SampleWalk w = walk_start(p, b, m, t0);
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     slot[r] = -1;
     rank[r] = 0;
-    if (s0 + r * 256 < per_b) {
+    if (t0 + r * 256 < per_head) {
       slot[r] = slot_of_sample(p, lt, w, u[r], v[r]);
       if (slot[r] >= 0)
         rank[r] = __hip_atomic_fetch_add(&hist[slot[r]], 1u, __ATOMIC_RELAXED,
@@ -423,17 +438,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
   // that stripe's first sorted position; kReserve returning atomics per
   // thread are in flight together
   constexpr int kReserve = 8;
-  for (int e0 = 0; e0 < p.hist_size; e0 += 256 * kReserve) {
+  for (int e0 = 0; e0 < p.tiles_bm; e0 += 256 * kReserve) {
     uint32_t n[kReserve], got[kReserve];
 #pragma unroll
     for (int k = 0; k < kReserve; ++k) {
       const int e = e0 + k * 256 + (int)threadIdx.x;
-      n[k] = e < p.hist_size ? hist[e] : 0u;
+      n[k] = e < p.tiles_bm ? hist[e] : 0u;
     }
 #pragma unroll
     for (int k = 0; k < kReserve; ++k) {
       const int e = e0 + k * 256 + (int)threadIdx.x;
-      got[k] = n[k] ? __hip_atomic_fetch_add(&a.w.cursor[counter_index(bin_of_slot(p, lt, b, e), stripe)],
+      got[k] = n[k] ? __hip_atomic_fetch_add(&a.w.cursor[counter_index(bin_of_slot(p, lt, bm, e), stripe)],
                                              n[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                     : 0u;
     }
@@ -447,7 +462,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     if (slot[r] >= 0)
-      a.w.recs[hist[slot[r]] + rank[r]] = make_uint4(id0 + s0 + r * 256, __float_as_uint(u[r]),
+      a.w.recs[hist[slot[r]] + rank[r]] = make_uint4(sid[r], __float_as_uint(u[r]),
                                                      __float_as_uint(v[r]), __float_as_uint(aw[r]));
   }
 }
@@ -1132,9 +1147,10 @@ hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   prof_end(s, "bin_zero_tail");
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int64_t per_b = p.Q * p.M * p.L * p.K;
-  const dim3 grid((unsigned)((per_b + kCountSamples - 1) / kCountSamples), (unsigned)p.B);
-  const size_t hist = (size_t)p.hist_size * sizeof(uint32_t);
+  const int64_t per_head = p.Q * p.L * p.K;
+  const dim3 grid((unsigned)((per_head + kCountSamples - 1) / kCountSamples),
+                  (unsigned)(p.B * p.M));
+  const size_t hist = (size_t)p.tiles_bm * sizeof(uint32_t);
   prof_begin(s);
   hipLaunchKernelGGL((count_kernel<T>), grid, dim3(256), hist, s, a);
   prof_end(s, "bin_count");
@@ -1201,28 +1217,28 @@ bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, in
     *why = "too many samples or bins for the binned backward";
     return false;
   }
-  if ((int64_t)M * tiles * 4 > kHistLdsBytes) {
-    *why = "num_heads x tiles of the pyramid exceed the per-block histogram";
+  if (B * M > 65535) {  // one grid row of the count and scatter passes per (batch, head)
+    *why = "batch x num_heads exceeds 65535 for the binned backward";
+    return false;
+  }
+  if ((int64_t)tiles * 4 > kHistLdsBytes) {
+    *why = "the tiles of the pyramid exceed the per-block histogram";
     return false;
   }
   p.total = (uint32_t)total;
   p.div_lk = make_fastdiv((uint32_t)(L * K));
   p.div_k = make_fastdiv((uint32_t)K);
-  p.div_m = make_fastdiv((uint32_t)M);
-  p.step_hq = 256u / (uint32_t)(L * K);
   p.step_j = 256u % (uint32_t)(L * K);
-  p.step_m = p.step_hq % (uint32_t)M;
+  p.step_id = 256u / (uint32_t)(L * K) * (uint32_t)(M * L * K) + p.step_j;
+  p.wrap_id = (uint32_t)((M - 1) * L * K);
   p.magic_k = ((1u << 16) + (uint32_t)K - 1) / (uint32_t)K;
   p.nbins = (int)nbins;
-  p.hist_size = (int)(M * tiles);
   // coarsest level (highest index) first
-  int run_bins = 0, run_hist = 0, run_tiles = 0;
+  int run_bins = 0, run_tiles = 0;
   for (int l = L - 1; l >= 0; --l) {
     p.bin_base[l] = run_bins;
-    p.hist_base[l] = run_hist;
     p.tile_off[l] = run_tiles;
     run_bins += (int)(B * M) * p.ntiles[l];
-    run_hist += M * p.ntiles[l];
     run_tiles += p.ntiles[l];
   }
   p.tiles_bm = run_tiles;

@@ -46,20 +46,19 @@ struct BinPlan {
   int ntx[kMaxLevels];         // tiles per row of level l
   int ntiles[kMaxLevels];      // tiles of level l (per batch and head)
   int bin_base[kMaxLevels];    // first bin of level l
-  int hist_base[kMaxLevels];   // first per-batch histogram slot of level l
   int tile_off[kMaxLevels];    // first tile of level l among the tiles of one (batch, head),
                                // coarsest level first
   int tiles_bm;                // tiles of all levels of one (batch, head)
   int nbins;                   // B * M * (tiles of all levels)
-  int hist_size;               // M * (tiles of all levels): one batch's bins
   int max_chunks;              // nbins + ceil(total / chunk)
   int max_slots;               // 2 * ceil(total / chunk)
   int64_t pyramid_rows;        // sum_l H_l * W_l
   uint32_t total;              // B*Q*M*L*K samples
-  FastDiv div_lk, div_k, div_m;  // by L*K, K and M
-  // a stride of 256 samples inside one batch: whole head-queries, points and
-  // heads it advances (256 / (L K), 256 % (L K), (256 / (L K)) % M)
-  uint32_t step_hq, step_j, step_m;
+  FastDiv div_lk, div_k;       // by L*K and K
+  // a stride of 256 samples of one (batch, head), t = q (L K) + j: the points
+  // it advances (256 % (L K)), the sample ids it advances without and the
+  // extra ids with a wrap of j (one query more: the other M - 1 heads)
+  uint32_t step_j, step_id, wrap_id;
   uint32_t magic_k;              // ceil(2^16 / K): j / K = (j * magic_k) >> 16 for j < L K
 };
 
