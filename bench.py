@@ -6,9 +6,10 @@ of a 100x167, 50x84, 25x42, 13x21 pyramid, i.e. an ~800x1333 input at strides
 8-64), M=8 heads, D=32, L=4 levels, K=4 points, fp32, offsets N(0, 2 px),
 softmax weights; synthetic, seeded (workloads.py).
 
-A step is one msda_forward plus one msda_backward (grad_value by fp32 atomics,
-grad_sampling_locations, grad_attention_weights) over one batch of inputs that
-is already resident in HBM.  `--rotate R` cycles over R independently generated
+A step is one msda_forward (direct gather; `--gather binned` times
+msda_forward_binned instead) plus one msda_backward (grad_value, grad_sampling_locations, grad_attention_weights;
+destination-binned by default) over one batch of inputs that is already
+resident in HBM.  `--rotate R` cycles over R independently generated
 input batches so that consecutive steps do not find their operands in the
 L2 / MALL caches (R=1 times the warm, cache-resident regime).
 
@@ -60,10 +61,17 @@ def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
     recs = n * 16
     nbins = B * M * sum(-(-h // 8) * -(-w // 8) for h, w in wl.shapes)
     counters = nbins * 8 * 64 + -(-nbins // 256) * 24
+    hq = B * Q * M
     return {
         "samples": n,
         # forward: gather value, read loc / attn, write out
         "fwd": value + loc + attn + out,
+        # query-binned forward: the key reads the K finest-level points of every
+        # head-query and writes a 4-byte key; the scatter reads the keys and writes
+        # 4-byte sorted indices; the tile pass reads them once more
+        "fwd_count": hq * K * 2 * elt + hq * 4,
+        "fwd_scatter": hq * 8,
+        "fwd_tile": value + loc + attn + out + hq * 4,
         # atomic backward: value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written
         "bwd_atomic": value + loc + attn + out + value + loc + attn,
         "zero": value if scatter == "atomic" else counters,
@@ -148,6 +156,8 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=4, help="input batches cycled over")
     ap.add_argument("--scatter", default="binned", choices=["binned", "atomic"],
                     help="how the backward forms grad_value")
+    ap.add_argument("--gather", default="direct", choices=["direct", "binned"],
+                    help="forward schedule: msda_forward (direct gather) or msda_forward_binned")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_encoder.txt"),
                     help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -201,10 +211,15 @@ def main(argv=None) -> int:
     ga = torch.empty_like(t0["attention_weights"])
     dims = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
     sc = msda.MSDA_SCATTER_BINNED if args.scatter == "binned" else msda.MSDA_SCATTER_ATOMIC
-    need = msda.msda_backward_workspace_bytes(dims, 0 if wl.dtype == "fp32" else 1,
-                                              msda.MSDA_FP32, sc, shapes_host)
+    dcode = 0 if wl.dtype == "fp32" else 1
+    need_b = msda.msda_backward_workspace_bytes(dims, dcode, msda.MSDA_FP32, sc, shapes_host)
+    need_f = (msda.msda_forward_binned_workspace_bytes(dims, dcode, shapes_host)
+              if args.gather == "binned" else 0)
+    # one workspace serves both calls: they run one after the other on one stream
+    need = max(need_b, need_f)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    log(f"[bench] scatter={args.scatter}, workspace {need / 2**20:.1f} MiB")
+    log(f"[bench] gather={args.gather} (workspace {need_f / 2**20:.1f} MiB), "
+        f"scatter={args.scatter} (workspace {need_b / 2**20:.1f} MiB)")
 
     def ops(t):
         return (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"],
@@ -212,7 +227,8 @@ def main(argv=None) -> int:
 
     def step(i):
         t = batches[i % len(batches)]
-        msda.msda_forward(*ops(t), out=out, stream=stream)
+        msda.msda_forward(*ops(t), out=out, stream=stream, gather=args.gather,
+                          spatial_shapes_host=shapes_host, workspace=ws)
         msda.msda_backward(*ops(t), t["grad_out"], grad_value=gv, grad_loc=gl, grad_attn=ga,
                            scatter=args.scatter, spatial_shapes_host=shapes_host,
                            workspace=ws, stream=stream)
@@ -241,8 +257,9 @@ def main(argv=None) -> int:
         kernels[name] = {"us": round(us, 3), "launches_per_step": launches_per_step,
                          "alg_bytes": nbytes,
                          "gbps": round(nbytes / (us * 1e-6) / 1e9, 1) if nbytes else None}
-    fwd_us = sum(k["us"] * k["launches_per_step"] for n, k in kernels.items() if n == "fwd")
-    bwd_us = sum(k["us"] * k["launches_per_step"] for n, k in kernels.items() if n != "fwd")
+    is_fwd = lambda n: n == "fwd" or n.startswith("fwd_")
+    fwd_us = sum(k["us"] * k["launches_per_step"] for n, k in kernels.items() if is_fwd(n))
+    bwd_us = sum(k["us"] * k["launches_per_step"] for n, k in kernels.items() if not is_fwd(n))
     ms_per_step = wall / args.steps * 1e3
     dom_name = max(kernels, key=lambda n: kernels[n]["us"] * kernels[n]["launches_per_step"])
     dom = kernels[dom_name]
@@ -265,7 +282,7 @@ def main(argv=None) -> int:
         "config": {"workload": f"{wl.name}: B={wl.B} Q=S={wl.num_queries} M={wl.M} D={wl.D} "
                                f"L={wl.L} (" + ", ".join(f"{h}x{w}" for h, w in wl.shapes) +
                                f") K={wl.K} {wl.dtype}, forward + backward",
-                   "scatter": args.scatter, "rotate": args.rotate},
+                   "gather": args.gather, "scatter": args.scatter, "rotate": args.rotate},
         "fwd_us": round(fwd_us, 3),
         "bwd_us": round(bwd_us, 3),
         "kernels": kernels,

@@ -98,11 +98,46 @@ typedef struct {
  * sampling_locations, attention_weights).  Accumulates in fp32 and rounds
  * once to `dtype` (round to nearest even for BF16).  Deterministic: the
  * same inputs give bit-identical outputs.  Q = 0 or B = 0 enqueues nothing.
+ * Each block gathers the corner rows of a run of head-queries straight from
+ * global memory (through the L1/L2 caches); no workspace.
  */
 msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          const int64_t *level_start_index, const void *sampling_locations,
                          const void *attention_weights, void *out, const msda_dims *dims,
                          msda_dtype dtype, void *stream);
+
+/*
+ * Bytes of device workspace msda_forward_binned needs for these sizes and
+ * dtype (about 8 bytes per head-query plus per-block histograms), planned
+ * from spatial_shapes_host ([L,2] int64 on the host, the same values as
+ * spatial_shapes).  Returns SIZE_MAX when msda_forward_binned would reject
+ * the call, including sizes the binned gather does not support: head rows
+ * other than 64, 128 or 256 bytes, K > 8, too few queries per region of the
+ * finest level, or windows that do not fit in LDS (msda_last_error() then
+ * says why).
+ */
+size_t msda_forward_binned_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                           const int64_t *spatial_shapes_host);
+
+/*
+ * The forward of msda_forward computed on a second schedule (equal results
+ * up to the order of the fp32 additions; deterministic).  Head-queries are
+ * counting-sorted by the region (bin) of the finest level their points fall
+ * in; one block per bin stages, level by level, the value rows its samples
+ * can reach in LDS and gathers from there; a point whose cell leaves that
+ * window is gathered from global memory.  It pays off only when gathering
+ * from LDS saves more than the sort and the staging cost, which this
+ * library's measurements on MI355X have not shown for the encoder workloads
+ * (msda_forward is faster there); it is kept for study and comparison.
+ * workspace must hold at least msda_forward_binned_workspace_bytes() bytes
+ * (16-byte aligned; contents on entry do not matter and are clobbered),
+ * else MSDA_ERR_WORKSPACE.
+ */
+msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes,
+                                const int64_t *level_start_index, const void *sampling_locations,
+                                const void *attention_weights, void *out, const msda_dims *dims,
+                                msda_dtype dtype, const int64_t *spatial_shapes_host,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* How msda_backward forms grad_value. */
 typedef enum {

@@ -6,7 +6,10 @@ has not been built this module raises on first use; there is no fallback.
 
 The functions keep the C names:
     msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
-                 attention_weights, out=None, stream=None) -> out
+                 attention_weights, out=None, stream=None, gather="direct",
+                 spatial_shapes_host=None, workspace=None) -> out
+        (gather="binned" calls msda_forward_binned)
+    msda_forward_binned_workspace_bytes(dims, dtype, spatial_shapes_host) -> int
     msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
                   attention_weights, grad_out, grad_value=None, grad_loc=None,
                   grad_attn=None, accum_dtype=None, scatter="binned",
@@ -73,6 +76,11 @@ def load_library(path: str = LIB_PATH):
     vp, i64p, dims_p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MsdaDims)
     lib.msda_forward.argtypes = [vp, i64p, i64p, vp, vp, vp, dims_p, ctypes.c_int, vp]
     lib.msda_forward.restype = ctypes.c_int
+    lib.msda_forward_binned.argtypes = [vp, i64p, i64p, vp, vp, vp, dims_p, ctypes.c_int, vp, vp,
+                                        ctypes.c_size_t, vp]
+    lib.msda_forward_binned.restype = ctypes.c_int
+    lib.msda_forward_binned_workspace_bytes.argtypes = [dims_p, ctypes.c_int, vp]
+    lib.msda_forward_binned_workspace_bytes.restype = ctypes.c_size_t
     lib.msda_backward.argtypes = [vp, i64p, i64p, vp, vp, vp, vp, vp, vp, dims_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
     lib.msda_backward.restype = ctypes.c_int
@@ -159,20 +167,52 @@ def _common(value, spatial_shapes, level_start_index, sampling_locations, attent
     return dims, dt
 
 
+def msda_forward_binned_workspace_bytes(dims: MsdaDims, dtype: int, spatial_shapes_host) -> int:
+    """Workspace bytes msda_forward_binned needs; raises when it would reject the call."""
+    import numpy as np
+
+    host = np.ascontiguousarray(np.asarray(spatial_shapes_host, dtype=np.int64))
+    n = int(load_library().msda_forward_binned_workspace_bytes(ctypes.byref(dims), dtype,
+                                                                host.ctypes.data))
+    if n == SIZE_MAX:
+        raise ValueError(f"msda_forward_binned_workspace_bytes: {msda_last_error()}")
+    return n
+
+
 def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
-                 attention_weights, out=None, stream=None):
-    """out[B, Q, M*D] = MSDA(...) computed by the library's forward kernel."""
+                 attention_weights, out=None, stream=None, gather="direct",
+                 spatial_shapes_host=None, workspace=None):
+    """out[B, Q, M*D] = MSDA(...) computed by the library's forward kernels.
+
+    gather: "direct" (default, msda_forward) or "binned" (msda_forward_binned: head-queries
+    sorted by region, gathers from LDS-staged windows; needs the level shapes on the host,
+    read from spatial_shapes when spatial_shapes_host is omitted, and a workspace, allocated
+    here when none is given)."""
     dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations,
                        attention_weights)
+    if gather not in ("binned", "direct"):
+        raise ValueError(f"gather {gather!r} is not 'binned' or 'direct'")
     shape = (dims.batch, dims.num_queries, dims.num_heads * dims.head_dim)
     if out is None:
         out = torch.empty(shape, dtype=dt, device=value.device)
     _check(out, "out", dt, shape)
-    st = load_library().msda_forward(_ptr(value), _ptr(spatial_shapes), _ptr(level_start_index),
-                                     _ptr(sampling_locations), _ptr(attention_weights),
-                                     _ptr(out), ctypes.byref(dims), _DTYPES[dt], _stream(stream))
+    lib = load_library()
+    args = (_ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),
+            _ptr(attention_weights), _ptr(out), ctypes.byref(dims), _DTYPES[dt])
+    if gather == "direct":
+        st = lib.msda_forward(*args, _stream(stream))
+        if st != MSDA_OK:
+            raise MsdaError(st, "msda_forward")
+        return out
+    host = _host_shapes(spatial_shapes, spatial_shapes_host)
+    need = msda_forward_binned_workspace_bytes(dims, _DTYPES[dt], host)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=value.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.msda_forward_binned(*args, host.ctypes.data, _ptr(workspace), ws_bytes,
+                                 _stream(stream))
     if st != MSDA_OK:
-        raise MsdaError(st, "msda_forward")
+        raise MsdaError(st, "msda_forward_binned")
     return out
 
 

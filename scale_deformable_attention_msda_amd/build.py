@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libmsda.so")
-SOURCES = ["msda_api.hip", "msda_kernels.hip", "msda_binned.hip", "msda_profile.hip"]
+SOURCES = ["msda_api.hip", "msda_kernels.hip", "msda_binned.hip", "msda_fwd_binned.hip",
+           "msda_profile.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.

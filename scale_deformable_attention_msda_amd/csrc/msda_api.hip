@@ -133,6 +133,38 @@ msda_status hip_fail(hipError_t e, const char *what) {
   return fail(MSDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Plan of the query-binned forward for the largest batch chunk of a call.
+msda_status forward_binned_plan(const Checked &c, const int64_t *shapes_host,
+                                msda::FwdPlan *plan, size_t *ws) {
+  *ws = 0;
+  if (c.hq_elems == 0) return MSDA_OK;
+  if (!shapes_host) return fail(MSDA_ERR_NULL_POINTER, "the binned forward needs spatial_shapes_host");
+  const int64_t step = batches_per_launch(c);
+  const int64_t nb = c.B < step ? c.B : step;
+  if (!msda::make_fwd_plan(*plan, nb, c.Q, c.S, (int)c.M, (int)c.D, (int)c.L, (int)c.K,
+                           (int)c.elt, shapes_host))
+    return fail(MSDA_ERR_UNSUPPORTED,
+                "the binned forward does not suit these sizes (row bytes, K, queries per "
+                "region of the finest level or LDS windows)");
+  *ws = msda::fwd_workspace_bytes(*plan);
+  return MSDA_OK;
+}
+
+msda_status forward_checks(const void *value, const int64_t *spatial_shapes,
+                           const int64_t *level_start_index, const void *sampling_locations,
+                           const void *attention_weights, void *out, const msda_dims *dims,
+                           msda_dtype dtype, Checked *c) {
+  MSDA_TRY(check_dims(dims, dtype, c));
+  const bool work = c->hq_elems > 0;
+  MSDA_TRY(check_ptr(value, "value", true, 16));
+  MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
+  MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
+  MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
+  MSDA_TRY(check_ptr(attention_weights, "attention_weights", work, 16));
+  MSDA_TRY(check_ptr(out, "out", work, 16));
+  return MSDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,15 +175,9 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          msda_dtype dtype, void *stream) {
   g_last_error[0] = '\0';
   Checked c;
-  MSDA_TRY(check_dims(dims, dtype, &c));
-  const bool work = c.hq_elems > 0;
-  MSDA_TRY(check_ptr(value, "value", true, 16));
-  MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
-  MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
-  MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
-  MSDA_TRY(check_ptr(attention_weights, "attention_weights", work, 16));
-  MSDA_TRY(check_ptr(out, "out", work, 16));
-  if (!work) return MSDA_OK;
+  MSDA_TRY(forward_checks(value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, out, dims, dtype, &c));
+  if (c.hq_elems == 0) return MSDA_OK;
   const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t step = batches_per_launch(c);
@@ -162,6 +188,54 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
     a.out = static_cast<char *>(out) + b0 * c.Q * c.M * c.D * c.elt;
     hipError_t e = msda::launch_forward(a, dt, s);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
+  return MSDA_OK;
+}
+
+size_t msda_forward_binned_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                           const int64_t *spatial_shapes_host) {
+  g_last_error[0] = '\0';
+  Checked c;
+  if (check_dims(dims, dtype, &c) != MSDA_OK) return SIZE_MAX;
+  msda::FwdPlan plan;
+  size_t ws;
+  if (forward_binned_plan(c, spatial_shapes_host, &plan, &ws) != MSDA_OK) return SIZE_MAX;
+  return ws;
+}
+
+msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes,
+                                const int64_t *level_start_index, const void *sampling_locations,
+                                const void *attention_weights, void *out, const msda_dims *dims,
+                                msda_dtype dtype, const int64_t *spatial_shapes_host,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  Checked c;
+  MSDA_TRY(forward_checks(value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, out, dims, dtype, &c));
+  msda::FwdPlan plan;
+  size_t ws_need;
+  MSDA_TRY(forward_binned_plan(c, spatial_shapes_host, &plan, &ws_need));
+  if (c.hq_elems == 0) return MSDA_OK;
+  if (!workspace || workspace_bytes < ws_need)
+    return fail(MSDA_ERR_WORKSPACE, "this forward needs %zu bytes of workspace, got %zu%s",
+                ws_need, workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t step = batches_per_launch(c);
+  for (int64_t b0 = 0; b0 < c.B; b0 += step) {
+    const int64_t nb = c.B - b0 < step ? c.B - b0 : step;
+    msda::FwdArgs fa{};
+    fa.a = chunk_args(c, b0, nb, c.elt, value, spatial_shapes, level_start_index,
+                      sampling_locations, attention_weights);
+    fa.a.out = static_cast<char *>(out) + b0 * c.Q * c.M * c.D * c.elt;
+    // the plan of a smaller last chunk needs no more workspace than the first
+    if (!msda::make_fwd_plan(fa.p, nb, c.Q, c.S, (int)c.M, (int)c.D, (int)c.L, (int)c.K,
+                             (int)c.elt, spatial_shapes_host))
+      return fail(MSDA_ERR_UNSUPPORTED, "binned forward: no plan for %lld batches", (long long)nb);
+    fa.w = msda::carve_fwd_scratch(fa.p, workspace);
+    hipError_t e = msda::launch_forward_binned(fa, dt, s);
+    if (e != hipSuccess) return hip_fail(e, "binned forward launch");
   }
   return MSDA_OK;
 }

@@ -91,6 +91,57 @@ struct BinArgs {
   BinScratch w;
 };
 
+// ------------------------------------------------ query-binned forward
+//
+// The head-queries (b, q, m) of one launch are sorted by a spatial key: the
+// mean location of their points on the finest level (most pixels), cut into
+// square bins of `T` x `T` finest-level pixels.  One tile block per bin (or
+// per piece of at most `quads` head-queries of a bin) stages, level after
+// level, the window of value rows its samples can reach (the bin's extent on
+// that level plus a margin of R pixels) in LDS and gathers from there; the
+// rare sample whose cell leaves the window is read from global memory.
+constexpr int kFwdCountQ = 1024;             // queries (threads) per count / scatter block
+constexpr int kFwdMaxBinsBM = 4096;          // bins per (batch, head)
+constexpr int kFwdMaxPieces = 8;             // 16-byte staging pieces per thread and level
+constexpr int kFwdMaxSlots = 8;              // (level, point-round) slots a lane holds
+
+struct FwdPlan {
+  int64_t Q, S;
+  int nb, M, D, L, K;
+  int KR;                      // point rounds: ceil(K / 4)
+  int quads;                   // 4-lane groups per tile block (one head-query each): 128 or 256
+  int f;                       // finest level
+  int T, GX, GY, nbm;          // bin edge (finest-level pixels), bins per row and column, per (b, m)
+  int nqb;                     // scatter blocks per (b, m) (kFwdCountQ queries each)
+  int cq, nqc;                 // queries per count block (all heads; a power of two that
+                               // divides kFwdCountQ) and count blocks per batch
+  int max_chunks;              // chunk-list capacity
+  int H[kMaxLevels], W[kMaxLevels], start[kMaxLevels];
+  float sx[kMaxLevels], sy[kMaxLevels];  // bin edge in pixels of level l
+  int R[kMaxLevels];                     // window margin on level l (its pixels)
+  int ww[kMaxLevels], wh[kMaxLevels];    // window width and height (pixels of level l)
+  FastDiv div_ww[kMaxLevels];
+  int order[kMaxLevels];       // levels in processing order (smallest window first)
+  int half;                    // LDS byte offset of the second window buffer; phase
+                               // (chunk, level position i) uses buffer (i + parity) % 2,
+                               // the parity flipping after each chunk when L is odd
+  int lds_bytes;               // both window buffers
+};
+
+struct FwdScratch {
+  uint32_t *keys;     // [nb*M][Q] bin of each head-query
+  uint32_t *hist;     // [nb*M][nqc][nbm] per-count-block bin counts
+  uint32_t *sorted;   // [nb*M][Q] query index, sorted by bin within each (b, m)
+  uint32_t *nchunks;  // [1] chunks in the list
+  uint4 *chunks;      // [max_chunks] (b*M + m, first sorted position, bin, count)
+};
+
+struct FwdArgs {
+  LaunchArgs a;
+  FwdPlan p;
+  FwdScratch w;
+};
+
 // Kernel timing hooks (no-ops unless a profiling session is open on this
 // thread): every launch site calls prof_begin() before and prof_end() after
 // enqueueing its kernel.
@@ -112,6 +163,14 @@ bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, in
 size_t binned_workspace_bytes(const BinPlan &p);
 BinScratch carve_bin_scratch(const BinPlan &p, void *workspace);
 hipError_t launch_backward_binned(const BinArgs &a, Dtype dt, hipStream_t stream);
+// Query-binned forward: plan from host-side level shapes for a launch of
+// `nb` batches (false when the sizes do not suit it: the caller then runs
+// the direct gather), size and carve the workspace, enqueue the passes.
+bool make_fwd_plan(FwdPlan &p, int64_t nb, int64_t Q, int64_t S, int M, int D, int L, int K,
+                   int elt, const int64_t *shapes_host);
+size_t fwd_workspace_bytes(const FwdPlan &p);
+FwdScratch carve_fwd_scratch(const FwdPlan &p, void *workspace);
+hipError_t launch_forward_binned(const FwdArgs &a, Dtype dt, hipStream_t stream);
 hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, size_t n, hipStream_t stream);
 
 }  // namespace msda

@@ -43,9 +43,10 @@ def operands(t: dict):
             t["attention_weights"])
 
 
-def run_gpu(x: dict, accum=None, stream=None, scatter="binned") -> dict:
+def run_gpu(x: dict, accum=None, stream=None, scatter="binned", gather="direct") -> dict:
     t = upload(x)
-    out = msda.msda_forward(*operands(t), stream=stream)
+    out = msda.msda_forward(*operands(t), stream=stream, gather=gather,
+                            spatial_shapes_host=x["spatial_shapes"])
     gv, gl, ga = msda.msda_backward(*operands(t), t["grad_out"], accum_dtype=accum, stream=stream,
                                     scatter=scatter, spatial_shapes_host=x["spatial_shapes"])
     torch.cuda.synchronize()

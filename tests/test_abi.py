@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("msda_forward", "msda_backward", "msda_backward_workspace_bytes",
+    for n in ("msda_forward", "msda_forward_binned", "msda_forward_binned_workspace_bytes",
+              "msda_backward", "msda_backward_workspace_bytes",
               "msda_status_string", "msda_last_error"):
         assert n in names
 
@@ -57,7 +58,19 @@ def fwd(lib, d, dtype=0, value=FAKE, shapes=FAKE, starts=FAKE, loc=FAKE, attn=FA
                             None if d is None else ctypes.byref(d), dtype, None)
 
 
+def fwd_binned(lib, d, dtype=0, shapes_host=None, ws=None, ws_bytes=0):
+    return lib.msda_forward_binned(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), dtype,
+                                   shapes_host, ws, ws_bytes, None)
+
+
 SHAPES = (ctypes.c_int64 * 4)(8, 8, 4, 4)  # host copy of [[8, 8], [4, 4]]
+PYRAMID = (ctypes.c_int64 * 8)(100, 167, 50, 84, 25, 42, 13, 21)  # the 4-level encoder pyramid
+ENCODER = dict(B=2, S=22223, M=8, D=32, L=4, Q=22223, K=4)
+SIZE_MAX = 2 ** 64 - 1
+
+
+def fwd_ws(lib, d, dtype=0, shapes_host=None):
+    return lib.msda_forward_binned_workspace_bytes(ctypes.byref(d), dtype, shapes_host)
 
 
 def bwd(lib, d, dtype=0, acc=0, scatter=1, shapes_host=None, ws=None, ws_bytes=0, **p):
@@ -70,6 +83,31 @@ def bwd(lib, d, dtype=0, acc=0, scatter=1, shapes_host=None, ws=None, ws_bytes=0
 
 def ws_bytes(lib, d, dtype=0, acc=0, scatter=0, shapes_host=None):
     return lib.msda_backward_workspace_bytes(ctypes.byref(d), dtype, acc, scatter, shapes_host)
+
+
+def test_binned_forward_workspace_sizes(lib):
+    # one query per pyramid pixel: the binned gather plans it and needs a sort buffer
+    need = fwd_ws(lib, dims(**ENCODER), 0, PYRAMID)
+    assert 8 * 2 * 8 * 22223 <= need < 64 << 20
+    assert fwd_ws(lib, dims(**ENCODER), 1, PYRAMID) > 0                       # bf16, 64-byte rows
+    assert fwd_ws(lib, dims(**ENCODER), 0, None) == SIZE_MAX                  # needs host shapes
+    assert "spatial_shapes_host" in msda.msda_last_error()
+    for bad in (dict(Q=300), dict(D=8), dict(K=9)):  # few queries, 32-byte rows, K > 8
+        assert fwd_ws(lib, dims(**dict(ENCODER, **bad)), 0, PYRAMID) == SIZE_MAX
+        assert "binned forward" in msda.msda_last_error()
+    assert fwd_ws(lib, dims(D=12), 0, SHAPES) == SIZE_MAX
+
+
+def test_binned_forward_rejections(lib):
+    d = dims(**ENCODER)
+    need = fwd_ws(lib, d, 0, PYRAMID)
+    assert fwd_binned(lib, d, shapes_host=PYRAMID) == 5
+    assert "workspace" in msda.msda_last_error()
+    assert fwd_binned(lib, d, shapes_host=PYRAMID, ws=FAKE, ws_bytes=need - 1) == 5
+    assert fwd_binned(lib, d, shapes_host=PYRAMID, ws=FAKE + 4, ws_bytes=need) == 4
+    assert fwd_binned(lib, d, shapes_host=None, ws=FAKE, ws_bytes=need) == 1
+    assert fwd_binned(lib, dims(**dict(ENCODER, Q=300)), shapes_host=PYRAMID, ws=FAKE,
+                      ws_bytes=need) == 3
 
 
 @pytest.mark.parametrize("kwargs,code", [

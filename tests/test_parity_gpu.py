@@ -176,6 +176,101 @@ def test_outputs_are_overwritten_and_deterministic(dtype, scatter):
              dict(out=out1, grad_value=gv1, grad_loc=gl1, grad_attn=ga1).items()}, o)
 
 
+def uses_binned_forward(x) -> bool:
+    wl = x["workload"]
+    d = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
+    dt = msda.MSDA_FP32 if x["dtype"] == "fp32" else msda.MSDA_BF16
+    try:
+        return msda.msda_forward_binned_workspace_bytes(d, dt, x["spatial_shapes"]) > 0
+    except ValueError:
+        return False
+
+
+def forward_only(x, gather):
+    t = parity.upload(x)
+    out = msda.msda_forward(*parity.operands(t), gather=gather,
+                            spatial_shapes_host=x["spatial_shapes"])
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_forward(x):
+    import oracle
+    return oracle.forward(x["value"], x["spatial_shapes"], x["level_start_index"],
+                          x["sampling_locations"], x["attention_weights"])
+
+
+def gate_forward(x, out, want):
+    tol = TOL_FWD_FP32 if x["dtype"] == "fp32" else TOL_BF16
+    check("out", out.double().cpu().numpy(), want, *tol)
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_workload_forward_both_gathers(wid):
+    wl = workloads.WORKLOADS[wid]
+    say(f"[parity] forward, both gathers: workload {wid} {wl.name}")
+    x, o = workload_case(wid)
+    assert uses_binned_forward(x), "the query-binned forward should plan this workload"
+    for gather in ("binned", "direct"):
+        say(f"  gather={gather}")
+        gate_forward(x, forward_only(x, gather), o["out"])
+
+
+# Pyramids with one query per pixel: small enough for the oracle, large enough
+# that the query-binned forward plans them (several bins, chunks, windows).
+SMALL_PYR = ((20, 30), (10, 15), (5, 8))
+SMALL_S = 20 * 30 + 10 * 15 + 5 * 8
+SIX_LEVELS = ((24, 32), (12, 16), (6, 8), (3, 4), (2, 2), (1, 1))
+BINNED_FWD = {
+    "enc_fp32": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, ref="pixel_centres"),
+    "enc_bf16": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, dtype="bf16", ref="pixel_centres"),
+    "enc_wide_offsets": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, ref="pixel_centres",
+                                         sigma_px=7.0),
+    "enc_k8": workloads.custom(1, SMALL_S, 4, 32, SMALL_PYR, 8, ref="pixel_centres"),
+    "enc_k3": workloads.custom(1, SMALL_S, 3, 32, SMALL_PYR, 3, ref="pixel_centres"),
+    "enc_six_levels": workloads.custom(1, 1025, 2, 32, SIX_LEVELS, 4, ref="pixel_centres"),
+    "enc_d16_fp32": workloads.custom(2, SMALL_S, 4, 16, SMALL_PYR, 4, ref="pixel_centres"),
+    "enc_d64_fp32": workloads.custom(2, SMALL_S, 4, 64, SMALL_PYR, 4, ref="pixel_centres"),
+    "enc_d64_bf16": workloads.custom(2, SMALL_S, 4, 64, SMALL_PYR, 4, dtype="bf16",
+                                     ref="pixel_centres"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BINNED_FWD))
+def test_binned_forward(name):
+    wl = BINNED_FWD[name]
+    say(f"[parity] binned forward {name}: B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
+        f"L={wl.L} K={wl.K} {wl.dtype} sigma={wl.sigma_px}")
+    x = workloads.make_inputs(wl, seed=zlib.crc32(name.encode()) % 100000, with_grad=False)
+    assert uses_binned_forward(x)
+    want = oracle_forward(x)
+    out1 = forward_only(x, "binned")
+    gate_forward(x, out1, want)
+    out2 = forward_only(x, "binned")
+    assert torch.equal(out1, out2), "forward must be bit-identical across runs"
+    gate_forward(x, forward_only(x, "direct"), want)
+
+
+def test_binned_forward_clustered_and_nonfinite():
+    """All points near one spot (bins far above 256 head-queries, cut into chunks),
+    plus boundary and non-finite coordinates."""
+    say("[parity] binned forward: clustered locations, boundary and non-finite points")
+    wl = BINNED_FWD["enc_fp32"]
+    x = workloads.make_inputs(wl, seed=5, with_grad=False)
+    rng = np.random.default_rng(5)
+    loc = x["sampling_locations"]
+    loc[...] = (0.5 + 0.01 * rng.standard_normal(loc.shape)).astype(np.float32)
+    special = [(math.nan, 0.5), (0.5, math.inf), (-0.5 / 30, 0.5), (1.0, 1.0), (0.0, 0.0),
+               (1e30, -1e30), (-math.inf, math.nan)]
+    for i, (u, v) in enumerate(special):
+        loc[i % 2, 7 * i, i % 4, 0, i % 4, :] = (u, v)
+    assert uses_binned_forward(x)
+    want = oracle_forward(x)
+    out = forward_only(x, "binned")
+    assert torch.isfinite(out).all()
+    gate_forward(x, out, want)
+
+
 def test_side_stream():
     say("[parity] non-default stream")
     x = workloads.make_inputs(1)
