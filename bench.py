@@ -147,6 +147,37 @@ def cpu_baseline(x: dict, budget_s: float = 10.0) -> dict:
                       f"(host: {cpu}, {os.cpu_count()} logical CPUs, {platform.machine()})"}
 
 
+def cpu_baseline_single_thread(workload_id: int, seed: int, budget_s: float = 30.0) -> dict | None:
+    """The oracle on one host thread, in a child process (OMP_NUM_THREADS=1), on
+    the same seeded inputs; None if the child fails or runs over its budget."""
+    import subprocess
+
+    code = (
+        "import sys, time, json\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "import workloads, oracle\n"
+        f"x = workloads.make_inputs({workload_id}, seed={seed})\n"
+        "a = (x['value'], x['spatial_shapes'], x['level_start_index'], x['sampling_locations'],"
+        " x['attention_weights'])\n"
+        "o = oracle.default()\n"
+        "t0 = time.perf_counter(); o.forward(*a); o.backward(*a, x['grad_out'])\n"
+        "print(json.dumps({'s': time.perf_counter() - t0, 'threads': o.threads()}))\n")
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=budget_s)
+        j = json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception:  # noqa: BLE001 - a missing figure is reported as null
+        return None
+    return {"value": round(j["s"] * 1e6, 1), "unit": "us/call", "cores": j["threads"]}
+
+
+def percentiles(xs) -> dict:
+    a = np.sort(np.asarray(xs, dtype=np.float64))
+    return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.percentile(a, 50)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +190,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gather", default="direct", choices=["direct", "binned"],
                     help="forward schedule: msda_forward (direct gather) or msda_forward_binned")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the warm / cold regimes and the bandwidth microbenchmarks")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_encoder.txt"),
                     help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -238,12 +271,66 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     # timed region: K steps, every library kernel bracketed by HIP events on `stream`
     msda.msda_profile_start(64 * args.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     w0 = time.perf_counter()
+    ev[0].record(stream)
     for i in range(args.steps):
         step(i)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     records = msda.msda_profile_stop(64 * args.steps)
+    step_us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)]
+
+    def timed_steps(n, batch_of, before=None):
+        """Per-step microseconds of n steps (events around each step only)."""
+        out_us = []
+        for i in range(n):
+            if before is not None:
+                before()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(batch_of(i))
+            e1.record(stream)
+            e1.synchronize()
+            out_us.append(e0.elapsed_time(e1) * 1e3)
+        return out_us
+
+    extras = {}
+    if not args.no_extras:
+        # regimes: warm = one input batch back to back (L2 / MALL resident);
+        # cold = a 1 GiB buffer rewritten before every step (not timed), which
+        # evicts the 8 x 4 MB L2 and the 256 MB MALL
+        scratch = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
+        warm = timed_steps(20, lambda i: 0)
+        cold = timed_steps(20, lambda i: 0, before=lambda: scratch.fill_(1.0))
+        extras["regimes"] = {"rotate": dict(percentiles(step_us), steps=args.steps,
+                                            batches=args.rotate),
+                             "warm": dict(percentiles(warm), steps=20),
+                             "cold": dict(percentiles(cold), steps=20)}
+        # achievable HBM rates on this box: a streaming read (sum of 1 GiB) and a copy
+        src = torch.randn(2 ** 28, device=dev)
+        dst = torch.empty_like(src)
+
+        def rate(fn, nbytes):
+            ts = []
+            for _ in range(6):
+                scratch.fill_(0.0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            return nbytes / float(np.median(ts[1:])) / 1e9
+
+        rows = src.view(2 ** 17, -1)
+        extras["achievable"] = {"read_gbps": round(rate(lambda: rows.sum(1), src.numel() * 4), 1),
+                                "copy_gbps": round(rate(lambda: dst.copy_(src), src.numel() * 8), 1),
+                                "how": "torch row sums of 1 GiB fp32 in 131072 rows (read; the "
+                                       "fastest torch reduction shape measured) and a copy of 1 GiB "
+                                       "(read + write), L2/MALL evicted before each, median of 5"}
+        del scratch, src, dst
 
     bm = bytes_model(wl, args.scatter)
     per_kernel = {}
@@ -294,9 +381,16 @@ def main(argv=None) -> int:
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
+    res.update(extras)
+    if "achievable" in extras:
+        res["fwd_frac_of_read"] = round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 /
+                                        extras["achievable"]["read_gbps"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         res["cpu_baseline"] = cpu_baseline(host[0])
+        one = cpu_baseline_single_thread(args.workload, workloads.BASE_SEED + args.workload)
+        if one is not None:
+            res["cpu_baseline"]["single_thread"] = one
     print(json.dumps(res), flush=True)
     return 0
 
