@@ -77,6 +77,10 @@ class Oracle:
         lib.msda_oracle_backward.restype = None
         lib.msda_oracle_threads.argtypes = []
         lib.msda_oracle_threads.restype = ctypes.c_int
+        lib.msda_oracle_softmax.argtypes = [_f64p, _f64p, _i64, _i64]
+        lib.msda_oracle_softmax.restype = None
+        lib.msda_oracle_softmax_backward.argtypes = [_f64p, _f64p, _f64p, _i64, _i64]
+        lib.msda_oracle_softmax_backward.restype = None
         self._lib = lib
 
     def threads(self) -> int:
@@ -117,6 +121,43 @@ class Oracle:
         return grad_value, grad_loc, grad_attn
 
 
+    def softmax(self, logits):
+        """Attention weights from raw logits [B,Q,M,L,K]: softmax over the L*K
+        points of every (b, q, m) ("softmax" method), fp64."""
+        z = _f64(logits)
+        if z.ndim != 5:
+            raise ValueError("logits must be [B, Q, M, L, K]")
+        a = np.empty_like(z)
+        lk = z.shape[3] * z.shape[4]
+        self._lib.msda_oracle_softmax(_ptr(z, _f64p), _ptr(a, _f64p), z.size // lk, lk)
+        return a
+
+    def softmax_backward(self, weights, grad_weights):
+        """grad_logits from the softmax's weights and dLoss/dweights, fp64."""
+        a, ga = _f64(weights), _f64(grad_weights)
+        if a.shape != ga.shape or a.ndim != 5:
+            raise ValueError("weights and grad_weights must both be [B, Q, M, L, K]")
+        out = np.empty_like(a)
+        lk = a.shape[3] * a.shape[4]
+        self._lib.msda_oracle_softmax_backward(_ptr(a, _f64p), _ptr(ga, _f64p),
+                                               _ptr(out, _f64p), a.size // lk, lk)
+        return out
+
+    def forward_softmax(self, value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_logits):
+        """The forward with weights = softmax(attention_logits)."""
+        return self.forward(value, spatial_shapes, level_start_index, sampling_locations,
+                            self.softmax(attention_logits))
+
+    def backward_softmax(self, value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_logits, grad_out):
+        """(grad_value, grad_loc, grad_logits) of the forward with softmax weights."""
+        a = self.softmax(attention_logits)
+        gv, gl, ga = self.backward(value, spatial_shapes, level_start_index, sampling_locations,
+                                   a, grad_out)
+        return gv, gl, self.softmax_backward(a, ga)
+
+
 _default = None
 
 
@@ -136,3 +177,11 @@ def forward(*args):
 
 def backward(*args):
     return default().backward(*args)
+
+
+def forward_softmax(*args):
+    return default().forward_softmax(*args)
+
+
+def backward_softmax(*args):
+    return default().backward_softmax(*args)

@@ -22,8 +22,11 @@
  *   - section "The simplest possible implementation": the six nested loops,
  *     the use of floor, the per-corner bounds test and the row index
  *     start_l + yy*W_l + xx into the flattened pyramid.
- * The pages use the attention weights as given (DeformOps page, section
- * "Multi-scale deformable attention"); nothing here normalises them.
+ * The pages use the attention weights as given by default (DeformOps page,
+ * section "Multi-scale deformable attention"); the same section names a
+ * second method, "softmax", that normalises raw logits jointly over levels
+ * and points.  That normalisation and its derivative are the two functions at
+ * the end of this file; the operator itself never normalises.
  *
  * The gradients are not printed on the pages (the course's backward chapter
  * is not among them).  They are derived here by differentiating the forward
@@ -214,5 +217,51 @@ void msda_oracle_backward(const double *value, const int64_t *spatial_shapes,
                 }
             }
         }
+    }
+}
+
+/*
+ * The "softmax" method of the DeformOps page (section "Multi-scale deformable
+ * attention"): the L*K raw logits z of every head-query (b, q, m) become the
+ * attention weights
+ *     A_j = exp(z_j - max_i z_i) / sum_i exp(z_i - max_i z_i)
+ * (the usual softmax; subtracting the maximum changes nothing but the range).
+ * logits and weights are [n_hq][lk], contiguous.
+ */
+void msda_oracle_softmax(const double *logits, double *weights, int64_t n_hq, int64_t lk) {
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < n_hq; ++h) {
+        const double *z = logits + h * lk;
+        double *a = weights + h * lk;
+        double mx = z[0];
+        for (int64_t j = 1; j < lk; ++j)
+            if (z[j] > mx)
+                mx = z[j];
+        double sum = 0.0;
+        for (int64_t j = 0; j < lk; ++j) {
+            a[j] = exp(z[j] - mx);
+            sum += a[j];
+        }
+        for (int64_t j = 0; j < lk; ++j)
+            a[j] = a[j] / sum;
+    }
+}
+
+/*
+ * Derivative through that softmax.  With gA_j = dLoss/dA_j (the grad_attn of
+ * the operator) and dA_i/dz_j = A_i (delta_ij - A_j):
+ *     dLoss/dz_j = sum_i gA_i A_i (delta_ij - A_j) = A_j (gA_j - sum_i A_i gA_i).
+ */
+void msda_oracle_softmax_backward(const double *weights, const double *grad_weights,
+                                  double *grad_logits, int64_t n_hq, int64_t lk) {
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < n_hq; ++h) {
+        const double *a = weights + h * lk;
+        const double *ga = grad_weights + h * lk;
+        double dot = 0.0;
+        for (int64_t i = 0; i < lk; ++i)
+            dot += a[i] * ga[i];
+        for (int64_t j = 0; j < lk; ++j)
+            grad_logits[h * lk + j] = a[j] * (ga[j] - dot);
     }
 }

@@ -23,7 +23,10 @@ Independent formulations used here (none of them calls the oracle's code):
   * finite differences, which are exact up to rounding here: the output is
     linear in the attention weights and in the value, and linear in x for a
     fixed y inside one cell;
-  * the adjoint identity <F(V), G> = <V, F^T(G)> for the linear map V -> out.
+  * the adjoint identity <F(V), G> = <V, F^T(G)> for the linear map V -> out;
+  * for the "softmax" method: torch.softmax and its autograd in fp64, the
+    invariants sum A = 1 and sum grad_logits = 0, and central differences of
+    the whole operator with a numpy softmax.
 """
 from __future__ import annotations
 
@@ -416,6 +419,57 @@ def pin_out_of_range_and_nonfinite(orc):
     assert np.all(np.isfinite(gv)) and np.all(np.isfinite(gl)) and np.all(np.isfinite(ga))
 
 
+def _softmax_np(z):
+    """Softmax over the last two axes (L, K) of z, written out in numpy for the pins."""
+    sh = z.shape
+    z2 = z.reshape(sh[:3] + (-1,))
+    e = np.exp(z2 - z2.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)).reshape(sh)
+
+
+def pin_softmax_library(orc):
+    """The "softmax" method against torch.softmax in fp64, its derivative against
+    torch autograd, the weights summing to 1, grad_logits summing to 0 per
+    head-query, and constant logits giving exactly 1 / (L K)."""
+    import torch
+
+    rng = np.random.default_rng(71)
+    z = rng.standard_normal((2, 3, 2, 3, 4)) * 3.0
+    a = orc.softmax(z)
+    zt = torch.tensor(z.reshape(2, 3, 2, 12), dtype=torch.float64, requires_grad=True)
+    at = torch.softmax(zt, dim=-1)
+    _close(a.reshape(2, 3, 2, 12), at.detach().numpy(), 1e-15, "softmax vs torch.softmax")
+    ga = rng.standard_normal(a.shape)
+    (at * torch.tensor(ga.reshape(2, 3, 2, 12))).sum().backward()
+    gz = orc.softmax_backward(a, ga)
+    _close(gz.reshape(2, 3, 2, 12), zt.grad.numpy(), 1e-14, "softmax derivative vs autograd")
+    _close(a.sum(axis=(3, 4)), np.ones((2, 3, 2)), 1e-15, "weights sum to 1")
+    _close(gz.sum(axis=(3, 4)), np.zeros((2, 3, 2)), 1e-13, "grad_logits sum to 0")
+    c = orc.softmax(np.full((1, 2, 1, 2, 3), 5.0))
+    assert np.all(c == 1.0 / 6.0), "constant logits give uniform weights"
+
+
+def pin_softmax_composition(orc):
+    """grad_logits of the operator with softmax weights against central
+    differences of the tent-sum forward with a numpy softmax."""
+    p = random_problem(81, B=1, Q=2, M=2, D=3, shapes=((4, 5), (2, 3)), K=2)
+    ops = list(operands(p))[:4]
+    g = p["grad_out"]
+    z = np.random.default_rng(82).standard_normal(p["attention_weights"].shape)
+    out = orc.forward_softmax(*ops, z)
+    _close(out, tent_forward(*ops, _softmax_np(z)), 1e-12, "forward with softmax weights")
+    _, _, gz = orc.backward_softmax(*ops, z, g)
+    fd = np.empty_like(z)
+    h = 1e-5
+    for idx in np.ndindex(z.shape):
+        zp, zm = z.copy(), z.copy()
+        zp[idx] += h
+        zm[idx] -= h
+        fd[idx] = (_loss(tent_forward, ops + [_softmax_np(zp)], g)
+                   - _loss(tent_forward, ops + [_softmax_np(zm)], g)) / (2 * h)
+    _close(gz, fd, 1e-8, "grad_logits vs central differences")
+
+
 ALL_PINS = [
     pin_forward_tent_sum,
     pin_forward_grid_sample,
@@ -428,4 +482,6 @@ ALL_PINS = [
     pin_grad_loc_right_derivative_on_edges,
     pin_autograd_grid_sample,
     pin_out_of_range_and_nonfinite,
+    pin_softmax_library,
+    pin_softmax_composition,
 ]

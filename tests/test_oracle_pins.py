@@ -58,6 +58,10 @@ MUTANTS = [
     ("grad_value not zeroed", "memset(grad_value, 0, (size_t)(B * S * M * D) * sizeof(double));",
      "grad_value[0] += 0.0;"),
     ("empty-sample gradient not cleared", "grad_loc[2 * s] = 0.0;\n", "grad_loc[2 * s] = 1.0;\n"),
+    ("softmax not normalised", "a[j] = a[j] / sum;", "a[j] = a[j] / (sum + 1e-3);"),
+    ("softmax sum drops the last term", "sum += a[j];", "sum += (j + 1 < lk) ? a[j] : 0.0;"),
+    ("softmax derivative sign", "a[j] * (ga[j] - dot)", "a[j] * (ga[j] + dot)"),
+    ("softmax derivative drops the weights in the sum", "dot += a[i] * ga[i];", "dot += ga[i];"),
 ]
 
 

@@ -30,7 +30,9 @@ this order:
   3. offsets ~ N(0, sigma px) per (b, q, m, l, k, axis), divided by W_l for x
      and by H_l for y, added to the reference point;
   4. logits ~ N(0, 1), shape (B, Q, M, L*K); weights = fp64 softmax over the
-     L*K axis, then rounded to the workload's dtype;
+     L*K axis, then rounded to the workload's dtype; the logits themselves
+     (less their per-row maximum) are kept as attention_logits for the
+     "softmax" method;
   5. grad_out ~ N(0, 1), shape (B, Q, M*D).
 For bf16 workloads every floating array is rounded to bf16 (round to nearest
 even) and returned as float32 holding bf16-exact values, so that both the GPU
@@ -152,6 +154,9 @@ def make_inputs(wl: Workload | int, seed: int | None = None, with_grad: bool = T
         "value": value,
         "sampling_locations": loc.astype(np.float32),
         "attention_weights": weights.astype(np.float32),
+        # the same logits, raw, for the "softmax" method (weights normalised
+        # inside the operator); drawn above, so nothing else changes
+        "attention_logits": logits.reshape(B, Q, M, L, K).astype(np.float32),
     }
     if grad_out is not None:
         arrays["grad_out"] = grad_out
