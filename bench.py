@@ -9,7 +9,8 @@ softmax weights; synthetic, seeded (workloads.py).
 A step is one msda_forward (direct gather; `--gather binned` times
 msda_forward_binned instead) plus one msda_backward (grad_value, grad_sampling_locations, grad_attention_weights;
 destination-binned by default) over one batch of inputs that is already
-resident in HBM.  `--rotate R` cycles over R independently generated
+resident in HBM.  `--method softmax` times the "softmax" method instead
+(msda_forward_softmax + msda_backward_softmax on raw logits).  `--rotate R` cycles over R independently generated
 input batches so that consecutive steps do not find their operands in the
 L2 / MALL caches (R=1 times the warm, cache-resident regime).
 
@@ -72,6 +73,12 @@ def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
         "fwd_count": hq * K * 2 * elt + hq * 4,
         "fwd_scatter": hq * 8,
         "fwd_tile": value + loc + attn + out + hq * 4,
+        # softmax method: the fused forward reads logits in place of weights; the
+        # backward's row passes read logits and write weights, then read logits and
+        # grad_attn and write grad_logits
+        "fwd_softmax": value + loc + attn + out,
+        "softmax_rows": 2 * attn,
+        "softmax_grad_rows": 3 * attn,
         # atomic backward: value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written
         "bwd_atomic": value + loc + attn + out + value + loc + attn,
         "zero": value if scatter == "atomic" else counters,
@@ -189,6 +196,8 @@ def main(argv=None) -> int:
                     help="how the backward forms grad_value")
     ap.add_argument("--gather", default="direct", choices=["direct", "binned"],
                     help="forward schedule: msda_forward (direct gather) or msda_forward_binned")
+    ap.add_argument("--method", default="default", choices=["default", "softmax"],
+                    help="attention weights as given, or softmax of raw logits in the operator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the warm / cold regimes and the bandwidth microbenchmarks")
@@ -220,6 +229,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}))
         return 0
+    if args.method == "softmax" and args.gather != "direct":
+        log("the softmax method runs on the direct gather only")
+        return 2
     msda.load_library()
     wl = workloads.WORKLOADS[args.workload]
     dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
@@ -232,7 +244,7 @@ def main(argv=None) -> int:
     batches = []
     for x in host:
         t = {k: torch.from_numpy(x[k]).to(dev).to(dt) for k in
-             ("value", "sampling_locations", "attention_weights", "grad_out")}
+             ("value", "sampling_locations", "attention_weights", "attention_logits", "grad_out")}
         t["spatial_shapes"] = torch.from_numpy(x["spatial_shapes"]).to(dev)
         t["level_start_index"] = torch.from_numpy(x["level_start_index"]).to(dev)
         batches.append(t)
@@ -246,10 +258,12 @@ def main(argv=None) -> int:
     sc = msda.MSDA_SCATTER_BINNED if args.scatter == "binned" else msda.MSDA_SCATTER_ATOMIC
     dcode = 0 if wl.dtype == "fp32" else 1
     need_b = msda.msda_backward_workspace_bytes(dims, dcode, msda.MSDA_FP32, sc, shapes_host)
+    need_s = msda.msda_backward_softmax_workspace_bytes(dims, dcode, msda.MSDA_FP32, sc,
+                                                        shapes_host)
     need_f = (msda.msda_forward_binned_workspace_bytes(dims, dcode, shapes_host)
               if args.gather == "binned" else 0)
     # one workspace serves both calls: they run one after the other on one stream
-    need = max(need_b, need_f)
+    need = max(need_b, need_f, need_s)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     log(f"[bench] gather={args.gather} (workspace {need_f / 2**20:.1f} MiB), "
         f"scatter={args.scatter} (workspace {need_b / 2**20:.1f} MiB)")
@@ -258,13 +272,34 @@ def main(argv=None) -> int:
         return (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"],
                 t["attention_weights"])
 
-    def step(i):
-        t = batches[i % len(batches)]
+    def ops_softmax(t):
+        return ops(t)[:4] + (t["attention_logits"],)
+
+    def fwd_plain(t):
         msda.msda_forward(*ops(t), out=out, stream=stream, gather=args.gather,
                           spatial_shapes_host=shapes_host, workspace=ws)
+
+    def bwd_plain(t):
         msda.msda_backward(*ops(t), t["grad_out"], grad_value=gv, grad_loc=gl, grad_attn=ga,
                            scatter=args.scatter, spatial_shapes_host=shapes_host,
                            workspace=ws, stream=stream)
+
+    def fwd_softmax(t):
+        msda.msda_forward_softmax(*ops_softmax(t), out=out, stream=stream)
+
+    def bwd_softmax(t):
+        msda.msda_backward_softmax(*ops_softmax(t), t["grad_out"], grad_value=gv, grad_loc=gl,
+                                   grad_logits=ga, scatter=args.scatter,
+                                   spatial_shapes_host=shapes_host, workspace=ws, stream=stream)
+
+    def step(i):
+        t = batches[i % len(batches)]
+        if args.method == "softmax":
+            fwd_softmax(t)
+            bwd_softmax(t)
+        else:
+            fwd_plain(t)
+            bwd_plain(t)
 
     for i in range(args.warmup):
         step(i)
@@ -332,6 +367,37 @@ def main(argv=None) -> int:
                                        "(read + write), L2/MALL evicted before each, median of 5"}
         del scratch, src, dst
 
+        # the softmax method, fused against unfused: each call alone, over the rotated batches
+        def call_us(fn, n=20):
+            ts = []
+            for i in range(n):
+                t = batches[i % len(batches)]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn(t)
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            return round(float(np.median(ts)), 2)
+
+        LK = wl.L * wl.K
+
+        def fwd_unfused(t):
+            z = t["attention_logits"]
+            a = torch.softmax(z.view(-1, LK), dim=-1).view(z.shape)
+            msda.msda_forward(*ops(t)[:4], a, out=out, stream=stream)
+
+        if args.gather == "direct":
+            extras["softmax_method"] = {
+                "fwd_fused_us": call_us(fwd_softmax),
+                "fwd_unfused_us": call_us(fwd_unfused),
+                "fwd_plain_us": call_us(fwd_plain),
+                "bwd_softmax_us": call_us(bwd_softmax),
+                "bwd_plain_us": call_us(bwd_plain),
+                "how": "median of 20 single calls over the rotated batches; unfused = "
+                       "torch.softmax over the L*K logits, then msda_forward; plain = "
+                       "msda_forward / msda_backward on given weights"}
+
     bm = bytes_model(wl, args.scatter)
     per_kernel = {}
     for name, ms in records:
@@ -369,7 +435,8 @@ def main(argv=None) -> int:
         "config": {"workload": f"{wl.name}: B={wl.B} Q=S={wl.num_queries} M={wl.M} D={wl.D} "
                                f"L={wl.L} (" + ", ".join(f"{h}x{w}" for h, w in wl.shapes) +
                                f") K={wl.K} {wl.dtype}, forward + backward",
-                   "gather": args.gather, "scatter": args.scatter, "rotate": args.rotate},
+                   "gather": args.gather, "scatter": args.scatter, "rotate": args.rotate,
+                   "method": args.method},
         "fwd_us": round(fwd_us, 3),
         "bwd_us": round(bwd_us, 3),
         "kernels": kernels,

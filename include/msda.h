@@ -16,7 +16,9 @@
  * used as given (the DeformOps page, section "Multi-scale deformable
  * attention", describes that default).  The backward returns the gradients of
  * <out, grad_out> with respect to value, sampling_locations and
- * attention_weights.
+ * attention_weights.  The *_softmax entry points implement the same page's
+ * "softmax" method: they take raw attention logits z of the same shape and
+ * use A = softmax of z over the L*K samples of each (b, q, m).
  *
  * Tensor layouts (all row-major, contiguous, on the device that runs the
  * stream):
@@ -105,6 +107,23 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          const int64_t *level_start_index, const void *sampling_locations,
                          const void *attention_weights, void *out, const msda_dims *dims,
                          msda_dtype dtype, void *stream);
+
+/*
+ * Forward of the "softmax" method (DeformOps page, section "Multi-scale
+ * deformable attention"): as msda_forward with
+ *   A[b,q,m,l,k] = exp(z[b,q,m,l,k] - max) / sum_{l',k'} exp(z[b,q,m,l',k'] - max)
+ * where z = attention_logits ([B, Q, M, L, K], dtype `dtype`) and max is the
+ * largest of the L*K logits of (b, q, m).  The normalisation is fused: each
+ * block stages its head-queries' logits in LDS and forms A there (fp32), so
+ * the call reads the logits once and writes nothing but `out`.  A NaN logit,
+ * or a +Inf one, makes every weight of its head-query NaN (as exp(z - max)
+ * does in exact arithmetic); all logits -Inf likewise.  Deterministic; no
+ * workspace.  Errors as for msda_forward.
+ */
+msda_status msda_forward_softmax(const void *value, const int64_t *spatial_shapes,
+                                 const int64_t *level_start_index, const void *sampling_locations,
+                                 const void *attention_logits, void *out, const msda_dims *dims,
+                                 msda_dtype dtype, void *stream);
 
 /*
  * Bytes of device workspace msda_forward_binned needs for these sizes and
@@ -200,6 +219,41 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           msda_dtype dtype, msda_dtype accum_dtype, msda_scatter scatter,
                           const int64_t *spatial_shapes_host, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace msda_backward_softmax needs: the weights image
+ * (B*Q*M*L*K elements of `dtype`, rounded up to 256 bytes) followed by what
+ * msda_backward_workspace_bytes() reports for the same arguments; 0 when
+ * B*Q = 0.  SIZE_MAX when the call would be rejected.
+ */
+size_t msda_backward_softmax_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                             msda_dtype accum_dtype, msda_scatter scatter,
+                                             const int64_t *spatial_shapes_host);
+
+/*
+ * Backward of the "softmax" method (DeformOps page, section "Multi-scale
+ * deformable attention"): the gradients of <out, grad_out> for the forward of
+ * msda_forward_softmax, with respect to value, sampling_locations and the
+ * logits.  With gA = d<out, grad_out>/dA (msda_backward's grad_attn for
+ * A = softmax(z)):
+ *   grad_logits[b,q,m,j] = A_j * (gA_j - sum_i A_i gA_i)   over the L*K samples.
+ * Runs as three passes on `stream`: A = softmax(z) into the head of the
+ * workspace, msda_backward with those weights (grad_attn written into
+ * grad_logits), then an in-place pass that turns gA into grad_logits with A
+ * recomputed from z in fp32.  grad_value and grad_loc are those of
+ * msda_backward for weights A (in BF16, A is rounded to bf16 once before the
+ * scatter, and gA once before the last pass).  scatter, accum_dtype,
+ * spatial_shapes_host, limits and errors as for msda_backward; workspace must
+ * hold msda_backward_softmax_workspace_bytes() bytes (16-byte aligned).
+ */
+msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shapes,
+                                  const int64_t *level_start_index,
+                                  const void *sampling_locations, const void *attention_logits,
+                                  const void *grad_out, void *grad_value, void *grad_loc,
+                                  void *grad_logits, const msda_dims *dims, msda_dtype dtype,
+                                  msda_dtype accum_dtype, msda_scatter scatter,
+                                  const int64_t *spatial_shapes_host, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * Kernel timing for benchmarks.  Between msda_profile_start() and

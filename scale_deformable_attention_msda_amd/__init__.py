@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH):
     vp, i64p, dims_p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MsdaDims)
     lib.msda_forward.argtypes = [vp, i64p, i64p, vp, vp, vp, dims_p, ctypes.c_int, vp]
     lib.msda_forward.restype = ctypes.c_int
+    lib.msda_forward_softmax.argtypes = lib.msda_forward.argtypes
+    lib.msda_forward_softmax.restype = ctypes.c_int
     lib.msda_forward_binned.argtypes = [vp, i64p, i64p, vp, vp, vp, dims_p, ctypes.c_int, vp, vp,
                                         ctypes.c_size_t, vp]
     lib.msda_forward_binned.restype = ctypes.c_int
@@ -87,6 +89,10 @@ def load_library(path: str = LIB_PATH):
     lib.msda_backward_workspace_bytes.argtypes = [dims_p, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, vp]
     lib.msda_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.msda_backward_softmax.argtypes = lib.msda_backward.argtypes
+    lib.msda_backward_softmax.restype = ctypes.c_int
+    lib.msda_backward_softmax_workspace_bytes.argtypes = lib.msda_backward_workspace_bytes.argtypes
+    lib.msda_backward_softmax_workspace_bytes.restype = ctypes.c_size_t
     lib.msda_status_string.argtypes = [ctypes.c_int]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_last_error.argtypes = []
@@ -152,7 +158,8 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _common(value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
+def _common(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+            weights_name="attention_weights"):
     if value.dtype not in _DTYPES:
         raise ValueError(f"value dtype {value.dtype} is not float32 or bfloat16")
     dt = value.dtype
@@ -163,7 +170,7 @@ def _common(value, spatial_shapes, level_start_index, sampling_locations, attent
     B, S, M, D, L, Q, K = (dims.batch, dims.num_keys, dims.num_heads, dims.head_dim,
                            dims.num_levels, dims.num_queries, dims.num_points)
     _check(sampling_locations, "sampling_locations", dt, (B, Q, M, L, K, 2))
-    _check(attention_weights, "attention_weights", dt, (B, Q, M, L, K))
+    _check(attention_weights, weights_name, dt, (B, Q, M, L, K))
     return dims, dt
 
 
@@ -216,6 +223,24 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
     return out
 
 
+def msda_forward_softmax(value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_logits, out=None, stream=None):
+    """out[B, Q, M*D] of the "softmax" method: the weights are the softmax of
+    attention_logits over the L*K samples of each head-query, formed inside the kernel."""
+    dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations,
+                       attention_logits, "attention_logits")
+    shape = (dims.batch, dims.num_queries, dims.num_heads * dims.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=dt, device=value.device)
+    _check(out, "out", dt, shape)
+    st = load_library().msda_forward_softmax(
+        _ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),
+        _ptr(attention_logits), _ptr(out), ctypes.byref(dims), _DTYPES[dt], _stream(stream))
+    if st != MSDA_OK:
+        raise MsdaError(st, "msda_forward_softmax")
+    return out
+
+
 def _host_shapes(spatial_shapes, spatial_shapes_host):
     """A contiguous int64 host array of the level shapes (kept alive by the caller)."""
     import numpy as np
@@ -227,20 +252,69 @@ def _host_shapes(spatial_shapes, spatial_shapes_host):
     return np.ascontiguousarray(np.asarray(spatial_shapes_host, dtype=np.int64))
 
 
-def msda_backward_workspace_bytes(dims: MsdaDims, dtype: int, accum_dtype: int,
-                                  scatter: int = MSDA_SCATTER_BINNED,
-                                  spatial_shapes_host=None) -> int:
-    """Workspace bytes msda_backward needs; raises when the call would be rejected."""
+def _backward_ws_bytes(fn_name: str, dims: MsdaDims, dtype: int, accum_dtype: int, scatter: int,
+                       spatial_shapes_host) -> int:
     host = None
     if spatial_shapes_host is not None:
         import numpy as np
         host = np.ascontiguousarray(np.asarray(spatial_shapes_host, dtype=np.int64))
-    n = int(load_library().msda_backward_workspace_bytes(
+    n = int(getattr(load_library(), fn_name)(
         ctypes.byref(dims), dtype, accum_dtype, scatter,
         None if host is None else host.ctypes.data))
     if n == SIZE_MAX:
-        raise ValueError(f"msda_backward_workspace_bytes: {msda_last_error()}")
+        raise ValueError(f"{fn_name}: {msda_last_error()}")
     return n
+
+
+def msda_backward_workspace_bytes(dims: MsdaDims, dtype: int, accum_dtype: int,
+                                  scatter: int = MSDA_SCATTER_BINNED,
+                                  spatial_shapes_host=None) -> int:
+    """Workspace bytes msda_backward needs; raises when the call would be rejected."""
+    return _backward_ws_bytes("msda_backward_workspace_bytes", dims, dtype, accum_dtype, scatter,
+                              spatial_shapes_host)
+
+
+def msda_backward_softmax_workspace_bytes(dims: MsdaDims, dtype: int, accum_dtype: int,
+                                          scatter: int = MSDA_SCATTER_BINNED,
+                                          spatial_shapes_host=None) -> int:
+    """Workspace bytes msda_backward_softmax needs; raises when the call would be rejected."""
+    return _backward_ws_bytes("msda_backward_softmax_workspace_bytes", dims, dtype, accum_dtype,
+                              scatter, spatial_shapes_host)
+
+
+def _backward(fn_name, value, spatial_shapes, level_start_index, sampling_locations, weights,
+              grad_out, grad_value, grad_loc, grad_weights, accum_dtype, scatter,
+              spatial_shapes_host, workspace, stream):
+    dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations, weights,
+                       "attention_logits" if fn_name.endswith("softmax") else "attention_weights")
+    B, S, M, D, L, Q, K = (dims.batch, dims.num_keys, dims.num_heads, dims.head_dim,
+                           dims.num_levels, dims.num_queries, dims.num_points)
+    _check(grad_out, "grad_out", dt, (B, Q, M * D))
+    acc = _DTYPES[accum_dtype if accum_dtype is not None else torch.float32]
+    sc = _SCATTER[scatter]
+    host = _host_shapes(spatial_shapes, spatial_shapes_host) if sc == MSDA_SCATTER_BINNED else None
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty_like(value)
+    if grad_loc is None:
+        grad_loc = torch.empty_like(sampling_locations)
+    if grad_weights is None:
+        grad_weights = torch.empty_like(weights)
+    _check(grad_value, "grad_value", dt, value.shape)
+    _check(grad_loc, "grad_loc", dt, sampling_locations.shape)
+    _check(grad_weights, "grad of the weights", dt, weights.shape)
+    need = _backward_ws_bytes(fn_name + "_workspace_bytes", dims, _DTYPES[dt], acc, sc, host)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(load_library(), fn_name)(
+        _ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),
+        _ptr(weights), _ptr(grad_out), _ptr(grad_value), _ptr(grad_loc),
+        _ptr(grad_weights), ctypes.byref(dims), _DTYPES[dt], acc, sc,
+        None if host is None else host.ctypes.data, _ptr(workspace), ws_bytes, _stream(stream))
+    if st != MSDA_OK:
+        raise MsdaError(st, fn_name)
+    return grad_value, grad_loc, grad_weights
 
 
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
@@ -254,33 +328,18 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
     (atomic scatter of bf16 data only: packed-bf16 atomics).  spatial_shapes_host: the
     level shapes on the host (array-like [L, 2]); read from spatial_shapes when omitted.
     A workspace is allocated here when none is given."""
-    dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations,
-                       attention_weights)
-    B, S, M, D, L, Q, K = (dims.batch, dims.num_keys, dims.num_heads, dims.head_dim,
-                           dims.num_levels, dims.num_queries, dims.num_points)
-    _check(grad_out, "grad_out", dt, (B, Q, M * D))
-    acc = _DTYPES[accum_dtype if accum_dtype is not None else torch.float32]
-    sc = _SCATTER[scatter]
-    host = _host_shapes(spatial_shapes, spatial_shapes_host) if sc == MSDA_SCATTER_BINNED else None
-    dev = value.device
-    if grad_value is None:
-        grad_value = torch.empty_like(value)
-    if grad_loc is None:
-        grad_loc = torch.empty_like(sampling_locations)
-    if grad_attn is None:
-        grad_attn = torch.empty_like(attention_weights)
-    _check(grad_value, "grad_value", dt, value.shape)
-    _check(grad_loc, "grad_loc", dt, sampling_locations.shape)
-    _check(grad_attn, "grad_attn", dt, attention_weights.shape)
-    need = msda_backward_workspace_bytes(dims, _DTYPES[dt], acc, sc, host)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().msda_backward(
-        _ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),
-        _ptr(attention_weights), _ptr(grad_out), _ptr(grad_value), _ptr(grad_loc),
-        _ptr(grad_attn), ctypes.byref(dims), _DTYPES[dt], acc, sc,
-        None if host is None else host.ctypes.data, _ptr(workspace), ws_bytes, _stream(stream))
-    if st != MSDA_OK:
-        raise MsdaError(st, "msda_backward")
-    return grad_value, grad_loc, grad_attn
+    return _backward("msda_backward", value, spatial_shapes, level_start_index,
+                     sampling_locations, attention_weights, grad_out, grad_value, grad_loc,
+                     grad_attn, accum_dtype, scatter, spatial_shapes_host, workspace, stream)
+
+
+def msda_backward_softmax(value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_logits, grad_out, grad_value=None, grad_loc=None,
+                          grad_logits=None, accum_dtype=None, scatter="binned",
+                          spatial_shapes_host=None, workspace=None, stream=None):
+    """Gradients of <out, grad_out> for the "softmax" method (weights = softmax of the
+    logits over the L*K samples of each head-query) w.r.t. value, sampling_locations and
+    attention_logits.  Arguments as for msda_backward."""
+    return _backward("msda_backward_softmax", value, spatial_shapes, level_start_index,
+                     sampling_locations, attention_logits, grad_out, grad_value, grad_loc,
+                     grad_logits, accum_dtype, scatter, spatial_shapes_host, workspace, stream)

@@ -153,15 +153,42 @@ msda_status forward_binned_plan(const Checked &c, const int64_t *shapes_host,
 msda_status forward_checks(const void *value, const int64_t *spatial_shapes,
                            const int64_t *level_start_index, const void *sampling_locations,
                            const void *attention_weights, void *out, const msda_dims *dims,
-                           msda_dtype dtype, Checked *c) {
+                           msda_dtype dtype, Checked *c,
+                           const char *weights_name = "attention_weights") {
   MSDA_TRY(check_dims(dims, dtype, c));
   const bool work = c->hq_elems > 0;
   MSDA_TRY(check_ptr(value, "value", true, 16));
   MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
   MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
   MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
-  MSDA_TRY(check_ptr(attention_weights, "attention_weights", work, 16));
+  MSDA_TRY(check_ptr(attention_weights, weights_name, work, 16));
   MSDA_TRY(check_ptr(out, "out", work, 16));
+  return MSDA_OK;
+}
+
+// Direct-gather forward over batch chunks; `weights` holds attention weights,
+// or raw logits when `softmax` is set.
+msda_status forward_direct(const void *value, const int64_t *spatial_shapes,
+                           const int64_t *level_start_index, const void *sampling_locations,
+                           const void *weights, void *out, const msda_dims *dims,
+                           msda_dtype dtype, bool softmax, void *stream) {
+  g_last_error[0] = '\0';
+  Checked c;
+  MSDA_TRY(forward_checks(value, spatial_shapes, level_start_index, sampling_locations, weights,
+                          out, dims, dtype, &c,
+                          softmax ? "attention_logits" : "attention_weights"));
+  if (c.hq_elems == 0) return MSDA_OK;
+  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t step = batches_per_launch(c);
+  for (int64_t b0 = 0; b0 < c.B; b0 += step) {
+    const int64_t nb = c.B - b0 < step ? c.B - b0 : step;
+    msda::LaunchArgs a = chunk_args(c, b0, nb, c.elt, value, spatial_shapes, level_start_index,
+                                    sampling_locations, weights);
+    a.out = static_cast<char *>(out) + b0 * c.Q * c.M * c.D * c.elt;
+    hipError_t e = msda::launch_forward(a, dt, s, softmax);
+    if (e != hipSuccess) return hip_fail(e, softmax ? "softmax forward launch" : "forward launch");
+  }
   return MSDA_OK;
 }
 
@@ -173,23 +200,16 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          const int64_t *level_start_index, const void *sampling_locations,
                          const void *attention_weights, void *out, const msda_dims *dims,
                          msda_dtype dtype, void *stream) {
-  g_last_error[0] = '\0';
-  Checked c;
-  MSDA_TRY(forward_checks(value, spatial_shapes, level_start_index, sampling_locations,
-                          attention_weights, out, dims, dtype, &c));
-  if (c.hq_elems == 0) return MSDA_OK;
-  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t step = batches_per_launch(c);
-  for (int64_t b0 = 0; b0 < c.B; b0 += step) {
-    const int64_t nb = c.B - b0 < step ? c.B - b0 : step;
-    msda::LaunchArgs a = chunk_args(c, b0, nb, c.elt, value, spatial_shapes, level_start_index,
-                                    sampling_locations, attention_weights);
-    a.out = static_cast<char *>(out) + b0 * c.Q * c.M * c.D * c.elt;
-    hipError_t e = msda::launch_forward(a, dt, s);
-    if (e != hipSuccess) return hip_fail(e, "forward launch");
-  }
-  return MSDA_OK;
+  return forward_direct(value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_weights, out, dims, dtype, false, stream);
+}
+
+msda_status msda_forward_softmax(const void *value, const int64_t *spatial_shapes,
+                                 const int64_t *level_start_index, const void *sampling_locations,
+                                 const void *attention_logits, void *out, const msda_dims *dims,
+                                 msda_dtype dtype, void *stream) {
+  return forward_direct(value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_logits, out, dims, dtype, true, stream);
 }
 
 size_t msda_forward_binned_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
@@ -285,55 +305,21 @@ msda_status backward_setup(const msda_dims *dims, msda_dtype dtype, msda_dtype a
   return MSDA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
-                                     msda_dtype accum_dtype, msda_scatter scatter,
-                                     const int64_t *spatial_shapes_host) {
-  g_last_error[0] = '\0';
-  BackwardSetup su;
-  if (backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su) != MSDA_OK)
-    return SIZE_MAX;
-  return su.ws_need;
-}
-
-msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
-                          const int64_t *level_start_index, const void *sampling_locations,
-                          const void *attention_weights, const void *grad_out, void *grad_value,
-                          void *grad_loc, void *grad_attn, const msda_dims *dims,
-                          msda_dtype dtype, msda_dtype accum_dtype, msda_scatter scatter,
-                          const int64_t *spatial_shapes_host, void *workspace,
-                          size_t workspace_bytes, void *stream) {
-  g_last_error[0] = '\0';
-  BackwardSetup su;
-  MSDA_TRY(backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su));
+// Enqueue the backward of a validated call (backward_setup + pointer checks
+// done); `workspace` is the part of the caller's workspace the scatter uses.
+msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const void *value,
+                         const int64_t *spatial_shapes, const int64_t *level_start_index,
+                         const void *sampling_locations, const void *attention_weights,
+                         const void *grad_out, void *grad_value, void *grad_loc, void *grad_attn,
+                         void *workspace, hipStream_t s) {
   const Checked &c = su.c;
-  const bool work = su.work;
-  MSDA_TRY(check_ptr(value, "value", true, 16));
-  MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
-  MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
-  MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
-  MSDA_TRY(check_ptr(attention_weights, "attention_weights", work, 16));
-  MSDA_TRY(check_ptr(grad_out, "grad_out", work, 16));
-  MSDA_TRY(check_ptr(grad_value, "grad_value", c.value_elems > 0, 16));
-  MSDA_TRY(check_ptr(grad_loc, "grad_loc", work, 16));
-  MSDA_TRY(check_ptr(grad_attn, "grad_attn", work, 16));
-  if (su.ws_need > 0) {
-    if (!workspace || workspace_bytes < su.ws_need)
-      return fail(MSDA_ERR_WORKSPACE, "this backward needs %zu bytes of workspace, got %zu%s",
-                  su.ws_need, workspace_bytes, workspace ? "" : " (NULL)");
-    if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (c.value_elems == 0) return MSDA_OK;
   hipError_t e;
-  if (!work) {
+  if (!su.work) {
     e = msda::launch_zero(grad_value, (size_t)(c.value_elems * c.elt), s);
     return e == hipSuccess ? MSDA_OK : hip_fail(e, "grad_value zero-fill launch");
   }
-  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const auto dt = c.elt == 4 ? msda::Dtype::F32 : msda::Dtype::BF16;
   if (su.binned) {
     msda::BinArgs a{};
     a.value = value;
@@ -377,6 +363,122 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
     e = msda::launch_cast_f32_to_bf16(static_cast<const float *>(workspace), grad_value,
                                       (size_t)c.value_elems, s);
     if (e != hipSuccess) return hip_fail(e, "workspace cast launch");
+  }
+  return MSDA_OK;
+}
+
+msda_status backward_pointer_checks(const Checked &c, const void *value,
+                                    const int64_t *spatial_shapes,
+                                    const int64_t *level_start_index,
+                                    const void *sampling_locations, const void *weights,
+                                    const char *weights_name, const void *grad_out,
+                                    void *grad_value, void *grad_loc, void *grad_weights,
+                                    const char *grad_weights_name) {
+  const bool work = c.hq_elems > 0;
+  MSDA_TRY(check_ptr(value, "value", true, 16));
+  MSDA_TRY(check_ptr(spatial_shapes, "spatial_shapes", true, 8));
+  MSDA_TRY(check_ptr(level_start_index, "level_start_index", true, 8));
+  MSDA_TRY(check_ptr(sampling_locations, "sampling_locations", work, 16));
+  MSDA_TRY(check_ptr(weights, weights_name, work, 16));
+  MSDA_TRY(check_ptr(grad_out, "grad_out", work, 16));
+  MSDA_TRY(check_ptr(grad_value, "grad_value", c.value_elems > 0, 16));
+  MSDA_TRY(check_ptr(grad_loc, "grad_loc", work, 16));
+  MSDA_TRY(check_ptr(grad_weights, grad_weights_name, work, 16));
+  return MSDA_OK;
+}
+
+msda_status workspace_check(size_t need, void *workspace, size_t workspace_bytes,
+                            const char *what) {
+  if (need == 0) return MSDA_OK;
+  if (!workspace || workspace_bytes < need)
+    return fail(MSDA_ERR_WORKSPACE, "this %s needs %zu bytes of workspace, got %zu%s", what, need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return MSDA_OK;
+}
+
+// Bytes of the softmax backward's weights image at the head of its workspace
+// (256-byte multiple, so the scatter's part keeps its alignment).
+size_t softmax_weights_bytes(const Checked &c) {
+  return ((size_t)(c.sample_elems * c.elt) + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                     msda_dtype accum_dtype, msda_scatter scatter,
+                                     const int64_t *spatial_shapes_host) {
+  g_last_error[0] = '\0';
+  BackwardSetup su;
+  if (backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su) != MSDA_OK)
+    return SIZE_MAX;
+  return su.ws_need;
+}
+
+msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
+                          const int64_t *level_start_index, const void *sampling_locations,
+                          const void *attention_weights, const void *grad_out, void *grad_value,
+                          void *grad_loc, void *grad_attn, const msda_dims *dims,
+                          msda_dtype dtype, msda_dtype accum_dtype, msda_scatter scatter,
+                          const int64_t *spatial_shapes_host, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  BackwardSetup su;
+  MSDA_TRY(backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su));
+  MSDA_TRY(backward_pointer_checks(su.c, value, spatial_shapes, level_start_index,
+                                   sampling_locations, attention_weights, "attention_weights",
+                                   grad_out, grad_value, grad_loc, grad_attn, "grad_attn"));
+  MSDA_TRY(workspace_check(su.ws_need, workspace, workspace_bytes, "backward"));
+  return backward_run(su, accum_dtype, value, spatial_shapes, level_start_index,
+                      sampling_locations, attention_weights, grad_out, grad_value, grad_loc,
+                      grad_attn, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t msda_backward_softmax_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
+                                             msda_dtype accum_dtype, msda_scatter scatter,
+                                             const int64_t *spatial_shapes_host) {
+  g_last_error[0] = '\0';
+  BackwardSetup su;
+  if (backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su) != MSDA_OK)
+    return SIZE_MAX;
+  return su.work ? softmax_weights_bytes(su.c) + su.ws_need : 0;
+}
+
+msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shapes,
+                                  const int64_t *level_start_index,
+                                  const void *sampling_locations, const void *attention_logits,
+                                  const void *grad_out, void *grad_value, void *grad_loc,
+                                  void *grad_logits, const msda_dims *dims, msda_dtype dtype,
+                                  msda_dtype accum_dtype, msda_scatter scatter,
+                                  const int64_t *spatial_shapes_host, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  BackwardSetup su;
+  MSDA_TRY(backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su));
+  const Checked &c = su.c;
+  MSDA_TRY(backward_pointer_checks(c, value, spatial_shapes, level_start_index,
+                                   sampling_locations, attention_logits, "attention_logits",
+                                   grad_out, grad_value, grad_loc, grad_logits, "grad_logits"));
+  const size_t wbytes = su.work ? softmax_weights_bytes(c) : 0;
+  MSDA_TRY(workspace_check(wbytes + su.ws_need, workspace, workspace_bytes, "softmax backward"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const int lk = (int)(c.L * c.K);
+  void *weights = workspace;
+  if (su.work) {
+    hipError_t e = msda::launch_softmax_rows(attention_logits, weights, c.hq_elems, lk, dt, s);
+    if (e != hipSuccess) return hip_fail(e, "softmax launch");
+  }
+  void *scatter_ws = su.work ? static_cast<char *>(workspace) + wbytes : workspace;
+  MSDA_TRY(backward_run(su, accum_dtype, value, spatial_shapes, level_start_index,
+                        sampling_locations, weights, grad_out, grad_value, grad_loc, grad_logits,
+                        scatter_ws, s));
+  if (su.work) {
+    hipError_t e = msda::launch_softmax_grad_rows(attention_logits, grad_logits, c.hq_elems, lk,
+                                                  dt, s);
+    if (e != hipSuccess) return hip_fail(e, "softmax derivative launch");
   }
   return MSDA_OK;
 }

@@ -22,6 +22,13 @@
 //            hardware turns into zeros (loads) or no-ops (atomics).
 // The operator is a data-dependent gather / scatter with one FMA per loaded
 // element: it is memory-bound, so there is no MFMA here.
+//
+// "softmax" method (DeformOps documentation, section "Multi-scale deformable
+// attention"): the weights of one head-query are the softmax of its L*K raw
+// logits taken jointly over levels and points.  The forward kernel forms them
+// on chip (phase 0 below) from the logits it reads in place of the weights;
+// the backward uses the two row passes at the end of this file around the
+// regular backward.
 #include "msda_device.h"
 #include "msda_launch.h"
 
@@ -75,7 +82,9 @@ __device__ inline void stage_levels(Level *lv, const LaunchArgs &a) {
 
 // ------------------------------------------------------------------ forward
 
-template <typename T, int D>
+// SOFTMAX: a.attn holds raw logits; the weight of sample j of head-query h is
+// exp(z_j - max_h) / sum_i exp(z_i - max_h) over the L*K samples of h.
+template <typename T, int D, bool SOFTMAX>
 __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   using RL = RowLayout<T, D>;
   constexpr int G = RL::G;
@@ -91,6 +100,31 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   if (hq0 >= total_hq) return;
   const int nhq = (int)min((int64_t)hqb, total_hq - hq0);
   stage_levels(lv, a);
+
+  // phase 0 (softmax): the block's logits, [hqb][L*K + 1] in LDS, become
+  // exp(z - max) in place, with 1 / sum per head-query beside them
+  float *zb = reinterpret_cast<float *>(geo + LK * gs_stride);
+  float *inv = zb + hqb * (LK + 1);
+  if constexpr (SOFTMAX) {
+    const int zs = LK + 1;
+    for (int s = threadIdx.x; s < nhq * LK; s += blockDim.x) {
+      const int hl = s / LK;
+      zb[hl * zs + s - hl * LK] = ld<T>(a.attn, hq0 * LK + s);
+    }
+    __syncthreads();
+    for (int hl = threadIdx.x; hl < nhq; hl += blockDim.x) {
+      float *z = zb + hl * zs;
+      float mx = z[0];
+      for (int j = 1; j < LK; ++j) mx = z[j] > mx ? z[j] : mx;
+      float sum = 0.0f;
+      for (int j = 0; j < LK; ++j) {
+        const float e = expf(z[j] - mx);
+        z[j] = e;
+        sum += e;
+      }
+      inv[hl] = 1.0f / sum;
+    }
+  }
   __syncthreads();
 
   // phase 1: geometry, one lane per sample
@@ -103,7 +137,7 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
     const int m = (int)(hq % M);
     const int64_t b = hq / M / a.Q;
     const float u = ld<T>(a.loc, 2 * gs), v = ld<T>(a.loc, 2 * gs + 1);
-    const float w = ld<T>(a.attn, gs);
+    const float w = SOFTMAX ? zb[hl * (LK + 1) + j] * inv[hl] : ld<T>(a.attn, gs);
     Corners cs;
     float lx, ly;
     sample_corners(u, v, lv[j / K], (uint32_t)(b * a.S), row_stride,
@@ -303,6 +337,194 @@ __global__ __launch_bounds__(256) void cast_kernel(const float4 *src, uint4 *dst
   }
 }
 
+// Softmax row passes of the backward.  A row is the L*K logits of one
+// head-query.  A block of 256 lanes owns `rows` consecutive rows at a time
+// (one contiguous range of the tensor): it stages them in LDS with 16-byte
+// loads, one lane then works through one row, and the results leave with
+// 16-byte stores.  LDS rows are `zs` = L*K | 1 floats apart: an odd stride
+// puts the per-row reads of the 64 lanes of a wave on distinct banks.
+constexpr int kRowThreads = 256;
+
+struct RowPass {
+  int64_t n_rows;
+  int lk, zs, rows;  // rows per pass: a multiple of 64, at most 256
+  FastDiv div_lk;
+};
+
+template <typename T>
+struct Vec16 {
+  static constexpr int N = 16 / (int)sizeof(T);
+};
+
+template <typename T>
+__device__ inline void unpack16(const uint4 &w, float (&f)[Vec16<T>::N]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+
+template <typename T>
+__device__ inline uint4 pack16(const float (&f)[Vec16<T>::N]) {
+  uint32_t u[4];
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(f[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = bf16_bits_rne(f[2 * i]) | (bf16_bits_rne(f[2 * i + 1]) << 16);
+  }
+  return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
+// n elements of src (16-byte aligned) -> LDS rows of stride zs
+template <typename T>
+__device__ inline void stage_rows(const T *src, float *lds, int n, const RowPass &p) {
+  constexpr int V = Vec16<T>::N;
+  const int nv = n / V;
+  for (int v = threadIdx.x; v < nv; v += kRowThreads) {
+    float f[V];
+    unpack16<T>(*reinterpret_cast<const uint4 *>(src + (int64_t)v * V), f);
+    uint32_t r = fdiv((uint32_t)(v * V), p.div_lk);
+    int c = v * V - (int)r * p.lk;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      lds[r * p.zs + c] = f[e];
+      if (++c == p.lk) {
+        c = 0;
+        ++r;
+      }
+    }
+  }
+  for (int k = nv * V + threadIdx.x; k < n; k += kRowThreads) {
+    const uint32_t r = fdiv((uint32_t)k, p.div_lk);
+    lds[r * p.zs + k - (int)r * p.lk] = to_float<T>(src[k]);
+  }
+}
+
+// LDS rows -> n elements of dst (16-byte aligned)
+template <typename T>
+__device__ inline void unstage_rows(T *dst, const float *lds, int n, const RowPass &p) {
+  constexpr int V = Vec16<T>::N;
+  const int nv = n / V;
+  for (int v = threadIdx.x; v < nv; v += kRowThreads) {
+    float f[V];
+    uint32_t r = fdiv((uint32_t)(v * V), p.div_lk);
+    int c = v * V - (int)r * p.lk;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      f[e] = lds[r * p.zs + c];
+      if (++c == p.lk) {
+        c = 0;
+        ++r;
+      }
+    }
+    *reinterpret_cast<uint4 *>(dst + (int64_t)v * V) = pack16<T>(f);
+  }
+  for (int k = nv * V + threadIdx.x; k < n; k += kRowThreads) {
+    const uint32_t r = fdiv((uint32_t)k, p.div_lk);
+    store_scalar<T>(dst + k, lds[r * p.zs + k - (int)r * p.lk]);
+  }
+}
+
+// One row in registers: a[j] = exp(z[j] - max) / sum for j < lk (LKMAX >= lk,
+// fully unrolled so that the row's LDS reads are issued together).
+template <int LKMAX>
+__device__ inline void softmax_row(const float *z, int lk, float (&a)[LKMAX]) {
+  float mx = z[0];
+#pragma unroll
+  for (int j = 0; j < LKMAX; ++j) {
+    a[j] = j < lk ? z[j] : -INFINITY;
+    mx = a[j] > mx ? a[j] : mx;
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < LKMAX; ++j) {
+    a[j] = j < lk ? expf(a[j] - mx) : 0.0f;
+    sum += a[j];
+  }
+  const float r = 1.0f / sum;
+#pragma unroll
+  for (int j = 0; j < LKMAX; ++j) a[j] *= r;
+}
+
+// weights[r][j] = exp(z[r][j] - max_r) / sum_i exp(z[r][i] - max_r)
+template <typename T, int LKMAX>
+__global__ __launch_bounds__(kRowThreads) void softmax_rows_kernel(const T *__restrict__ logits,
+                                                                   T *__restrict__ weights,
+                                                                   RowPass p) {
+  extern __shared__ float zrow[];
+  for (int64_t r0 = (int64_t)blockIdx.x * p.rows; r0 < p.n_rows;
+       r0 += (int64_t)gridDim.x * p.rows) {
+    const int nr = (int)min((int64_t)p.rows, p.n_rows - r0);
+    stage_rows<T>(logits + r0 * p.lk, zrow, nr * p.lk, p);
+    __syncthreads();
+    if (threadIdx.x < nr) {
+      float *z = zrow + threadIdx.x * p.zs;
+      float a[LKMAX];
+      softmax_row<LKMAX>(z, p.lk, a);
+#pragma unroll
+      for (int j = 0; j < LKMAX; ++j)
+        if (j < p.lk) z[j] = a[j];
+    }
+    __syncthreads();
+    unstage_rows<T>(weights + r0 * p.lk, zrow, nr * p.lk, p);
+    __syncthreads();
+  }
+}
+
+// Derivative through the softmax, in place: on entry g holds dLoss/dA (the
+// regular backward's grad_attn for weights A = softmax(z)); on exit
+// dLoss/dz_j = A_j (g_j - sum_i A_i g_i), with A recomputed from z in fp32.
+template <typename T, int LKMAX>
+__global__ __launch_bounds__(kRowThreads) void softmax_grad_rows_kernel(
+    const T *__restrict__ logits, T *g, RowPass p) {
+  extern __shared__ float zrow[];
+  float *grow = zrow + p.rows * p.zs;
+  for (int64_t r0 = (int64_t)blockIdx.x * p.rows; r0 < p.n_rows;
+       r0 += (int64_t)gridDim.x * p.rows) {
+    const int nr = (int)min((int64_t)p.rows, p.n_rows - r0);
+    stage_rows<T>(logits + r0 * p.lk, zrow, nr * p.lk, p);
+    stage_rows<T>(g + r0 * p.lk, grow, nr * p.lk, p);
+    __syncthreads();
+    if (threadIdx.x < nr) {
+      float *gr = grow + threadIdx.x * p.zs;
+      float a[LKMAX], ga[LKMAX];
+      softmax_row<LKMAX>(zrow + threadIdx.x * p.zs, p.lk, a);
+      float dot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < LKMAX; ++j) {
+        ga[j] = j < p.lk ? gr[j] : 0.0f;
+        dot = fmaf(a[j], ga[j], dot);
+      }
+#pragma unroll
+      for (int j = 0; j < LKMAX; ++j)
+        if (j < p.lk) gr[j] = a[j] * (ga[j] - dot);
+    }
+    __syncthreads();
+    unstage_rows<T>(g + r0 * p.lk, grow, nr * p.lk, p);
+    __syncthreads();
+  }
+}
+
+RowPass make_row_pass(int64_t n_rows, int lk) {
+  RowPass p{};
+  p.n_rows = n_rows;
+  p.lk = lk;
+  p.zs = lk | 1;
+  // about 33 KB of LDS per staged tensor
+  p.rows = std::max(64, std::min(kRowThreads, (33 * kRowThreads) / p.zs / 64 * 64));
+  p.div_lk = make_fastdiv((uint32_t)lk);
+  return p;
+}
+
 // Head-queries per block: one block of up to 256 lanes, shrunk so the
 // per-sample LDS stays within budget; always a whole number of wavefronts.
 int pick_hqb(int G, int LK, int bytes_per_sample) {
@@ -312,18 +534,24 @@ int pick_hqb(int G, int LK, int bytes_per_sample) {
 }
 
 template <typename T, int D>
-hipError_t fwd_launch(const LaunchArgs &a, hipStream_t stream) {
+hipError_t fwd_launch(const LaunchArgs &a, bool softmax, hipStream_t stream) {
   using RL = RowLayout<T, D>;
   const int LK = (int)(a.L * a.K);
-  const int hqb = pick_hqb(RL::G, LK, (int)sizeof(Corners));
+  // softmax: one more fp32 per sample (the logit) and one per head-query (1 / sum)
+  const int hqb = pick_hqb(RL::G, LK, (int)sizeof(Corners) + (softmax ? 8 : 0));
   const int64_t total_hq = a.nb * a.Q * a.M;
   const int64_t blocks = padded_grid((total_hq + hqb - 1) / hqb);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)LK * (hqb + 1) * sizeof(Corners);
+  size_t lds = (size_t)LK * (hqb + 1) * sizeof(Corners);
+  if (softmax) lds += ((size_t)hqb * (LK + 1) + hqb) * sizeof(float);
   prof_begin(stream);
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds, stream,
-                     a, hqb);
-  prof_end(stream, "fwd");
+  if (softmax)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
+                       stream, a, hqb);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
+                       stream, a, hqb);
+  prof_end(stream, softmax ? "fwd_softmax" : "fwd");
   return hipGetLastError();
 }
 
@@ -346,12 +574,12 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
 }
 
 template <typename T>
-hipError_t fwd_dispatch_d(const LaunchArgs &a, hipStream_t s) {
+hipError_t fwd_dispatch_d(const LaunchArgs &a, bool softmax, hipStream_t s) {
   switch (a.D) {
-    case 8: return fwd_launch<T, 8>(a, s);
-    case 16: return fwd_launch<T, 16>(a, s);
-    case 32: return fwd_launch<T, 32>(a, s);
-    case 64: return fwd_launch<T, 64>(a, s);
+    case 8: return fwd_launch<T, 8>(a, softmax, s);
+    case 16: return fwd_launch<T, 16>(a, softmax, s);
+    case 32: return fwd_launch<T, 32>(a, softmax, s);
+    case 64: return fwd_launch<T, 64>(a, softmax, s);
   }
   return hipErrorInvalidValue;
 }
@@ -369,9 +597,10 @@ hipError_t bwd_dispatch_d(const LaunchArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream) {
+hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream, bool softmax) {
   if (a.nb * a.Q * a.M == 0) return hipSuccess;
-  return dt == Dtype::F32 ? fwd_dispatch_d<float>(a, stream) : fwd_dispatch_d<bf16_t>(a, stream);
+  return dt == Dtype::F32 ? fwd_dispatch_d<float>(a, softmax, stream)
+                          : fwd_dispatch_d<bf16_t>(a, softmax, stream);
 }
 
 hipError_t launch_backward(const LaunchArgs &a, Dtype dt, Accum acc, hipStream_t stream) {
@@ -379,6 +608,68 @@ hipError_t launch_backward(const LaunchArgs &a, Dtype dt, Accum acc, hipStream_t
   if (dt == Dtype::F32) return bwd_dispatch_d<float, float>(a, stream);
   if (acc == Accum::F32) return bwd_dispatch_d<bf16_t, float>(a, stream);
   return bwd_dispatch_d<bf16_t, bf16_t>(a, stream);
+}
+
+template <int LKMAX>
+void enqueue_softmax_rows(const void *logits, void *weights, const RowPass &p, int64_t blocks,
+                          size_t lds, Dtype dt, hipStream_t stream) {
+  if (dt == Dtype::F32)
+    hipLaunchKernelGGL((softmax_rows_kernel<float, LKMAX>), dim3((unsigned)blocks),
+                       dim3(kRowThreads), lds, stream, static_cast<const float *>(logits),
+                       static_cast<float *>(weights), p);
+  else
+    hipLaunchKernelGGL((softmax_rows_kernel<bf16_t, LKMAX>), dim3((unsigned)blocks),
+                       dim3(kRowThreads), lds, stream, static_cast<const bf16_t *>(logits),
+                       static_cast<bf16_t *>(weights), p);
+}
+
+template <int LKMAX>
+void enqueue_softmax_grad_rows(const void *logits, void *grad, const RowPass &p, int64_t blocks,
+                               size_t lds, Dtype dt, hipStream_t stream) {
+  if (dt == Dtype::F32)
+    hipLaunchKernelGGL((softmax_grad_rows_kernel<float, LKMAX>), dim3((unsigned)blocks),
+                       dim3(kRowThreads), lds, stream, static_cast<const float *>(logits),
+                       static_cast<float *>(grad), p);
+  else
+    hipLaunchKernelGGL((softmax_grad_rows_kernel<bf16_t, LKMAX>), dim3((unsigned)blocks),
+                       dim3(kRowThreads), lds, stream, static_cast<const bf16_t *>(logits),
+                       static_cast<bf16_t *>(grad), p);
+}
+
+hipError_t launch_softmax_rows(const void *logits, void *weights, int64_t n_rows, int lk,
+                               Dtype dt, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  if (lk < 1 || lk > 64) return hipErrorInvalidValue;
+  const RowPass p = make_row_pass(n_rows, lk);
+  const int64_t blocks = std::min<int64_t>((n_rows + p.rows - 1) / p.rows, int64_t(1) << 20);
+  const size_t lds = (size_t)p.rows * p.zs * sizeof(float);
+  prof_begin(stream);
+  if (lk <= 16)
+    enqueue_softmax_rows<16>(logits, weights, p, blocks, lds, dt, stream);
+  else if (lk <= 32)
+    enqueue_softmax_rows<32>(logits, weights, p, blocks, lds, dt, stream);
+  else
+    enqueue_softmax_rows<64>(logits, weights, p, blocks, lds, dt, stream);
+  prof_end(stream, "softmax_rows");
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_grad_rows(const void *logits, void *grad, int64_t n_rows, int lk,
+                                    Dtype dt, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  if (lk < 1 || lk > 64) return hipErrorInvalidValue;
+  const RowPass p = make_row_pass(n_rows, lk);
+  const int64_t blocks = std::min<int64_t>((n_rows + p.rows - 1) / p.rows, int64_t(1) << 20);
+  const size_t lds = 2 * (size_t)p.rows * p.zs * sizeof(float);
+  prof_begin(stream);
+  if (lk <= 16)
+    enqueue_softmax_grad_rows<16>(logits, grad, p, blocks, lds, dt, stream);
+  else if (lk <= 32)
+    enqueue_softmax_grad_rows<32>(logits, grad, p, blocks, lds, dt, stream);
+  else
+    enqueue_softmax_grad_rows<64>(logits, grad, p, blocks, lds, dt, stream);
+  prof_end(stream, "softmax_grad_rows");
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {

@@ -151,7 +151,14 @@ void prof_end(hipStream_t stream, const char *name);
 enum class Dtype { F32, BF16 };
 enum class Accum { F32, BF16 };
 
-hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream);
+// softmax: a.attn holds raw logits, normalised per head-query inside the kernel
+hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream, bool softmax = false);
+// Row passes of the softmax method over n_rows rows of lk logits each:
+// weights = softmax(logits); grad (dLoss/dA on entry) becomes dLoss/dlogits.
+hipError_t launch_softmax_rows(const void *logits, void *weights, int64_t n_rows, int lk,
+                               Dtype dt, hipStream_t stream);
+hipError_t launch_softmax_grad_rows(const void *logits, void *grad, int64_t n_rows, int lk,
+                                    Dtype dt, hipStream_t stream);
 hipError_t launch_backward(const LaunchArgs &a, Dtype dt, Accum acc, hipStream_t stream);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 

@@ -21,7 +21,7 @@ TOL_FWD_FP32 = (1e-5, 1e-6)
 TOL_BWD_FP32 = (1e-4, 1e-5)
 TOL_BF16 = (2e-2, 2e-2)
 
-FLOAT_KEYS = ("value", "sampling_locations", "attention_weights", "grad_out")
+FLOAT_KEYS = ("value", "sampling_locations", "attention_weights", "attention_logits", "grad_out")
 
 
 def say(msg: str):
@@ -60,6 +60,28 @@ def run_oracle(x: dict) -> dict:
     out = oracle.forward(*args)
     gv, gl, ga = oracle.backward(*args, x["grad_out"])
     return dict(out=out, grad_value=gv, grad_loc=gl, grad_attn=ga)
+
+
+def run_gpu_softmax(x: dict, accum=None, scatter="binned") -> dict:
+    """The "softmax" method: msda_forward_softmax and msda_backward_softmax on the logits."""
+    t = upload(x)
+    ops = (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"],
+           t["attention_logits"])
+    out = msda.msda_forward_softmax(*ops)
+    gv, gl, gz = msda.msda_backward_softmax(*ops, t["grad_out"], accum_dtype=accum,
+                                            scatter=scatter,
+                                            spatial_shapes_host=x["spatial_shapes"])
+    torch.cuda.synchronize()
+    return {k: v.double().cpu().numpy() for k, v in
+            dict(out=out, grad_value=gv, grad_loc=gl, grad_logits=gz).items()}
+
+
+def run_oracle_softmax(x: dict) -> dict:
+    args = (x["value"], x["spatial_shapes"], x["level_start_index"], x["sampling_locations"],
+            x["attention_logits"])
+    out = oracle.forward_softmax(*args)
+    gv, gl, gz = oracle.backward_softmax(*args, x["grad_out"])
+    return dict(out=out, grad_value=gv, grad_loc=gl, grad_logits=gz)
 
 
 def violations(got: np.ndarray, want: np.ndarray, rtol: float, atol: float):

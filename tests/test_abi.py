@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("msda_forward", "msda_forward_binned", "msda_forward_binned_workspace_bytes",
-              "msda_backward", "msda_backward_workspace_bytes",
+              "msda_forward_softmax", "msda_backward", "msda_backward_workspace_bytes",
+              "msda_backward_softmax", "msda_backward_softmax_workspace_bytes",
               "msda_status_string", "msda_last_error"):
         assert n in names
 
@@ -173,3 +174,62 @@ def test_last_error_is_cleared_by_a_good_call(lib):
     assert msda.msda_last_error() != ""
     assert fwd(lib, dims(Q=0), loc=None, attn=None, out=None) == 0
     assert msda.msda_last_error() == ""
+
+
+def fwd_softmax(lib, d, dtype=0, value=FAKE, logits=FAKE, out=FAKE):
+    return lib.msda_forward_softmax(value, FAKE, FAKE, FAKE, logits, out,
+                                    None if d is None else ctypes.byref(d), dtype, None)
+
+
+def bwd_softmax(lib, d, dtype=0, acc=0, scatter=1, shapes_host=None, ws=None, ws_bytes=0,
+                logits=FAKE, grad_logits=FAKE):
+    return lib.msda_backward_softmax(FAKE, FAKE, FAKE, FAKE, logits, FAKE, FAKE, FAKE,
+                                     grad_logits, ctypes.byref(d), dtype, acc, scatter,
+                                     shapes_host, ws, ws_bytes, None)
+
+
+def softmax_ws_bytes(lib, d, dtype=0, acc=0, scatter=1, shapes_host=None):
+    return lib.msda_backward_softmax_workspace_bytes(ctypes.byref(d), dtype, acc, scatter,
+                                                     shapes_host)
+
+
+def test_softmax_forward_rejections(lib):
+    assert fwd_softmax(lib, None) == 1
+    assert fwd_softmax(lib, dims(D=12)) == 3
+    assert fwd_softmax(lib, dims(L=8, K=9)) == 3
+    assert fwd_softmax(lib, dims(), logits=None) == 1
+    assert "attention_logits" in msda.msda_last_error()
+    assert fwd_softmax(lib, dims(), logits=FAKE + 4) == 4
+    assert fwd_softmax(lib, dims(), dtype=2) == 3
+    assert fwd_softmax(lib, dims(Q=0), logits=None, out=None) == 0
+    assert msda.msda_last_error() == ""
+
+
+def test_softmax_backward_workspace_sizes(lib):
+    # the weights image (B*Q*M*L*K elements rounded up to 256 bytes) ahead of the scatter's part
+    d = dims()                                                   # 1*16*2*2*2 = 128 samples
+    assert softmax_ws_bytes(lib, d, 0, 0, 1) == 512              # fp32, atomic: 512 + 0
+    assert softmax_ws_bytes(lib, d, 1, 1, 1) == 256              # bf16 data, bf16 accum
+    assert softmax_ws_bytes(lib, d, 1, 0, 1) == 256 + ws_bytes(lib, d, 1, 0, scatter=1)
+    binned = ws_bytes(lib, d, 0, 0, scatter=0, shapes_host=SHAPES)
+    assert softmax_ws_bytes(lib, d, 0, 0, 0, SHAPES) == 512 + binned
+    assert softmax_ws_bytes(lib, dims(Q=3), 0, 0, 1) == 256      # 3*2*4*4 = 96 bytes, rounded
+    assert softmax_ws_bytes(lib, dims(Q=0), 0, 0, 0, None) == 0
+    assert softmax_ws_bytes(lib, d, 0, 0, 0, None) == SIZE_MAX   # binned needs host shapes
+    assert softmax_ws_bytes(lib, d, 0, 1, 1) == SIZE_MAX         # fp32 data, bf16 accum
+
+
+def test_softmax_backward_rejections(lib):
+    d = dims()
+    need = softmax_ws_bytes(lib, d, 0, 0, 1)
+    assert bwd_softmax(lib, d) == 5                              # the weights need workspace
+    assert "softmax backward" in msda.msda_last_error()
+    assert bwd_softmax(lib, d, ws=FAKE, ws_bytes=need - 1) == 5
+    assert bwd_softmax(lib, d, ws=FAKE + 4, ws_bytes=need) == 4
+    assert bwd_softmax(lib, d, ws=FAKE, ws_bytes=need, grad_logits=None) == 1
+    assert "grad_logits" in msda.msda_last_error()
+    assert bwd_softmax(lib, d, ws=FAKE, ws_bytes=need, logits=None) == 1
+    assert "attention_logits" in msda.msda_last_error()
+    assert bwd_softmax(lib, d, scatter=0, ws=FAKE, ws_bytes=need) == 1
+    assert bwd_softmax(lib, d, acc=1) == 3
+    assert bwd_softmax(lib, dims(D=12)) == 3

@@ -278,3 +278,80 @@ def test_side_stream():
     with torch.cuda.stream(s):
         g = parity.run_gpu(x, stream=s)
     gate(x, g, parity.run_oracle(x))
+
+
+# ---------------------------------------------------------------- softmax method
+
+def gate_softmax(x, g, o):
+    fwd, bwd = (TOL_FWD_FP32, TOL_BWD_FP32) if x["dtype"] == "fp32" else (TOL_BF16, TOL_BF16)
+    check("out", g["out"], o["out"], *fwd)
+    for k in ("grad_value", "grad_loc", "grad_logits"):
+        check(k, g[k], o[k], *bwd)
+
+
+@pytest.mark.parametrize("wid,scatter", [(0, "binned"), (0, "atomic"), (1, "binned"),
+                                         (1, "atomic"), (2, "binned"), (3, "binned"),
+                                         (4, "binned")])
+def test_workload_softmax(wid, scatter):
+    wl = workloads.WORKLOADS[wid]
+    say(f"[parity] softmax method: workload {wid} {wl.name} {wl.dtype} scatter={scatter}")
+    x = workloads.make_inputs(wid)
+    gate_softmax(x, parity.run_gpu_softmax(x, scatter=scatter), parity.run_oracle_softmax(x))
+
+
+SOFTMAX_EDGE = ("ragged_fp32", "ragged_bf16", "one_level_one_point", "max_lk_16_levels",
+                "max_lk_32_points", "d64_bf16", "d8_fp32")
+
+
+@pytest.mark.parametrize("name", SOFTMAX_EDGE)
+def test_softmax_edge(name):
+    wl = EDGE[name]
+    say(f"[parity] softmax method, edge {name}: L*K={wl.L * wl.K} D={wl.D} {wl.dtype}")
+    x = workloads.make_inputs(wl, seed=zlib.crc32(name.encode()) % 100000)
+    o = parity.run_oracle_softmax(x)
+    g = parity.run_gpu_softmax(x)
+    gate_softmax(x, g, o)
+    if wl.L * wl.K == 1:  # one sample per head-query: weight 1, zero logit gradient
+        assert np.all(g["grad_logits"] == 0.0)
+
+
+def test_softmax_extreme_logits():
+    """Shift invariance at large magnitudes, -Inf logits (zero weight), rows of equal
+    logits and exp underflow; also that the forward is bit-identical across runs."""
+    say("[parity] softmax method: extreme logits")
+    wl = EDGE["ragged_fp32"]
+    x = workloads.make_inputs(wl, seed=11)
+    z = x["attention_logits"]
+    z[0, 0, 0] += 3.0e4                       # one row shifted far up
+    z[0, 1, 1] -= 3.0e4                       # one far down
+    z[1, 2, 0] = 7.25                         # all equal: uniform weights
+    z[1, 3, 2, 0, 0] = -np.inf                # one sample with weight exactly 0
+    z[2, 4, 1] = 0.0
+    z[2, 4, 1, 0, 0] = 150.0                  # the others underflow in fp32 and fp64 alike
+    z[2, 5, 2] *= 60.0                        # a wide spread
+    o = parity.run_oracle_softmax(x)
+    assert all(np.isfinite(v).all() for v in o.values())
+    g = parity.run_gpu_softmax(x)
+    gate_softmax(x, g, o)
+    t = parity.upload(x)
+    ops = (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"],
+           t["attention_logits"])
+    a, b = msda.msda_forward_softmax(*ops), msda.msda_forward_softmax(*ops)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "the softmax forward must be bit-identical across runs"
+
+
+def test_softmax_matches_plain_method_on_normalised_weights():
+    """At full encoder size: the fused softmax forward against msda_forward on weights
+    that torch normalised (the two differ only by the fp32 rounding of the weights)."""
+    say("[parity] softmax forward vs msda_forward(torch.softmax(logits)), encoder sizes")
+    wl = workloads.WORKLOADS[2]
+    x = workloads.make_inputs(2, with_grad=False)
+    t = parity.upload(x)
+    ops = (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"])
+    z = t["attention_logits"]
+    a = torch.softmax(z.reshape(wl.B, -1, wl.M, wl.L * wl.K), dim=-1).reshape(z.shape)
+    fused = msda.msda_forward_softmax(*ops, z)
+    plain = msda.msda_forward(*ops, a.contiguous())
+    torch.cuda.synchronize()
+    check("out", fused.double().cpu().numpy(), plain.double().cpu().numpy(), *TOL_FWD_FP32)
