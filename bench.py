@@ -179,6 +179,105 @@ def cpu_baseline_single_thread(workload_id: int, seed: int, budget_s: float = 30
     return {"value": round(j["s"] * 1e6, 1), "unit": "us/call", "cores": j["threads"]}
 
 
+def grid_sample_msda_softmax(value, spatial_shapes, level_start_index, sampling_locations,
+                             attention_logits, spatial_shapes_host):
+    """The softmax-method operator composed from torch ops alone, for comparison:
+    torch.softmax over the L*K logits, then per level one
+    F.grid_sample(align_corners=False, padding_mode="zeros") of that level's
+    value map at grid = 2 * location - 1 (the equivalence chapter 1 of the
+    msda-triton course states, section "Bilinear interpolation: reading between
+    the pixels"), weighted and summed over levels and points.  Autograd provides
+    its backward; every intermediate it saves is what the fused kernels avoid."""
+    import torch
+    import torch.nn.functional as F
+
+    B, S, M, D = value.shape
+    Q, L, K = sampling_locations.shape[1], sampling_locations.shape[3], sampling_locations.shape[4]
+    a = torch.softmax(attention_logits.reshape(B, Q, M, L * K), dim=-1).view(B, Q, M, L, K)
+    out = None
+    start = 0
+    for lvl in range(L):
+        H, W = int(spatial_shapes_host[lvl][0]), int(spatial_shapes_host[lvl][1])
+        vl = value[:, start:start + H * W].permute(0, 2, 3, 1).reshape(B * M, D, H, W)
+        grid = (2.0 * sampling_locations[:, :, :, lvl] - 1.0).permute(0, 2, 1, 3, 4)
+        s = F.grid_sample(vl, grid.reshape(B * M, Q, K, 2), mode="bilinear",
+                          padding_mode="zeros", align_corners=False)        # (B*M, D, Q, K)
+        w = a[:, :, :, lvl].permute(0, 2, 1, 3).reshape(B * M, 1, Q, K)
+        part = (s * w).sum(-1)                                                 # (B*M, D, Q)
+        out = part if out is None else out + part
+        start += H * W
+    return out.view(B, M, D, Q).permute(0, 3, 1, 2).reshape(B, Q, M * D)
+
+
+def layer_comparison(wl: workloads.Workload, dev, steps: int = 5) -> dict:
+    """A multi-scale deformable attention layer (projections around the operator,
+    softmax method) at the workload's sizes, forward + backward: the library's
+    kernels against the grid_sample composition.  Peak memory is the growth of
+    torch's allocated bytes over one step beyond what is resident before it
+    (parameters, inputs); time is the median of `steps` steps (HIP events)."""
+    import torch
+
+    from scale_deformable_attention_msda_amd.layer import MultiScaleDeformAttn
+
+    B, Q, S, M, D, L, K = wl.B, wl.num_queries, wl.S, wl.M, wl.D, wl.L, wl.K
+    C = M * D
+    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+    gen = torch.Generator(device="cpu").manual_seed(workloads.BASE_SEED)
+    query = torch.randn(B, Q, C, generator=gen).to(dev, dt)
+    value = torch.randn(B, S, C, generator=gen).to(dev, dt)
+    gout = torch.randn(B, Q, C, generator=gen).to(dev, dt)
+    host = np.asarray(wl.shapes, dtype=np.int64).reshape(L, 2)
+    shapes = torch.from_numpy(host).to(dev)
+    starts = torch.from_numpy(workloads.level_start_index(wl.shapes)).to(dev)
+    if wl.ref == "pixel_centres":
+        ref = torch.from_numpy(workloads.pixel_centre_refs(wl.shapes)).to(dev, dt)
+        ref = ref[None, :, None, :].expand(B, Q, L, 2).contiguous()
+    else:
+        ref = torch.rand(B, Q, 1, 2, generator=gen).to(dev, dt).expand(B, Q, L, 2).contiguous()
+    res = {}
+    for name, sampler, scatter in (("library", None, "binned"),
+                                   ("library_atomic", None, "atomic"),
+                                   ("grid_sample", grid_sample_msda_softmax, "binned")):
+        torch.manual_seed(0)
+        layer = MultiScaleDeformAttn(C, M, L, K, sampler=sampler, scatter=scatter).to(dev, dt)
+
+        def one_step():
+            layer.zero_grad(set_to_none=True)
+            out = layer(query, ref, value, shapes, starts, host)
+            out.backward(gout)
+
+        for _ in range(2):
+            one_step()
+        torch.cuda.synchronize()
+        layer.zero_grad(set_to_none=True)
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        one_step()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            one_step()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name] = {"ms_per_step": round(float(np.median(ts)), 3),
+                     "peak_mib": round(peak / 2 ** 20, 1)}
+        del layer
+        torch.cuda.empty_cache()
+    for name in ("library", "library_atomic"):
+        res[name]["peak_vs_grid_sample"] = round(res[name]["peak_mib"] /
+                                                 res["grid_sample"]["peak_mib"], 4)
+    res["how"] = (f"dim {C}, {M} heads, {L} levels, {K} points, B={B}, Q={Q}, S={S}, {wl.dtype}; "
+                  "library = the layer on msda_forward_softmax / msda_backward_softmax (binned or "
+                  "atomic scatter); grid_sample = the same layer on torch.softmax + F.grid_sample; "
+                  "peak = torch max_memory_allocated growth over one forward + backward step; "
+                  f"time = median of {steps} steps")
+    return res
+
+
 def percentiles(xs) -> dict:
     a = np.sort(np.asarray(xs, dtype=np.float64))
     return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.percentile(a, 50)), 3),
@@ -386,6 +485,9 @@ def main(argv=None) -> int:
             z = t["attention_logits"]
             a = torch.softmax(z.view(-1, LK), dim=-1).view(z.shape)
             msda.msda_forward(*ops(t)[:4], a, out=out, stream=stream)
+
+        log("[bench] layer-level forward + backward against the grid_sample composition")
+        extras["layer"] = layer_comparison(wl, dev)
 
         if args.gather == "direct":
             extras["softmax_method"] = {

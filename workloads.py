@@ -111,7 +111,8 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def _pixel_centre_refs(shapes) -> np.ndarray:
+def pixel_centre_refs(shapes) -> np.ndarray:
+    """(x, y) of every pyramid pixel centre, normalised per level; shape (S, 2)."""
     refs = []
     for h, w in shapes:
         r, c = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
@@ -138,7 +139,7 @@ def make_inputs(wl: Workload | int, seed: int | None = None, with_grad: bool = T
     elif wl.ref == "pixel_centres":
         if Q != S:
             raise ValueError("pixel-centre references need one query per pyramid pixel")
-        ref = _pixel_centre_refs(wl.shapes)[None, :, None, None, None, :]
+        ref = pixel_centre_refs(wl.shapes)[None, :, None, None, None, :]
     else:
         raise ValueError(f"unknown reference-point recipe {wl.ref!r}")
     offsets = rng.standard_normal((B, Q, M, L, K, 2)) * wl.sigma_px
