@@ -273,6 +273,15 @@ typedef struct {
 
 msda_status msda_profile_start(int capacity);
 int msda_profile_stop(msda_kernel_time *out, int max);
+/*
+ * Restrict the sessions of this thread to the kernels named `name` (the names
+ * msda_profile_stop reports); NULL or "" records every kernel again.  Kernels
+ * left out get no events at all, so a session can time one kernel while
+ * disturbing the others as little as possible.  The events are created with
+ * hipEventDisableSystemFence: recording one does not write back or invalidate
+ * caches.
+ */
+void msda_profile_select(const char *name);
 
 /* Static description of a status code. */
 const char *msda_status_string(msda_status status);

@@ -101,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.msda_profile_start.restype = ctypes.c_int
     lib.msda_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
     lib.msda_profile_stop.restype = ctypes.c_int
+    lib.msda_profile_select.argtypes = [ctypes.c_char_p]
+    lib.msda_profile_select.restype = None
     _lib = lib
     return lib
 
@@ -118,6 +120,11 @@ def msda_profile_start(capacity: int) -> None:
     st = load_library().msda_profile_start(capacity)
     if st != MSDA_OK:
         raise MsdaError(st, "msda_profile_start")
+
+
+def msda_profile_select(name: str | None) -> None:
+    """Time only kernels of this name in later sessions (None: all kernels)."""
+    load_library().msda_profile_select(None if name is None else name.encode())
 
 
 def msda_profile_stop(max_records: int = 1 << 16) -> list:

@@ -1111,12 +1111,12 @@ size_t tile_lds_bytes() {
 template <typename T, int D>
 hipError_t launch_tile_and_merge(const BinArgs &a, hipStream_t s) {
   const size_t lds = tile_lds_bytes<T, D>();
-  prof_begin(s);
+  prof_begin(s, "bin_tile");
   hipLaunchKernelGGL((tile_kernel<T, D>), dim3(a.p.max_chunks), dim3(256), lds, s, a);
   prof_end(s, "bin_tile");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  prof_begin(s);
+  prof_begin(s, "bin_merge");
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.p.nbins), dim3(256), 0, s, a);
   prof_end(s, "bin_merge");
   return hipGetLastError();
@@ -1142,7 +1142,7 @@ hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   e = launch_zero(a.w.counts, counts_and_status_bytes(p), s);
   if (e != hipSuccess) return e;
   if (p.S > p.pyramid_rows) {
-    prof_begin(s);
+    prof_begin(s, "bin_zero_tail");
   hipLaunchKernelGGL((zero_tail_kernel<T>), dim3(1024), dim3(256), 0, s, a);
   prof_end(s, "bin_zero_tail");
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1151,16 +1151,16 @@ hipError_t launch_binned_t(const BinArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)((per_head + kCountSamples - 1) / kCountSamples),
                   (unsigned)(p.B * p.M));
   const size_t hist = (size_t)p.tiles_bm * sizeof(uint32_t);
-  prof_begin(s);
+  prof_begin(s, "bin_count");
   hipLaunchKernelGGL((count_kernel<T>), grid, dim3(256), hist, s, a);
   prof_end(s, "bin_count");
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  prof_begin(s);
+  prof_begin(s, "bin_plan");
   hipLaunchKernelGGL(plan_kernel, dim3((unsigned)((p.nbins + kPlanBlock - 1) / kPlanBlock)),
                      dim3(kPlanBlock), 0, s, a);
   prof_end(s, "bin_plan");
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  prof_begin(s);
+  prof_begin(s, "bin_scatter");
   hipLaunchKernelGGL((scatter_kernel<T>), grid, dim3(256), hist, s, a);
   prof_end(s, "bin_scatter");
   if ((e = hipGetLastError()) != hipSuccess) return e;

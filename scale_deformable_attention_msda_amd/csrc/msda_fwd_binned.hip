@@ -678,7 +678,7 @@ hipError_t launch_binned_t(const FwdArgs &fa, hipStream_t s) {
   const FwdPlan &p = fa.p;
   const dim3 grid((unsigned)p.nqb, (unsigned)(p.nb * p.M));
   hipError_t e;
-  prof_begin(s);
+  prof_begin(s, "fwd_count");
   const dim3 cgrid((unsigned)p.nqc, (unsigned)p.nb);
   const size_t clds = (size_t)p.M * p.nbm * 4;
   if (p.K <= 4)
@@ -687,12 +687,12 @@ hipError_t launch_binned_t(const FwdArgs &fa, hipStream_t s) {
     hipLaunchKernelGGL((fwd_count_kernel<T, 8>), cgrid, dim3(kFwdCountQ), clds, s, fa);
   prof_end(s, "fwd_count");
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  prof_begin(s);
+  prof_begin(s, "fwd_scatter");
   hipLaunchKernelGGL(fwd_scatter_kernel, grid, dim3(kFwdCountQ), (size_t)p.nbm * 12, s, fa);
   prof_end(s, "fwd_scatter");
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int row = p.D * (int)sizeof(T);
-  prof_begin(s);
+  prof_begin(s, "fwd_tile");
   switch (row) {
     case 64: e = launch_tile_nt<T, 16>(fa, s); break;
     case 128: e = launch_tile_nt<T, 32>(fa, s); break;

@@ -544,7 +544,7 @@ hipError_t fwd_launch(const LaunchArgs &a, bool softmax, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   size_t lds = (size_t)LK * (hqb + 1) * sizeof(Corners);
   if (softmax) lds += ((size_t)hqb * (LK + 1) + hqb) * sizeof(float);
-  prof_begin(stream);
+  prof_begin(stream, softmax ? "fwd_softmax" : "fwd");
   if (softmax)
     hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
                        stream, a, hqb);
@@ -566,7 +566,7 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t lds = (size_t)LK * (hqb + 1) * (sizeof(Corners) + sizeof(SampleAux)) +
                     (size_t)LK * hqb * 3 * sizeof(float);
-  prof_begin(stream);
+  prof_begin(stream, "bwd_atomic");
   hipLaunchKernelGGL((bwd_kernel<T, D, AccT>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
                      stream, a, hqb);
   prof_end(stream, "bwd_atomic");
@@ -643,7 +643,7 @@ hipError_t launch_softmax_rows(const void *logits, void *weights, int64_t n_rows
   const RowPass p = make_row_pass(n_rows, lk);
   const int64_t blocks = std::min<int64_t>((n_rows + p.rows - 1) / p.rows, int64_t(1) << 20);
   const size_t lds = (size_t)p.rows * p.zs * sizeof(float);
-  prof_begin(stream);
+  prof_begin(stream, "softmax_rows");
   if (lk <= 16)
     enqueue_softmax_rows<16>(logits, weights, p, blocks, lds, dt, stream);
   else if (lk <= 32)
@@ -661,7 +661,7 @@ hipError_t launch_softmax_grad_rows(const void *logits, void *grad, int64_t n_ro
   const RowPass p = make_row_pass(n_rows, lk);
   const int64_t blocks = std::min<int64_t>((n_rows + p.rows - 1) / p.rows, int64_t(1) << 20);
   const size_t lds = 2 * (size_t)p.rows * p.zs * sizeof(float);
-  prof_begin(stream);
+  prof_begin(stream, "softmax_grad_rows");
   if (lk <= 16)
     enqueue_softmax_grad_rows<16>(logits, grad, p, blocks, lds, dt, stream);
   else if (lk <= 32)
@@ -676,7 +676,7 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
   const size_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((n16 + 255) / 256, 4096);
-  prof_begin(stream);
+  prof_begin(stream, "zero");
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<uint4 *>(p), n16);
   prof_end(stream, "zero");
@@ -687,7 +687,7 @@ hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, size_t n, hipStr
   const size_t n8 = n / 8;
   if (n8 == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((n8 + 255) / 256, 4096);
-  prof_begin(stream);
+  prof_begin(stream, "cast");
   hipLaunchKernelGGL(cast_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const float4 *>(src), reinterpret_cast<uint4 *>(dst), n8);
   prof_end(stream, "cast");

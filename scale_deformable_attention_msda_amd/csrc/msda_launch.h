@@ -144,8 +144,8 @@ struct FwdArgs {
 
 // Kernel timing hooks (no-ops unless a profiling session is open on this
 // thread): every launch site calls prof_begin() before and prof_end() after
-// enqueueing its kernel.
-void prof_begin(hipStream_t stream);
+// enqueueing its kernel, with the same name.
+void prof_begin(hipStream_t stream, const char *name);
 void prof_end(hipStream_t stream, const char *name);
 
 enum class Dtype { F32, BF16 };

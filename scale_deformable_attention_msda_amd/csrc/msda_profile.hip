@@ -2,6 +2,8 @@
 #include "msda.h"
 #include "msda_launch.h"
 
+#include <cstring>
+#include <string>
 #include <vector>
 
 namespace msda {
@@ -21,6 +23,7 @@ struct Session {
   size_t next = 0;               // next free pool entry in this session
   bool failed = false;
   hipEvent_t pending = nullptr;  // begin event of the launch being enqueued
+  std::string only;              // record only kernels of this name ("" = all)
 };
 
 thread_local Session g_session;
@@ -28,7 +31,9 @@ thread_local Session g_session;
 hipEvent_t take_event(Session &s) {
   if (s.next == s.pool.size()) {
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) {
+    // timing-only events: no system-scope fence, so recording one does not
+    // write back and invalidate the caches in the middle of the measured work
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       s.failed = true;
       return nullptr;
     }
@@ -39,10 +44,14 @@ hipEvent_t take_event(Session &s) {
 
 }  // namespace
 
-void prof_begin(hipStream_t stream) {
+static bool selected(const Session &s, const char *name) {
+  return s.only.empty() || std::strcmp(s.only.c_str(), name) == 0;
+}
+
+void prof_begin(hipStream_t stream, const char *name) {
   Session &s = g_session;
   s.pending = nullptr;
-  if (!s.on || (int)s.records.size() >= s.capacity) return;
+  if (!s.on || !selected(s, name) || (int)s.records.size() >= s.capacity) return;
   hipEvent_t e = take_event(s);
   if (e && hipEventRecord(e, stream) == hipSuccess) s.pending = e;
   else s.failed = true;
@@ -50,7 +59,7 @@ void prof_begin(hipStream_t stream) {
 
 void prof_end(hipStream_t stream, const char *name) {
   Session &s = g_session;
-  if (!s.on) return;
+  if (!s.on || !selected(s, name)) return;
   if (!s.pending) {
     ++s.dropped;
     return;
@@ -78,6 +87,8 @@ msda_status msda_profile_start(int capacity) {
   s.pending = nullptr;
   return MSDA_OK;
 }
+
+void msda_profile_select(const char *name) { msda::g_session.only = name ? name : ""; }
 
 int msda_profile_stop(msda_kernel_time *out, int max) {
   msda::Session &s = msda::g_session;

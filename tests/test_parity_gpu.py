@@ -355,3 +355,35 @@ def test_softmax_matches_plain_method_on_normalised_weights():
     plain = msda.msda_forward(*ops, a.contiguous())
     torch.cuda.synchronize()
     check("out", fused.double().cpu().numpy(), plain.double().cpu().numpy(), *TOL_FWD_FP32)
+
+
+# ---------------------------------------------------------- query dispatch order
+
+@pytest.mark.parametrize("kind", ["morton", "hilbert"])
+def test_query_order_permutes_outputs(kind):
+    """The kernels take head-queries in memory order, so permuting the query axis
+    reorders the dispatch.  At encoder size: the forward of the permuted inputs is
+    the permutation of the forward, bit for bit (a head-query's sum does not depend
+    on its block); the backward's outputs agree within the backward tolerance (the
+    order of additions into grad_value, and the fp64 grouping of a sample's
+    partial dot products, follow its position in the binned records)."""
+    wl = workloads.WORKLOADS[2]
+    say(f"[parity] query order {kind}: workload 2 {wl.name}")
+    x = workloads.make_inputs(2)
+    t = parity.upload(x)
+    perm = torch.from_numpy(workloads.query_order(wl.shapes, kind)).cuda()
+    pt = dict(t)
+    for k in ("sampling_locations", "attention_weights", "grad_out"):
+        pt[k] = t[k][:, perm].contiguous()
+    host = x["spatial_shapes"]
+    out = msda.msda_forward(*parity.operands(t))
+    gv, gl, ga = msda.msda_backward(*parity.operands(t), t["grad_out"], spatial_shapes_host=host)
+    out_p = msda.msda_forward(*parity.operands(pt))
+    gv_p, gl_p, ga_p = msda.msda_backward(*parity.operands(pt), pt["grad_out"],
+                                          spatial_shapes_host=host)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out[:, perm]), "forward must not depend on the dispatch order"
+    np_ = lambda v: v.double().cpu().numpy()
+    check("grad_value", np_(gv_p), np_(gv), *TOL_BWD_FP32)
+    check("grad_loc", np_(gl_p), np_(gl[:, perm]), *TOL_BWD_FP32)
+    check("grad_attn", np_(ga_p), np_(ga[:, perm]), *TOL_BWD_FP32)

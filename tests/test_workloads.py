@@ -70,3 +70,28 @@ def test_bf16_rounding_is_exact_and_nearest_even():
     arr = workloads.make_inputs(small, seed=3)
     for k in ("value", "sampling_locations", "attention_weights", "grad_out"):
         assert np.all(arr[k].view(np.uint32) & 0xFFFF == 0), k
+
+
+@pytest.mark.parametrize("kind", ["linear", "morton", "hilbert"])
+def test_query_orders_are_level_major_permutations(kind):
+    shapes = workloads.PYRAMID_DETR
+    order = workloads.query_order(shapes, kind)
+    S = sum(h * w for h, w in shapes)
+    assert np.array_equal(np.sort(order), np.arange(S))
+    base = 0
+    for h, w in shapes:  # each level's queries stay in that level's block
+        assert set(order[base:base + h * w]) == set(range(base, base + h * w))
+        base += h * w
+
+
+def test_hilbert_order_steps_to_a_neighbour_on_square_levels():
+    # on a 2^k x 2^k level the Hilbert curve moves one pixel at a time
+    for n in (2, 4, 8, 32):
+        r, c = np.divmod(workloads.query_order(((n, n),), "hilbert"), n)
+        assert np.all(np.abs(np.diff(r)) + np.abs(np.diff(c)) == 1)
+        assert (r[0], c[0]) == (0, 0)
+
+
+def test_morton_order_is_z_order():
+    r, c = np.divmod(workloads.query_order(((4, 4),), "morton"), 4)
+    assert list(zip(r[:8], c[:8])) == [(0, 0), (0, 1), (1, 0), (1, 1), (0, 2), (0, 3), (1, 2), (1, 3)]

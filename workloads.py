@@ -120,6 +120,59 @@ def pixel_centre_refs(shapes) -> np.ndarray:
     return np.concatenate(refs, axis=0)  # (S, 2), level-major, row-major
 
 
+def _morton_key(r: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Z-order key: the bits of row and column interleaved (column in the even bits)."""
+    key = np.zeros(r.shape, dtype=np.int64)
+    for bit in range(16):
+        key |= ((c >> bit) & 1) << (2 * bit)
+        key |= ((r >> bit) & 1) << (2 * bit + 1)
+    return key
+
+
+def _hilbert_key(r: np.ndarray, c: np.ndarray, n: int) -> np.ndarray:
+    """Distance along the Hilbert curve over an n x n grid (n a power of two) of
+    cell (x = c, y = r): at each scale s the quadrant adds s^2 * (3 rx xor ry),
+    and the coordinates are reflected and swapped into that quadrant's frame."""
+    x, y = c.astype(np.int64).copy(), r.astype(np.int64).copy()
+    d = np.zeros(x.shape, dtype=np.int64)
+    s = n // 2
+    while s > 0:
+        rx = ((x & s) > 0).astype(np.int64)
+        ry = ((y & s) > 0).astype(np.int64)
+        d += s * s * ((3 * rx) ^ ry)
+        flip = (ry == 0) & (rx == 1)
+        x = np.where(flip, s - 1 - x, x)
+        y = np.where(flip, s - 1 - y, y)
+        swap = ry == 0
+        x, y = np.where(swap, y, x), np.where(swap, x, y)
+        x &= s - 1
+        y &= s - 1
+        s //= 2
+    return d
+
+
+def query_order(shapes, kind: str) -> np.ndarray:
+    """A dispatch order of the encoder's queries (one per pyramid pixel, level-major,
+    row-major): position i of the result is the query visited i-th.  "linear"
+    keeps raster order; "morton" and "hilbert" visit each level's pixels along
+    that space-filling curve, levels still in order."""
+    if kind not in ("linear", "morton", "hilbert"):
+        raise ValueError(f"unknown query order {kind!r}")
+    order, base = [], 0
+    for h, w in shapes:
+        r, c = np.divmod(np.arange(h * w, dtype=np.int64), w)
+        if kind == "linear":
+            key = np.arange(h * w)
+        elif kind == "morton":
+            key = _morton_key(r, c)
+        else:
+            n = 1 << int(np.ceil(np.log2(max(h, w, 1))))
+            key = _hilbert_key(r, c, n)
+        order.append(base + np.argsort(key, kind="stable"))
+        base += h * w
+    return np.concatenate(order)
+
+
 def make_inputs(wl: Workload | int, seed: int | None = None, with_grad: bool = True) -> dict:
     """Build one workload's operands as numpy arrays (see the module docstring)."""
     if isinstance(wl, int):
