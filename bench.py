@@ -221,7 +221,7 @@ def layer_comparison(wl: workloads.Workload, dev, steps: int = 5) -> dict:
 
     B, Q, S, M, D, L, K = wl.B, wl.num_queries, wl.S, wl.M, wl.D, wl.L, wl.K
     C = M * D
-    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
     gen = torch.Generator(device="cpu").manual_seed(workloads.BASE_SEED)
     query = torch.randn(B, Q, C, generator=gen).to(dev, dt)
     value = torch.randn(B, S, C, generator=gen).to(dev, dt)
@@ -333,7 +333,7 @@ def main(argv=None) -> int:
         return 2
     msda.load_library()
     wl = workloads.WORKLOADS[args.workload]
-    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
@@ -355,7 +355,7 @@ def main(argv=None) -> int:
     ga = torch.empty_like(t0["attention_weights"])
     dims = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
     sc = msda.MSDA_SCATTER_BINNED if args.scatter == "binned" else msda.MSDA_SCATTER_ATOMIC
-    dcode = 0 if wl.dtype == "fp32" else 1
+    dcode = msda._DTYPES[dt]
     need_b = msda.msda_backward_workspace_bytes(dims, dcode, msda.MSDA_FP32, sc, shapes_host)
     need_s = msda.msda_backward_softmax_workspace_bytes(dims, dcode, msda.MSDA_FP32, sc,
                                                         shapes_host)
@@ -565,7 +565,7 @@ def main(argv=None) -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.dtype == "fp32" else "bf16",
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16"}[wl.dtype],
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.B} Q=S={wl.num_queries} M={wl.M} D={wl.D} "
                                f"L={wl.L} (" + ", ".join(f"{h}x{w}" for h, w in wl.shapes) +

@@ -45,7 +45,7 @@
  *   - Errors: a non-OK status is returned before anything is enqueued when the
  *     arguments are rejected; msda_last_error() then describes the reason.
  *     MSDA_ERR_HIP reports a failed launch.
- *   - Supported: dtype FP32 or BF16; D in {8, 16, 32, 64}; 1 <= L <= 16;
+ *   - Supported: dtype FP32, BF16 or FP16 (IEEE binary16); D in {8, 16, 32, 64}; 1 <= L <= 16;
  *     1 <= K <= 32; L*K <= 64; B, Q >= 0; S >= 1; M >= 1; one batch image of
  *     value (S*M*D elements) below 2^30 bytes; every element count below 2^62.
  *     Float pointers must be 16-byte aligned.  Anything else returns
@@ -82,7 +82,7 @@ typedef enum {
     MSDA_ERR_HIP = 6
 } msda_status;
 
-typedef enum { MSDA_FP32 = 0, MSDA_BF16 = 1 } msda_dtype;
+typedef enum { MSDA_FP32 = 0, MSDA_BF16 = 1, MSDA_FP16 = 2 } msda_dtype;
 
 /* Sizes of one call, in the pages' notation. */
 typedef struct {
@@ -98,7 +98,8 @@ typedef struct {
 /*
  * Forward: out = MSDA(value, spatial_shapes, level_start_index,
  * sampling_locations, attention_weights).  Accumulates in fp32 and rounds
- * once to `dtype` (round to nearest even for BF16).  Deterministic: the
+ * once to `dtype` (round to nearest even for BF16 and FP16; FP16 overflows
+ * to +-Inf past 65504).  Deterministic: the
  * same inputs give bit-identical outputs.  Q = 0 or B = 0 enqueues nothing.
  * Each block gathers the corner rows of a run of head-queries straight from
  * global memory (through the L1/L2 caches); no workspace.
@@ -166,7 +167,7 @@ typedef enum {
      * workspace and a host copy of spatial_shapes.  fp32 accumulation. */
     MSDA_SCATTER_BINNED = 0,
     /* Each sample adds A * w_c * grad_out into its four corner rows with
-     * device-scope atomics (fp32, or packed bf16 for BF16 data). */
+     * device-scope atomics (fp32, or packed bf16 / fp16 for 16-bit data). */
     MSDA_SCATTER_ATOMIC = 1
 } msda_scatter;
 
@@ -175,8 +176,9 @@ typedef enum {
  * accumulator and scatter:
  *   BINNED:            bin tables, sorted sample ids and tile-rim partials
  *                      (planned from spatial_shapes_host, [L,2] on the host);
- *   ATOMIC, BF16 data,
- *   FP32 accumulator:  B*S*M*D*4 (the fp32 accumulator);
+ *   ATOMIC, BF16 or
+ *   FP16 data, FP32
+ *   accumulator:       B*S*M*D*4 (the fp32 accumulator);
  *   otherwise          0.
  * Returns SIZE_MAX when the arguments would be rejected by msda_backward
  * (msda_last_error() then says why).
@@ -204,9 +206,10 @@ size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
  *           Limits (else MSDA_ERR_UNSUPPORTED): at most 12288 8x8 tiles over
  *           all levels, B*M <= 65535, B*Q*M*L*K < 2^32 - 1.
  *   ATOMIC: FP32 data -> accum FP32 (fp32 atomics into grad_value);
- *           BF16 data -> accum FP32 (atomics into an fp32 workspace, then one
- *           rounding to bf16) or accum BF16 (packed-bf16 atomics straight
- *           into grad_value, every partial sum rounded to bf16).
+ *           BF16 / FP16 data -> accum FP32 (atomics into an fp32 workspace,
+ *           then one rounding to the data type) or accum = the data type
+ *           (packed-bf16 / packed-fp16 atomics straight into grad_value,
+ *           every partial sum rounded to that type).
  *           spatial_shapes_host may be NULL.
  * workspace must hold at least msda_backward_workspace_bytes() bytes
  * (16-byte aligned; NULL when that is 0).  Its contents on entry do not
@@ -241,8 +244,8 @@ size_t msda_backward_softmax_workspace_bytes(const msda_dims *dims, msda_dtype d
  * workspace, msda_backward with those weights (grad_attn written into
  * grad_logits), then an in-place pass that turns gA into grad_logits with A
  * recomputed from z in fp32.  grad_value and grad_loc are those of
- * msda_backward for weights A (in BF16, A is rounded to bf16 once before the
- * scatter, and gA once before the last pass).  scatter, accum_dtype,
+ * msda_backward for weights A (for BF16 and FP16 data, A is rounded to the
+ * data type once before the scatter, and gA once before the last pass).  scatter, accum_dtype,
  * spatial_shapes_host, limits and errors as for msda_backward; workspace must
  * hold msda_backward_softmax_workspace_bytes() bytes (16-byte aligned).
  */

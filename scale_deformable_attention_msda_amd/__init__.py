@@ -37,9 +37,10 @@ LIB_PATH = os.path.join(_PKG, "libmsda.so")
 MSDA_OK = 0
 MSDA_FP32 = 0
 MSDA_BF16 = 1
+MSDA_FP16 = 2
 MSDA_SCATTER_BINNED = 0
 MSDA_SCATTER_ATOMIC = 1
-_DTYPES = {torch.float32: MSDA_FP32, torch.bfloat16: MSDA_BF16}
+_DTYPES = {torch.float32: MSDA_FP32, torch.bfloat16: MSDA_BF16, torch.float16: MSDA_FP16}
 _SCATTER = {"binned": MSDA_SCATTER_BINNED, "atomic": MSDA_SCATTER_ATOMIC}
 SIZE_MAX = 2 ** 64 - 1
 
@@ -168,7 +169,7 @@ def _stream(stream) -> int:
 def _common(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
             weights_name="attention_weights"):
     if value.dtype not in _DTYPES:
-        raise ValueError(f"value dtype {value.dtype} is not float32 or bfloat16")
+        raise ValueError(f"value dtype {value.dtype} is not float32, bfloat16 or float16")
     dt = value.dtype
     _check(value, "value")
     _check(spatial_shapes, "spatial_shapes", torch.int64)

@@ -34,7 +34,12 @@ bool mul_ok(int64_t a, int64_t b, int64_t *r) {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+msda::Dtype kernel_dtype(msda_dtype d) {
+  return d == MSDA_FP32 ? msda::Dtype::F32 : d == MSDA_BF16 ? msda::Dtype::BF16 : msda::Dtype::F16;
+}
+
 struct Checked {
+  msda_dtype dtype;      // data type of the floating tensors
   int64_t B, S, M, D, L, Q, K;
   int64_t elt;           // bytes per element of the data dtype
   int64_t value_elems;   // B*S*M*D
@@ -45,8 +50,10 @@ struct Checked {
 
 msda_status check_dims(const msda_dims *d, msda_dtype dtype, Checked *c) {
   if (!d) return fail(MSDA_ERR_NULL_POINTER, "dims is NULL");
-  if (dtype != MSDA_FP32 && dtype != MSDA_BF16)
-    return fail(MSDA_ERR_UNSUPPORTED, "dtype %d is not FP32 (0) or BF16 (1)", (int)dtype);
+  if (dtype != MSDA_FP32 && dtype != MSDA_BF16 && dtype != MSDA_FP16)
+    return fail(MSDA_ERR_UNSUPPORTED, "dtype %d is not FP32 (0), BF16 (1) or FP16 (2)",
+                (int)dtype);
+  c->dtype = dtype;
   c->B = d->batch;
   c->S = d->num_keys;
   c->M = d->num_heads;
@@ -178,7 +185,7 @@ msda_status forward_direct(const void *value, const int64_t *spatial_shapes,
                           out, dims, dtype, &c,
                           softmax ? "attention_logits" : "attention_weights"));
   if (c.hq_elems == 0) return MSDA_OK;
-  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const auto dt = kernel_dtype(dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t step = batches_per_launch(c);
   for (int64_t b0 = 0; b0 < c.B; b0 += step) {
@@ -240,7 +247,7 @@ msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes
     return fail(MSDA_ERR_WORKSPACE, "this forward needs %zu bytes of workspace, got %zu%s",
                 ws_need, workspace_bytes, workspace ? "" : " (NULL)");
   if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const auto dt = kernel_dtype(dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t step = batches_per_launch(c);
   for (int64_t b0 = 0; b0 < c.B; b0 += step) {
@@ -277,8 +284,8 @@ msda_status backward_setup(const msda_dims *dims, msda_dtype dtype, msda_dtype a
                            msda_scatter scatter, const int64_t *shapes_host, BackwardSetup *su) {
   MSDA_TRY(check_dims(dims, dtype, &su->c));
   const Checked &c = su->c;
-  if (accum_dtype != MSDA_FP32 && accum_dtype != MSDA_BF16)
-    return fail(MSDA_ERR_UNSUPPORTED, "accum_dtype %d is not FP32 (0) or BF16 (1)",
+  if (accum_dtype != MSDA_FP32 && accum_dtype != MSDA_BF16 && accum_dtype != MSDA_FP16)
+    return fail(MSDA_ERR_UNSUPPORTED, "accum_dtype %d is not FP32 (0), BF16 (1) or FP16 (2)",
                 (int)accum_dtype);
   if (scatter != MSDA_SCATTER_BINNED && scatter != MSDA_SCATTER_ATOMIC)
     return fail(MSDA_ERR_UNSUPPORTED, "scatter %d is not BINNED (0) or ATOMIC (1)", (int)scatter);
@@ -297,9 +304,11 @@ msda_status backward_setup(const msda_dims *dims, msda_dtype dtype, msda_dtype a
       su->ws_need = msda::binned_workspace_bytes(su->plan);
     }
   } else {
-    if (dtype == MSDA_FP32 && accum_dtype != MSDA_FP32)
-      return fail(MSDA_ERR_UNSUPPORTED, "FP32 data needs an FP32 accumulator");
-    su->use_ws = dtype == MSDA_BF16 && accum_dtype == MSDA_FP32 && su->work;
+    if (accum_dtype != MSDA_FP32 && accum_dtype != dtype)
+      return fail(MSDA_ERR_UNSUPPORTED,
+                  "the atomic scatter accumulates in FP32 or in the data type (dtype %d, "
+                  "accum_dtype %d)", (int)dtype, (int)accum_dtype);
+    su->use_ws = dtype != MSDA_FP32 && accum_dtype == MSDA_FP32 && su->work;
     su->ws_need = su->use_ws ? (size_t)c.value_elems * 4 : 0;
   }
   return MSDA_OK;
@@ -319,7 +328,7 @@ msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const 
     e = msda::launch_zero(grad_value, (size_t)(c.value_elems * c.elt), s);
     return e == hipSuccess ? MSDA_OK : hip_fail(e, "grad_value zero-fill launch");
   }
-  const auto dt = c.elt == 4 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const auto dt = kernel_dtype(c.dtype);
   if (su.binned) {
     msda::BinArgs a{};
     a.value = value;
@@ -343,7 +352,7 @@ msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const 
     e = msda::launch_zero(workspace, (size_t)c.value_elems * 4, s);
     if (e != hipSuccess) return hip_fail(e, "workspace zero-fill launch");
   }
-  const auto acc = accum_dtype == MSDA_FP32 ? msda::Accum::F32 : msda::Accum::BF16;
+  const auto acc = accum_dtype == MSDA_FP32 ? msda::Accum::F32 : msda::Accum::PACKED;
   const int64_t acc_elt = accum_dtype == MSDA_FP32 ? 4 : 2;
   char *acc_base = static_cast<char *>(use_ws ? workspace : grad_value);
   const int64_t step = batches_per_launch(c);
@@ -360,8 +369,8 @@ msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const 
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
   if (use_ws) {
-    e = msda::launch_cast_f32_to_bf16(static_cast<const float *>(workspace), grad_value,
-                                      (size_t)c.value_elems, s);
+    e = msda::launch_cast_f32_to_half(static_cast<const float *>(workspace), grad_value,
+                                      (size_t)c.value_elems, dt, s);
     if (e != hipSuccess) return hip_fail(e, "workspace cast launch");
   }
   return MSDA_OK;
@@ -464,7 +473,7 @@ msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shap
   const size_t wbytes = su.work ? softmax_weights_bytes(c) : 0;
   MSDA_TRY(workspace_check(wbytes + su.ws_need, workspace, workspace_bytes, "softmax backward"));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const auto dt = dtype == MSDA_FP32 ? msda::Dtype::F32 : msda::Dtype::BF16;
+  const auto dt = kernel_dtype(dtype);
   const int lk = (int)(c.L * c.K);
   void *weights = workspace;
   if (su.work) {

@@ -161,8 +161,8 @@ __device__ inline void load_loc(const void *loc, int64_t id, float &u, float &v)
     v = x.y;
   } else {
     const uint32_t x = reinterpret_cast<const uint32_t *>(loc)[id];
-    u = __uint_as_float(x << 16);
-    v = __uint_as_float(x & 0xffff0000u);
+    u = Half<T>::lo(x);
+    v = Half<T>::hi(x);
   }
 }
 
@@ -585,8 +585,8 @@ __device__ inline void load_vec(const void *base, int64_t e, float (&o)[VEC]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      o[2 * k] = __uint_as_float(w[k] << 16);
-      o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      o[2 * k] = Half<T>::lo(w[k]);
+      o[2 * k + 1] = Half<T>::hi(w[k]);
     }
   } else {
 #pragma unroll
@@ -1293,7 +1293,12 @@ BinScratch carve_bin_scratch(const BinPlan &p, void *workspace) {
 
 hipError_t launch_backward_binned(const BinArgs &a, Dtype dt, hipStream_t stream) {
   if (a.p.total == 0) return hipSuccess;
-  return dt == Dtype::F32 ? launch_binned_t<float>(a, stream) : launch_binned_t<bf16_t>(a, stream);
+  switch (dt) {
+    case Dtype::F32: return launch_binned_t<float>(a, stream);
+    case Dtype::BF16: return launch_binned_t<bf16_t>(a, stream);
+    case Dtype::F16: return launch_binned_t<f16_t>(a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace msda

@@ -117,6 +117,9 @@ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv &f) {
 struct bf16_t {
   uint16_t bits;
 };
+struct f16_t {  // IEEE binary16
+  uint16_t bits;
+};
 
 template <typename T>
 __device__ inline float to_float(T x);
@@ -134,6 +137,31 @@ __device__ inline uint32_t bf16_bits_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The 16-bit storage types: the fp32 value of the low and the high half of a
+// 32-bit word, and the bits of an fp32 rounded to the type (nearest even).
+template <typename T>
+struct Half;
+template <>
+struct Half<bf16_t> {
+  __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static uint32_t bits(float x) { return bf16_bits_rne(x); }
+};
+template <>
+struct Half<f16_t> {
+  __device__ static float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  // the hardware conversion rounds to nearest even (overflow to infinity)
+  __device__ static uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+};
+
+template <>
+__device__ inline float to_float<f16_t>(f16_t x) { return Half<f16_t>::lo(x.bits); }
+
 template <typename T>
 __device__ inline void store_scalar(T *p, float x);
 template <>
@@ -142,8 +170,12 @@ template <>
 __device__ inline void store_scalar<bf16_t>(bf16_t *p, float x) {
   p->bits = (uint16_t)bf16_bits_rne(x);
 }
+template <>
+__device__ inline void store_scalar<f16_t>(f16_t *p, float x) {
+  p->bits = (uint16_t)Half<f16_t>::bits(x);
+}
 
-// Two consecutive elements (p 8-byte aligned for fp32, 4-byte aligned for bf16).
+// Two consecutive elements (p 8-byte aligned for fp32, 4-byte aligned for 16-bit types).
 template <typename T>
 __device__ inline void store_pair(T *p, float x, float y);
 template <>
@@ -153,6 +185,10 @@ __device__ inline void store_pair<float>(float *p, float x, float y) {
 template <>
 __device__ inline void store_pair<bf16_t>(bf16_t *p, float x, float y) {
   *reinterpret_cast<uint32_t *>(p) = bf16_bits_rne(x) | (bf16_bits_rne(y) << 16);
+}
+template <>
+__device__ inline void store_pair<f16_t>(f16_t *p, float x, float y) {
+  *reinterpret_cast<uint32_t *>(p) = Half<f16_t>::bits(x) | (Half<f16_t>::bits(y) << 16);
 }
 
 // Unpack the 32-bit words of a row slice into fp32 channels.
@@ -171,20 +207,26 @@ __device__ inline void unpack<float, 4>(const uint32_t (&w)[4], float *o) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(w[i]);
 }
-template <int WORDS>
-__device__ inline void unpack_bf16(const uint32_t (&w)[WORDS], float *o) {
+template <typename H, int WORDS>
+__device__ inline void unpack_half(const uint32_t (&w)[WORDS], float *o) {
 #pragma unroll
   for (int i = 0; i < WORDS; ++i) {
-    o[2 * i] = __uint_as_float(w[i] << 16);
-    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    o[2 * i] = Half<H>::lo(w[i]);
+    o[2 * i + 1] = Half<H>::hi(w[i]);
   }
 }
 template <>
-__device__ inline void unpack<bf16_t, 1>(const uint32_t (&w)[1], float *o) { unpack_bf16<1>(w, o); }
+__device__ inline void unpack<bf16_t, 1>(const uint32_t (&w)[1], float *o) { unpack_half<bf16_t, 1>(w, o); }
 template <>
-__device__ inline void unpack<bf16_t, 2>(const uint32_t (&w)[2], float *o) { unpack_bf16<2>(w, o); }
+__device__ inline void unpack<bf16_t, 2>(const uint32_t (&w)[2], float *o) { unpack_half<bf16_t, 2>(w, o); }
 template <>
-__device__ inline void unpack<bf16_t, 4>(const uint32_t (&w)[4], float *o) { unpack_bf16<4>(w, o); }
+__device__ inline void unpack<bf16_t, 4>(const uint32_t (&w)[4], float *o) { unpack_half<bf16_t, 4>(w, o); }
+template <>
+__device__ inline void unpack<f16_t, 1>(const uint32_t (&w)[1], float *o) { unpack_half<f16_t, 1>(w, o); }
+template <>
+__device__ inline void unpack<f16_t, 2>(const uint32_t (&w)[2], float *o) { unpack_half<f16_t, 2>(w, o); }
+template <>
+__device__ inline void unpack<f16_t, 4>(const uint32_t (&w)[4], float *o) { unpack_half<f16_t, 4>(w, o); }
 
 // Range-checked load of WORDS dwords at byte offset `off` of a buffer.
 template <int WORDS>
@@ -242,7 +284,7 @@ __device__ inline void pack(const float *x, uint32_t (&w)[WORDS]) {
     for (int i = 0; i < WORDS; ++i) w[i] = __float_as_uint(x[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < WORDS; ++i) w[i] = bf16_bits_rne(x[2 * i]) | (bf16_bits_rne(x[2 * i + 1]) << 16);
+    for (int i = 0; i < WORDS; ++i) w[i] = Half<T>::bits(x[2 * i]) | (Half<T>::bits(x[2 * i + 1]) << 16);
   }
 }
 

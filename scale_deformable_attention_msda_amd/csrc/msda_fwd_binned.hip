@@ -55,8 +55,8 @@ __device__ inline void ld_loc(const void *loc, uint32_t s, float &u, float &v) {
     v = x.y;
   } else {
     const uint32_t x = reinterpret_cast<const uint32_t *>(loc)[s];
-    u = __uint_as_float(x << 16);
-    v = __uint_as_float(x & 0xffff0000u);
+    u = Half<T>::lo(x);
+    v = Half<T>::hi(x);
   }
 }
 
@@ -845,7 +845,12 @@ FwdScratch carve_fwd_scratch(const FwdPlan &p, void *workspace) {
 }
 
 hipError_t launch_forward_binned(const FwdArgs &fa, Dtype dt, hipStream_t stream) {
-  return dt == Dtype::F32 ? launch_binned_t<float>(fa, stream) : launch_binned_t<bf16_t>(fa, stream);
+  switch (dt) {
+    case Dtype::F32: return launch_binned_t<float>(fa, stream);
+    case Dtype::BF16: return launch_binned_t<bf16_t>(fa, stream);
+    case Dtype::F16: return launch_binned_t<f16_t>(fa, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace msda

@@ -33,6 +33,9 @@
 #include "msda_launch.h"
 
 #include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 namespace msda {
 namespace {
@@ -191,16 +194,23 @@ __device__ inline void scatter_corner(const __amdgpu_buffer_rsrc_t acc_rsrc, cha
     for (int i = 0; i < VEC; ++i)
       __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(wc * g[i], acc_rsrc, (int)(aoff + 4u * i), 0, 0);
   } else {
-    // bf16 accumulator: packed pairs, straight into grad_value through plain
-    // global atomics, so the range test is explicit here.
+    // 16-bit accumulator (the data type): packed pairs, straight into
+    // grad_value through plain global atomics, so the range test is explicit here.
     if (off >= acc_bytes) return;
     unsigned int *p = reinterpret_cast<unsigned int *>(acc_base + off + lane_off_acc);
 #pragma unroll
     for (int i = 0; i < VEC / 2; ++i) {
-      __hip_bfloat162_raw r;
-      r.x = (unsigned short)bf16_bits_rne(wc * g[2 * i]);
-      r.y = (unsigned short)bf16_bits_rne(wc * g[2 * i + 1]);
-      unsafeAtomicAdd(reinterpret_cast<__hip_bfloat162 *>(p + i), __hip_bfloat162(r));
+      const unsigned short x = (unsigned short)Half<AccT>::bits(wc * g[2 * i]);
+      const unsigned short y = (unsigned short)Half<AccT>::bits(wc * g[2 * i + 1]);
+      if constexpr (std::is_same_v<AccT, bf16_t>) {
+        __hip_bfloat162_raw r;
+        r.x = x;
+        r.y = y;
+        unsafeAtomicAdd(reinterpret_cast<__hip_bfloat162 *>(p + i), __hip_bfloat162(r));
+      } else {
+        unsafeAtomicAdd(reinterpret_cast<__half2 *>(p + i),
+                        __halves2half2(__ushort_as_half(x), __ushort_as_half(y)));
+      }
     }
   }
 }
@@ -326,14 +336,16 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4 *p, size_t n16) {
     p[i] = z;
 }
 
+// fp32 -> a 16-bit type H, eight elements per thread and step.
+template <typename H>
 __global__ __launch_bounds__(256) void cast_kernel(const float4 *src, uint4 *dst, size_t n8) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (size_t)gridDim.x * blockDim.x) {
     const float4 x = src[2 * i], y = src[2 * i + 1];
-    dst[i] = make_uint4(bf16_bits_rne(x.x) | (bf16_bits_rne(x.y) << 16),
-                        bf16_bits_rne(x.z) | (bf16_bits_rne(x.w) << 16),
-                        bf16_bits_rne(y.x) | (bf16_bits_rne(y.y) << 16),
-                        bf16_bits_rne(y.z) | (bf16_bits_rne(y.w) << 16));
+    dst[i] = make_uint4(Half<H>::bits(x.x) | (Half<H>::bits(x.y) << 16),
+                        Half<H>::bits(x.z) | (Half<H>::bits(x.w) << 16),
+                        Half<H>::bits(y.x) | (Half<H>::bits(y.y) << 16),
+                        Half<H>::bits(y.z) | (Half<H>::bits(y.w) << 16));
   }
 }
 
@@ -365,8 +377,8 @@ __device__ inline void unpack16(const uint4 &w, float (&f)[Vec16<T>::N]) {
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(u[i] << 16);
-      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      f[2 * i] = Half<T>::lo(u[i]);
+      f[2 * i + 1] = Half<T>::hi(u[i]);
     }
   }
 }
@@ -379,7 +391,7 @@ __device__ inline uint4 pack16(const float (&f)[Vec16<T>::N]) {
     for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(f[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = bf16_bits_rne(f[2 * i]) | (bf16_bits_rne(f[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) u[i] = Half<T>::bits(f[2 * i]) | (Half<T>::bits(f[2 * i + 1]) << 16);
   }
   return make_uint4(u[0], u[1], u[2], u[3]);
 }
@@ -599,41 +611,61 @@ hipError_t bwd_dispatch_d(const LaunchArgs &a, hipStream_t s) {
 
 hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream, bool softmax) {
   if (a.nb * a.Q * a.M == 0) return hipSuccess;
-  return dt == Dtype::F32 ? fwd_dispatch_d<float>(a, softmax, stream)
-                          : fwd_dispatch_d<bf16_t>(a, softmax, stream);
+  switch (dt) {
+    case Dtype::F32: return fwd_dispatch_d<float>(a, softmax, stream);
+    case Dtype::BF16: return fwd_dispatch_d<bf16_t>(a, softmax, stream);
+    case Dtype::F16: return fwd_dispatch_d<f16_t>(a, softmax, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_backward(const LaunchArgs &a, Dtype dt, Accum acc, hipStream_t stream) {
   if (a.nb * a.Q * a.M == 0) return hipSuccess;
-  if (dt == Dtype::F32) return bwd_dispatch_d<float, float>(a, stream);
-  if (acc == Accum::F32) return bwd_dispatch_d<bf16_t, float>(a, stream);
-  return bwd_dispatch_d<bf16_t, bf16_t>(a, stream);
+  switch (dt) {
+    case Dtype::F32: return bwd_dispatch_d<float, float>(a, stream);
+    case Dtype::BF16:
+      return acc == Accum::F32 ? bwd_dispatch_d<bf16_t, float>(a, stream)
+                               : bwd_dispatch_d<bf16_t, bf16_t>(a, stream);
+    case Dtype::F16:
+      return acc == Accum::F32 ? bwd_dispatch_d<f16_t, float>(a, stream)
+                               : bwd_dispatch_d<f16_t, f16_t>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int LKMAX>
+void enqueue_softmax_rows_t(const void *logits, void *weights, const RowPass &p, int64_t blocks,
+                            size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((softmax_rows_kernel<T, LKMAX>), dim3((unsigned)blocks), dim3(kRowThreads),
+                     lds, stream, static_cast<const T *>(logits), static_cast<T *>(weights), p);
 }
 
 template <int LKMAX>
 void enqueue_softmax_rows(const void *logits, void *weights, const RowPass &p, int64_t blocks,
                           size_t lds, Dtype dt, hipStream_t stream) {
-  if (dt == Dtype::F32)
-    hipLaunchKernelGGL((softmax_rows_kernel<float, LKMAX>), dim3((unsigned)blocks),
-                       dim3(kRowThreads), lds, stream, static_cast<const float *>(logits),
-                       static_cast<float *>(weights), p);
-  else
-    hipLaunchKernelGGL((softmax_rows_kernel<bf16_t, LKMAX>), dim3((unsigned)blocks),
-                       dim3(kRowThreads), lds, stream, static_cast<const bf16_t *>(logits),
-                       static_cast<bf16_t *>(weights), p);
+  switch (dt) {
+    case Dtype::F32: enqueue_softmax_rows_t<float, LKMAX>(logits, weights, p, blocks, lds, stream); break;
+    case Dtype::BF16: enqueue_softmax_rows_t<bf16_t, LKMAX>(logits, weights, p, blocks, lds, stream); break;
+    case Dtype::F16: enqueue_softmax_rows_t<f16_t, LKMAX>(logits, weights, p, blocks, lds, stream); break;
+  }
+}
+
+template <typename T, int LKMAX>
+void enqueue_softmax_grad_rows_t(const void *logits, void *grad, const RowPass &p, int64_t blocks,
+                                 size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((softmax_grad_rows_kernel<T, LKMAX>), dim3((unsigned)blocks),
+                     dim3(kRowThreads), lds, stream, static_cast<const T *>(logits),
+                     static_cast<T *>(grad), p);
 }
 
 template <int LKMAX>
 void enqueue_softmax_grad_rows(const void *logits, void *grad, const RowPass &p, int64_t blocks,
                                size_t lds, Dtype dt, hipStream_t stream) {
-  if (dt == Dtype::F32)
-    hipLaunchKernelGGL((softmax_grad_rows_kernel<float, LKMAX>), dim3((unsigned)blocks),
-                       dim3(kRowThreads), lds, stream, static_cast<const float *>(logits),
-                       static_cast<float *>(grad), p);
-  else
-    hipLaunchKernelGGL((softmax_grad_rows_kernel<bf16_t, LKMAX>), dim3((unsigned)blocks),
-                       dim3(kRowThreads), lds, stream, static_cast<const bf16_t *>(logits),
-                       static_cast<bf16_t *>(grad), p);
+  switch (dt) {
+    case Dtype::F32: enqueue_softmax_grad_rows_t<float, LKMAX>(logits, grad, p, blocks, lds, stream); break;
+    case Dtype::BF16: enqueue_softmax_grad_rows_t<bf16_t, LKMAX>(logits, grad, p, blocks, lds, stream); break;
+    case Dtype::F16: enqueue_softmax_grad_rows_t<f16_t, LKMAX>(logits, grad, p, blocks, lds, stream); break;
+  }
 }
 
 hipError_t launch_softmax_rows(const void *logits, void *weights, int64_t n_rows, int lk,
@@ -683,13 +715,19 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, size_t n, hipStream_t stream) {
+hipError_t launch_cast_f32_to_half(const float *src, void *dst, size_t n, Dtype dt,
+                                   hipStream_t stream) {
   const size_t n8 = n / 8;
   if (n8 == 0) return hipSuccess;
+  if (dt == Dtype::F32) return hipErrorInvalidValue;
   const size_t blocks = std::min<size_t>((n8 + 255) / 256, 4096);
   prof_begin(stream, "cast");
-  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const float4 *>(src), reinterpret_cast<uint4 *>(dst), n8);
+  if (dt == Dtype::BF16)
+    hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(src), reinterpret_cast<uint4 *>(dst), n8);
+  else
+    hipLaunchKernelGGL(cast_kernel<f16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(src), reinterpret_cast<uint4 *>(dst), n8);
   prof_end(stream, "cast");
   return hipGetLastError();
 }

@@ -148,8 +148,10 @@ struct FwdArgs {
 void prof_begin(hipStream_t stream, const char *name);
 void prof_end(hipStream_t stream, const char *name);
 
-enum class Dtype { F32, BF16 };
-enum class Accum { F32, BF16 };
+enum class Dtype { F32, BF16, F16 };
+// grad_value accumulator of the atomic scatter: fp32, or packed 16-bit atomics
+// in the data type (BF16 or F16 data only)
+enum class Accum { F32, PACKED };
 
 // softmax: a.attn holds raw logits, normalised per head-query inside the kernel
 hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream, bool softmax = false);
@@ -178,6 +180,7 @@ bool make_fwd_plan(FwdPlan &p, int64_t nb, int64_t Q, int64_t S, int M, int D, i
 size_t fwd_workspace_bytes(const FwdPlan &p);
 FwdScratch carve_fwd_scratch(const FwdPlan &p, void *workspace);
 hipError_t launch_forward_binned(const FwdArgs &a, Dtype dt, hipStream_t stream);
-hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, size_t n, hipStream_t stream);
+hipError_t launch_cast_f32_to_half(const float *src, void *dst, size_t n, Dtype dt,
+                                   hipStream_t stream);
 
 }  // namespace msda

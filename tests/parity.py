@@ -5,6 +5,8 @@ Tolerances are the ones stated for this operator:
   backward fp32  rtol 1e-4, atol 1e-5  (grad_value order is set by atomics)
   bf16 paths     rtol 2e-2, atol 2e-2  (against the fp64 oracle on the same
                                         bf16-exact inputs)
+  fp16 paths     rtol 2.5e-3, atol 2.5e-3  (the bf16 tolerance scaled by the
+                                        ratio of unit roundoffs, 2^-11 / 2^-8)
 An element passes when |gpu - oracle| <= atol + rtol * |oracle|.
 """
 from __future__ import annotations
@@ -20,6 +22,9 @@ import scale_deformable_attention_msda_amd as msda
 TOL_FWD_FP32 = (1e-5, 1e-6)
 TOL_BWD_FP32 = (1e-4, 1e-5)
 TOL_BF16 = (2e-2, 2e-2)
+TOL_FP16 = (2.5e-3, 2.5e-3)
+TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
+HALF_TOL = {"bf16": TOL_BF16, "fp16": TOL_FP16}
 
 FLOAT_KEYS = ("value", "sampling_locations", "attention_weights", "attention_logits", "grad_out")
 
@@ -30,7 +35,7 @@ def say(msg: str):
 
 
 def upload(x: dict, device="cuda") -> dict:
-    dt = torch.float32 if x["dtype"] == "fp32" else torch.bfloat16
+    dt = TORCH_DTYPE[x["dtype"]]
     t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(device).to(dt)
          for k in FLOAT_KEYS if k in x}
     t["spatial_shapes"] = torch.from_numpy(x["spatial_shapes"]).to(device)

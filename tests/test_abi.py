@@ -91,6 +91,7 @@ def test_binned_forward_workspace_sizes(lib):
     need = fwd_ws(lib, dims(**ENCODER), 0, PYRAMID)
     assert 8 * 2 * 8 * 22223 <= need < 64 << 20
     assert fwd_ws(lib, dims(**ENCODER), 1, PYRAMID) > 0                       # bf16, 64-byte rows
+    assert fwd_ws(lib, dims(**ENCODER), 2, PYRAMID) > 0                       # fp16, 64-byte rows
     assert fwd_ws(lib, dims(**ENCODER), 0, None) == SIZE_MAX                  # needs host shapes
     assert "spatial_shapes_host" in msda.msda_last_error()
     for bad in (dict(Q=300), dict(D=8), dict(K=9)):  # few queries, 32-byte rows, K > 8
@@ -127,7 +128,7 @@ def test_forward_rejects_bad_pointers_and_dtype(lib):
     assert fwd(lib, dims(), out=None) == 1
     assert fwd(lib, dims(), loc=FAKE + 4) == 4
     assert fwd(lib, dims(), value=FAKE + 8) == 4
-    assert fwd(lib, dims(), dtype=2) == 3
+    assert fwd(lib, dims(), dtype=3) == 3
     assert "dtype" in msda.msda_last_error()
 
 
@@ -200,7 +201,7 @@ def test_softmax_forward_rejections(lib):
     assert fwd_softmax(lib, dims(), logits=None) == 1
     assert "attention_logits" in msda.msda_last_error()
     assert fwd_softmax(lib, dims(), logits=FAKE + 4) == 4
-    assert fwd_softmax(lib, dims(), dtype=2) == 3
+    assert fwd_softmax(lib, dims(), dtype=3) == 3
     assert fwd_softmax(lib, dims(Q=0), logits=None, out=None) == 0
     assert msda.msda_last_error() == ""
 
@@ -233,3 +234,16 @@ def test_softmax_backward_rejections(lib):
     assert bwd_softmax(lib, d, scatter=0, ws=FAKE, ws_bytes=need) == 1
     assert bwd_softmax(lib, d, acc=1) == 3
     assert bwd_softmax(lib, dims(D=12)) == 3
+
+
+def test_fp16_accumulators(lib):
+    # FP16 data: the atomic scatter accumulates in FP32 (workspace) or FP16 (packed atomics)
+    assert ws_bytes(lib, dims(), 2, 0, scatter=1) == 1 * 80 * 2 * 8 * 4
+    assert ws_bytes(lib, dims(), 2, 2, scatter=1) == 0
+    assert ws_bytes(lib, dims(), 2, 1, scatter=1) == SIZE_MAX      # BF16 accumulator, FP16 data
+    assert "accumulates in FP32 or in the data type" in msda.msda_last_error()
+    assert ws_bytes(lib, dims(), 1, 2, scatter=1) == SIZE_MAX      # FP16 accumulator, BF16 data
+    assert bwd(lib, dims(), dtype=2, acc=0) == 5                   # needs the fp32 workspace
+    assert bwd(lib, dims(), dtype=2, acc=2, scatter=0, shapes_host=SHAPES) == 3  # binned: fp32
+    assert ws_bytes(lib, dims(), 2, 0, scatter=0, shapes_host=SHAPES) > 0
+    assert bwd(lib, dims(), dtype=0, acc=2) == 3                   # FP32 data, FP16 accumulator

@@ -9,7 +9,7 @@ import torch
 
 import parity
 import workloads
-from parity import TOL_BF16, TOL_BWD_FP32, TOL_FWD_FP32, check, say
+from parity import HALF_TOL, TORCH_DTYPE, TOL_BWD_FP32, TOL_FWD_FP32, check, say
 
 import scale_deformable_attention_msda_amd as msda
 
@@ -23,21 +23,22 @@ def _gpu():
     msda.load_library()  # raises if the library is not built
 
 
-def gate(x, g, o, accum_bf16=False):
+def gate(x, g, o, accum_packed=False):
     if x["dtype"] == "fp32":
         check("out", g["out"], o["out"], *TOL_FWD_FP32)
         check("grad_value", g["grad_value"], o["grad_value"], *TOL_BWD_FP32)
         check("grad_loc", g["grad_loc"], o["grad_loc"], *TOL_BWD_FP32)
         check("grad_attn", g["grad_attn"], o["grad_attn"], *TOL_BWD_FP32)
     else:
-        check("out", g["out"], o["out"], *TOL_BF16)
-        check("grad_loc", g["grad_loc"], o["grad_loc"], *TOL_BF16)
-        check("grad_attn", g["grad_attn"], o["grad_attn"], *TOL_BF16)
-        if accum_bf16:
-            say(f"  grad_value (packed-bf16 accumulator, reported): "
+        tol = HALF_TOL[x["dtype"]]
+        check("out", g["out"], o["out"], *tol)
+        check("grad_loc", g["grad_loc"], o["grad_loc"], *tol)
+        check("grad_attn", g["grad_attn"], o["grad_attn"], *tol)
+        if accum_packed:
+            say(f"  grad_value (packed {x['dtype']} accumulator, reported): "
                 f"{parity.error_stats(g['grad_value'], o['grad_value'])}")
         else:
-            check("grad_value", g["grad_value"], o["grad_value"], *TOL_BF16)
+            check("grad_value", g["grad_value"], o["grad_value"], *tol)
 
 
 _CACHE = {}
@@ -61,9 +62,10 @@ def test_workload(wid, scatter):
     x, o = workload_case(wid)
     g = parity.run_gpu(x, scatter=scatter)
     gate(x, g, o)
-    if wl.dtype == "bf16" and scatter == "atomic":
-        say("  accumulator bf16:")
-        gate(x, parity.run_gpu(x, accum=torch.bfloat16, scatter="atomic"), o, accum_bf16=True)
+    if wl.dtype != "fp32" and scatter == "atomic":
+        say(f"  accumulator {wl.dtype}:")
+        gate(x, parity.run_gpu(x, accum=TORCH_DTYPE[wl.dtype], scatter="atomic"), o,
+             accum_packed=True)
 
 
 EDGE = {
@@ -76,6 +78,10 @@ EDGE = {
     "d8_bf16": workloads.custom(2, 50, 4, 8, ((9, 11), (5, 6)), 4, dtype="bf16"),
     "d16_bf16": workloads.custom(2, 50, 4, 16, ((9, 11), (5, 6)), 4, dtype="bf16"),
     "d64_bf16": workloads.custom(2, 50, 4, 64, ((9, 11), (5, 6)), 4, dtype="bf16"),
+    "ragged_fp16": workloads.custom(3, 37, 3, 32, ((7, 9), (4, 5), (1, 3)), 3, dtype="fp16"),
+    "d8_fp16": workloads.custom(2, 50, 4, 8, ((9, 11), (5, 6)), 4, dtype="fp16"),
+    "d16_fp16": workloads.custom(2, 50, 4, 16, ((9, 11), (5, 6)), 4, dtype="fp16"),
+    "d64_fp16": workloads.custom(2, 50, 4, 64, ((9, 11), (5, 6)), 4, dtype="fp16"),
     "one_level_one_point": workloads.custom(2, 33, 5, 32, ((6, 10),), 1),
     "max_lk_16_levels": workloads.custom(1, 21, 3, 16, tuple((2 + i % 5, 3 + i % 4) for i in range(16)), 4),
     "max_lk_32_points": workloads.custom(1, 21, 3, 32, ((8, 8), (4, 4)), 32),
@@ -93,8 +99,9 @@ def test_edge(name, scatter):
     x = workloads.make_inputs(wl, seed=zlib.crc32(name.encode()) % 100000)
     o = parity.run_oracle(x)
     gate(x, parity.run_gpu(x, scatter=scatter), o)
-    if wl.dtype == "bf16" and scatter == "atomic":
-        gate(x, parity.run_gpu(x, accum=torch.bfloat16, scatter="atomic"), o, accum_bf16=True)
+    if wl.dtype != "fp32" and scatter == "atomic":
+        gate(x, parity.run_gpu(x, accum=TORCH_DTYPE[wl.dtype], scatter="atomic"), o,
+             accum_packed=True)
 
 
 def special_locations():
@@ -150,7 +157,7 @@ def test_empty_queries_zero_grad_value(scatter):
     assert torch.count_nonzero(gv).item() == 0
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("scatter", ["binned", "atomic"])
 def test_outputs_are_overwritten_and_deterministic(dtype, scatter):
     say(f"[parity] overwrite + determinism {dtype} scatter={scatter}")
@@ -179,7 +186,7 @@ def test_outputs_are_overwritten_and_deterministic(dtype, scatter):
 def uses_binned_forward(x) -> bool:
     wl = x["workload"]
     d = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
-    dt = msda.MSDA_FP32 if x["dtype"] == "fp32" else msda.MSDA_BF16
+    dt = msda._DTYPES[TORCH_DTYPE[x["dtype"]]]
     try:
         return msda.msda_forward_binned_workspace_bytes(d, dt, x["spatial_shapes"]) > 0
     except ValueError:
@@ -201,7 +208,7 @@ def oracle_forward(x):
 
 
 def gate_forward(x, out, want):
-    tol = TOL_FWD_FP32 if x["dtype"] == "fp32" else TOL_BF16
+    tol = TOL_FWD_FP32 if x["dtype"] == "fp32" else HALF_TOL[x["dtype"]]
     check("out", out.double().cpu().numpy(), want, *tol)
 
 
@@ -224,6 +231,7 @@ SIX_LEVELS = ((24, 32), (12, 16), (6, 8), (3, 4), (2, 2), (1, 1))
 BINNED_FWD = {
     "enc_fp32": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, ref="pixel_centres"),
     "enc_bf16": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, dtype="bf16", ref="pixel_centres"),
+    "enc_fp16": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, dtype="fp16", ref="pixel_centres"),
     "enc_wide_offsets": workloads.custom(2, SMALL_S, 4, 32, SMALL_PYR, 4, ref="pixel_centres",
                                          sigma_px=7.0),
     "enc_k8": workloads.custom(1, SMALL_S, 4, 32, SMALL_PYR, 8, ref="pixel_centres"),
@@ -283,7 +291,8 @@ def test_side_stream():
 # ---------------------------------------------------------------- softmax method
 
 def gate_softmax(x, g, o):
-    fwd, bwd = (TOL_FWD_FP32, TOL_BWD_FP32) if x["dtype"] == "fp32" else (TOL_BF16, TOL_BF16)
+    fwd, bwd = ((TOL_FWD_FP32, TOL_BWD_FP32) if x["dtype"] == "fp32"
+                else (HALF_TOL[x["dtype"]], HALF_TOL[x["dtype"]]))
     check("out", g["out"], o["out"], *fwd)
     for k in ("grad_value", "grad_loc", "grad_logits"):
         check(k, g[k], o[k], *bwd)
@@ -299,8 +308,8 @@ def test_workload_softmax(wid, scatter):
     gate_softmax(x, parity.run_gpu_softmax(x, scatter=scatter), parity.run_oracle_softmax(x))
 
 
-SOFTMAX_EDGE = ("ragged_fp32", "ragged_bf16", "one_level_one_point", "max_lk_16_levels",
-                "max_lk_32_points", "d64_bf16", "d8_fp32")
+SOFTMAX_EDGE = ("ragged_fp32", "ragged_bf16", "ragged_fp16", "one_level_one_point",
+                "max_lk_16_levels", "max_lk_32_points", "d64_bf16", "d8_fp32")
 
 
 @pytest.mark.parametrize("name", SOFTMAX_EDGE)
@@ -387,3 +396,29 @@ def test_query_order_permutes_outputs(kind):
     check("grad_value", np_(gv_p), np_(gv), *TOL_BWD_FP32)
     check("grad_loc", np_(gl_p), np_(gl[:, perm]), *TOL_BWD_FP32)
     check("grad_attn", np_(ga_p), np_(ga[:, perm]), *TOL_BWD_FP32)
+
+
+# ---------------------------------------------------------------- fp16 at full size
+
+# Workload 5: the Mask2Former configuration of workload 3 (B=2, Q=S=21504, M=8,
+# D=32, three levels 128x128 / 64x64 / 32x32, K=4, pixel-centre references) in
+# IEEE fp16.
+M2F_FP16 = workloads.WORKLOADS[5]
+
+
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_fp16_mask2former_size(scatter):
+    say(f"[parity] fp16, Mask2Former sizes, scatter={scatter}")
+    x = workloads.make_inputs(5)
+    o = parity.run_oracle(x)
+    gate(x, parity.run_gpu(x, scatter=scatter), o)
+    gate_forward(x, forward_only(x, "binned"), o["out"])
+    if scatter == "atomic":
+        say("  accumulator fp16:")
+        gate(x, parity.run_gpu(x, accum=torch.float16, scatter="atomic"), o, accum_packed=True)
+
+
+def test_fp16_softmax_mask2former_size():
+    say("[parity] fp16 softmax method, Mask2Former sizes")
+    x = workloads.make_inputs(5)
+    gate_softmax(x, parity.run_gpu_softmax(x), parity.run_oracle_softmax(x))

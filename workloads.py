@@ -13,6 +13,10 @@ the msda-triton course, "The equation, term by term"):
   2   encoder      2  S=22223   8  32  100x167, 50x84, 25x42, 13x21       4  fp32   N(0, 2 px)
   3   mask2former  2  S=21504   8  32  128x128, 64x64, 32x32              4  bf16   N(0, 2 px)
   4   contention   1  S=22223   8  32  100x167, 50x84, 25x42, 13x21       8  bf16   N(0, 0.5 px)
+  5   m2f_fp16     2  S=21504   8  32  128x128, 64x64, 32x32              4  fp16   N(0, 2 px)
+
+Workload 5 is workload 3 in IEEE binary16, the other half-precision type the
+DeformOps page names (introduction: bfloat16 and float16 throughout).
 
 The 4-level pyramid is that of an ~800x1333 detection input at strides 8, 16,
 32 and 64 (chapter 1, "The problem: attention over images is quadratic"); the
@@ -34,9 +38,10 @@ this order:
      (less their per-row maximum) are kept as attention_logits for the
      "softmax" method;
   5. grad_out ~ N(0, 1), shape (B, Q, M*D).
-For bf16 workloads every floating array is rounded to bf16 (round to nearest
-even) and returned as float32 holding bf16-exact values, so that both the GPU
-path (which converts exactly to bf16) and the oracle (which upcasts exactly to
+For bf16 (fp16) workloads every floating array is rounded to bf16 (IEEE
+binary16), round to nearest even, and returned as float32 holding exactly
+representable values, so that both the GPU path (which converts exactly) and
+the oracle (which upcasts exactly to
 fp64) see identical numbers.
 """
 from __future__ import annotations
@@ -58,7 +63,7 @@ class Workload:
     D: int
     shapes: tuple
     K: int
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32", "bf16" or "fp16"
     ref: str            # "uniform" or "pixel_centres"
     sigma_px: float
     Q: int | None = None  # None: one query per pyramid pixel (Q = S)
@@ -88,6 +93,8 @@ WORKLOADS = {
                 ref="pixel_centres", sigma_px=2.0),
     4: Workload("contention", B=1, M=8, D=32, shapes=PYRAMID_DETR, K=8, dtype="bf16",
                 ref="pixel_centres", sigma_px=0.5),
+    5: Workload("m2f_fp16", B=2, M=8, D=32, shapes=PYRAMID_M2F, K=4, dtype="fp16",
+                ref="pixel_centres", sigma_px=2.0),
 }
 
 
@@ -216,6 +223,9 @@ def make_inputs(wl: Workload | int, seed: int | None = None, with_grad: bool = T
         arrays["grad_out"] = grad_out
     if wl.dtype == "bf16":
         arrays = {k: round_to_bf16(v) for k, v in arrays.items()}
+    elif wl.dtype == "fp16":
+        # numpy's float32 -> float16 conversion rounds to nearest even
+        arrays = {k: v.astype(np.float16).astype(np.float32) for k, v in arrays.items()}
     elif wl.dtype != "fp32":
         raise ValueError(f"unsupported dtype {wl.dtype!r}")
     arrays["spatial_shapes"] = shapes
