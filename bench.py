@@ -530,6 +530,34 @@ def main(argv=None) -> int:
                              "of 20 forward + backward steps over the rotated batches")
             extras["query_order"] = orders
 
+        # the atomic scatter (the pages' design) against what device-scope fp32
+        # atomics reach on this machine: torch's index_add_ of whole 128-byte rows
+        # (32 lanes x 4 B per row, the best pattern measured)
+        log("[bench] atomic scatter and the atomic-add ceiling")
+        adds = bm["samples"] * 4 * wl.D
+        t0 = batches[0]
+        gv_a = torch.empty_like(t0["value"])
+
+        def bwd_atomic(t):
+            msda.msda_backward(*ops(t), t["grad_out"], grad_value=gv_a, grad_loc=gl, grad_attn=ga,
+                               scatter="atomic", stream=stream)
+
+        atomic_us = call_us(bwd_atomic, n=5)
+        rows = torch.zeros(2 ** 18, 32, device=dev)
+        idx = torch.randint(0, rows.shape[0], (2 ** 22,), device=dev)
+        src = torch.ones(idx.numel(), 32, device=dev)
+        ceil_us = call_us(lambda t: rows.index_add_(0, idx, src), n=5)
+        extras["atomic_scatter"] = {
+            "bwd_us": atomic_us,
+            "element_adds": adds,
+            "adds_per_s": round(adds / (atomic_us * 1e-6), 1),
+            "ceiling_adds_per_s": round(src.numel() / (ceil_us * 1e-6), 1),
+            "frac_of_ceiling": round(adds / (atomic_us * 1e-6) / (src.numel() / (ceil_us * 1e-6)), 4),
+            "how": "msda_backward with the atomic scatter (fp32 atomics into grad_value), median "
+                   "of 5 calls; ceiling = torch index_add_ of 2^22 random 32-float rows into "
+                   "2^18 rows, median of 5"}
+        del rows, idx, src, gv_a
+
         log("[bench] layer-level forward + backward against the grid_sample composition")
         extras["layer"] = layer_comparison(wl, dev)
 
@@ -553,6 +581,7 @@ def main(argv=None) -> int:
     dom["us_timed_region"] = round(dom_us, 3)
     achieved = dom["alg_bytes"] / (dom_us * 1e-6) / 1e9
     traffic = read_traffic(args.traffic_file, wl.name, args.scatter, dom_name)
+    traffic_gbps = round(traffic / (dom_us * 1e-6) / 1e9, 1) if traffic else None
     step_bytes = bm["fwd"] + (bm["bwd_atomic"] if args.scatter == "atomic" else bm["bin_tile"])
     res = {
         "metric": METRIC,
@@ -585,7 +614,8 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "kernel": dom_name, "kernel_us": round(dom_us, 3),
                      "launches": len(dom_ms), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_gbps": traffic_gbps},
     }
     res.update(extras)
     if "achievable" in extras:
