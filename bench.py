@@ -278,6 +278,65 @@ def layer_comparison(wl: workloads.Workload, dev, steps: int = 5) -> dict:
     return res
 
 
+def graph_comparison(dev, wid: int = 1, n: int = 50) -> dict:
+    """One forward + backward step at a small configuration (launch-bound): n steps
+    enqueued back to back from Python, against n replays of the same step captured
+    once in a HIP graph (torch.cuda.CUDAGraph).  Microseconds per step."""
+    import torch
+
+    import scale_deformable_attention_msda_amd as msda
+
+    wl = workloads.WORKLOADS[wid]
+    x = workloads.make_inputs(wid)
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
+    t = {k: torch.from_numpy(x[k]).to(dev, dt) for k in
+         ("value", "sampling_locations", "attention_weights", "grad_out")}
+    shapes = torch.from_numpy(x["spatial_shapes"]).to(dev)
+    starts = torch.from_numpy(x["level_start_index"]).to(dev)
+    host = x["spatial_shapes"]
+    ops = (t["value"], shapes, starts, t["sampling_locations"], t["attention_weights"])
+    out, gv = torch.empty_like(t["grad_out"]), torch.empty_like(t["value"])
+    gl, ga = torch.empty_like(t["sampling_locations"]), torch.empty_like(t["attention_weights"])
+    dims = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
+    need = msda.msda_backward_workspace_bytes(dims, msda._DTYPES[dt], msda.MSDA_FP32,
+                                              msda.MSDA_SCATTER_BINNED, host)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        msda.msda_forward(*ops, out=out)
+        msda.msda_backward(*ops, t["grad_out"], grad_value=gv, grad_loc=gl, grad_attn=ga,
+                           spatial_shapes_host=host, workspace=ws)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    eager_us = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    graph_us = timed(g.replay)
+    return {"workload": f"{wl.name}: B={wl.B} Q={wl.num_queries} S={wl.S} M={wl.M} D={wl.D} "
+                        f"L={wl.L} K={wl.K} {wl.dtype}",
+            "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+            "how": f"{n} forward + binned backward steps enqueued back to back, eager from "
+                   "Python against replays of one captured step"}
+
+
 def percentiles(xs) -> dict:
     a = np.sort(np.asarray(xs, dtype=np.float64))
     return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.percentile(a, 50)), 3),
@@ -557,6 +616,9 @@ def main(argv=None) -> int:
                    "of 5 calls; ceiling = torch index_add_ of 2^22 random 32-float rows into "
                    "2^18 rows, median of 5"}
         del rows, idx, src, gv_a
+
+        log("[bench] HIP graph replay of a small (launch-bound) step")
+        extras["graph"] = {"tiny": graph_comparison(dev, 0), "decoder": graph_comparison(dev, 1)}
 
         log("[bench] layer-level forward + backward against the grid_sample composition")
         extras["layer"] = layer_comparison(wl, dev)

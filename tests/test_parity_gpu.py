@@ -422,3 +422,48 @@ def test_fp16_softmax_mask2former_size():
     say("[parity] fp16 softmax method, Mask2Former sizes")
     x = workloads.make_inputs(5)
     gate_softmax(x, parity.run_gpu_softmax(x), parity.run_oracle_softmax(x))
+
+
+# ---------------------------------------------------------------- HIP graphs
+
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_graph_capture_replays_match_eager(scatter):
+    """Forward + backward captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed several times, with eager work and synchronisations between the
+    replays: every replay matches the eager call (forward, grad_loc and grad_attn
+    bit for bit; grad_value within the backward tolerance, since its additions
+    are unordered) and the oracle.  Fill kernels, not memsets, clear the
+    accumulators and counters, so nothing in the graph is a memset node."""
+    wl = workloads.WORKLOADS[1]
+    say(f"[parity] graph capture: workload 1 {wl.name} scatter={scatter}")
+    x, o = workload_case(1)
+    t = parity.upload(x)
+    ops = parity.operands(t)
+    host = x["spatial_shapes"]
+    out_e = msda.msda_forward(*ops)
+    gv_e, gl_e, ga_e = msda.msda_backward(*ops, t["grad_out"], scatter=scatter,
+                                          spatial_shapes_host=host)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the allocator outside the capture
+        msda.msda_backward(*ops, t["grad_out"], scatter=scatter, spatial_shapes_host=host)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_g = msda.msda_forward(*ops)
+        gv_g, gl_g, ga_g = msda.msda_backward(*ops, t["grad_out"], scatter=scatter,
+                                              spatial_shapes_host=host)
+    for rep in range(3):
+        for v in (out_g, gv_g, gl_g, ga_g):
+            v.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep}: forward differs from eager"
+        assert torch.equal(gl_g, gl_e) and torch.equal(ga_g, ga_e), f"replay {rep}"
+        np_ = lambda v: v.double().cpu().numpy()
+        check(f"replay {rep} grad_value vs eager", np_(gv_g), np_(gv_e), *TOL_BWD_FP32)
+    gate(x, {k: v.double().cpu().numpy() for k, v in
+             dict(out=out_g, grad_value=gv_g, grad_loc=gl_g, grad_attn=ga_g).items()}, o)
