@@ -337,6 +337,16 @@ def graph_comparison(dev, wid: int = 1, n: int = 50) -> dict:
                    "Python against replays of one captured step"}
 
 
+def need_f_plan(wl, dims, dcode, shapes_host) -> bool:
+    """Whether the query-binned forward plans these sizes."""
+    import scale_deformable_attention_msda_amd as msda
+
+    try:
+        return msda.msda_forward_binned_workspace_bytes(dims, dcode, shapes_host) > 0
+    except ValueError:
+        return False
+
+
 def percentiles(xs) -> dict:
     a = np.sort(np.asarray(xs, dtype=np.float64))
     return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.percentile(a, 50)), 3),
@@ -354,6 +364,9 @@ def main(argv=None) -> int:
                     help="how the backward forms grad_value")
     ap.add_argument("--gather", default="direct", choices=["direct", "binned"],
                     help="forward schedule: msda_forward (direct gather) or msda_forward_binned")
+    ap.add_argument("--reuse-order", action="store_true",
+                    help="with --gather binned: sort once (in the warm-up) and reuse that query "
+                         "order (msda_forward_binned_reuse)")
     ap.add_argument("--method", default="default", choices=["default", "softmax"],
                     help="attention weights as given, or softmax of raw logits in the operator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -390,6 +403,9 @@ def main(argv=None) -> int:
     if args.method == "softmax" and args.gather != "direct":
         log("the softmax method runs on the direct gather only")
         return 2
+    if args.reuse_order and args.gather != "binned":
+        log("--reuse-order applies to --gather binned")
+        return 2
     msda.load_library()
     wl = workloads.WORKLOADS[args.workload]
     dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
@@ -421,8 +437,10 @@ def main(argv=None) -> int:
     need_f = (msda.msda_forward_binned_workspace_bytes(dims, dcode, shapes_host)
               if args.gather == "binned" else 0)
     # one workspace serves both calls: they run one after the other on one stream
-    need = max(need_b, need_f, need_s)
+    # (with --reuse-order the forward keeps its own, which holds the order)
+    need = max(need_b, need_s) if args.reuse_order else max(need_b, need_f, need_s)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(need_f, 1), dtype=torch.uint8, device=dev) if args.reuse_order else ws
     log(f"[bench] gather={args.gather} (workspace {need_f / 2**20:.1f} MiB), "
         f"scatter={args.scatter} (workspace {need_b / 2**20:.1f} MiB)")
 
@@ -433,9 +451,14 @@ def main(argv=None) -> int:
     def ops_softmax(t):
         return ops(t)[:4] + (t["attention_logits"],)
 
+    n_fwd_calls = [0]
+
     def fwd_plain(t):
+        # with --reuse-order, the first call sorts and every later one reuses its order
+        reuse = args.reuse_order and n_fwd_calls[0] > 0
+        n_fwd_calls[0] += 1
         msda.msda_forward(*ops(t), out=out, stream=stream, gather=args.gather,
-                          spatial_shapes_host=shapes_host, workspace=ws)
+                          spatial_shapes_host=shapes_host, workspace=ws_f, reuse_order=reuse)
 
     def bwd_plain(t):
         msda.msda_backward(*ops(t), t["grad_out"], grad_value=gv, grad_loc=gl, grad_attn=ga,
@@ -622,6 +645,27 @@ def main(argv=None) -> int:
 
         log("[bench] layer-level forward + backward against the grid_sample composition")
         extras["layer"] = layer_comparison(wl, dev)
+
+        if args.gather == "direct" and need_f_plan(wl, dims, dcode, shapes_host):
+            # the query-binned forward: sorting every call, or reusing the order that the
+            # last sorted call left (taken from another input batch)
+            log("[bench] query-binned forward, order sorted per call and reused")
+            ws_o = torch.empty(msda.msda_forward_binned_workspace_bytes(dims, dcode, shapes_host),
+                               dtype=torch.uint8, device=dev)
+
+            def fwd_binned(t, reuse):
+                msda.msda_forward(*ops(t), out=out, stream=stream, gather="binned",
+                                  spatial_shapes_host=shapes_host, workspace=ws_o,
+                                  reuse_order=reuse)
+
+            extras["binned_forward"] = {
+                "direct_us": call_us(fwd_plain),
+                "binned_us": call_us(lambda t: fwd_binned(t, False)),
+                "binned_reuse_us": call_us(lambda t: fwd_binned(t, True)),
+                "how": "median of 20 single calls over the rotated batches; binned = "
+                       "msda_forward_binned (sort + tile passes); reuse = "
+                       "msda_forward_binned_reuse on the order the last sorted call left"}
+            del ws_o
 
         if args.gather == "direct":
             extras["softmax_method"] = {

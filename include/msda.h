@@ -159,6 +159,32 @@ msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes
                                 msda_dtype dtype, const int64_t *spatial_shapes_host,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * msda_forward_binned without its sort: the tile pass walks the query order
+ * (head-queries sorted by region, cut into chunks) that an earlier
+ * msda_forward_binned call left in `workspace`, for the inputs given now.  The
+ * result is the same operator, exact for any inputs, because every point whose
+ * cell leaves its region's LDS window is gathered from global memory; only
+ * the speed depends on how well the old order fits the new locations.  That
+ * suits calls whose reference points repeat and whose offsets move little,
+ * such as an encoder layer across training steps.
+ * Precondition (not checked: the order lives in device memory): the workspace
+ * holds the order of an msda_forward_binned call with the same dims, dtype and
+ * spatial_shapes_host, and nothing has written to it since (msda_backward does
+ * not share it).  If that is violated the output is wrong, but every index
+ * read from the workspace is clamped to the plan's ranges, so no access leaves
+ * its buffer.  The call must fit one launch (one batch image of value below
+ * 2^30 bytes for all B together), else MSDA_ERR_UNSUPPORTED.  Other arguments
+ * and errors as for msda_forward_binned.
+ */
+msda_status msda_forward_binned_reuse(const void *value, const int64_t *spatial_shapes,
+                                      const int64_t *level_start_index,
+                                      const void *sampling_locations,
+                                      const void *attention_weights, void *out,
+                                      const msda_dims *dims, msda_dtype dtype,
+                                      const int64_t *spatial_shapes_host, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* How msda_backward forms grad_value. */
 typedef enum {
     /* Samples are counting-sorted by destination tile (batch, head, level,

@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.msda_forward_binned.argtypes = [vp, i64p, i64p, vp, vp, vp, dims_p, ctypes.c_int, vp, vp,
                                         ctypes.c_size_t, vp]
     lib.msda_forward_binned.restype = ctypes.c_int
+    lib.msda_forward_binned_reuse.argtypes = lib.msda_forward_binned.argtypes
+    lib.msda_forward_binned_reuse.restype = ctypes.c_int
     lib.msda_forward_binned_workspace_bytes.argtypes = [dims_p, ctypes.c_int, vp]
     lib.msda_forward_binned_workspace_bytes.restype = ctypes.c_size_t
     lib.msda_backward.argtypes = [vp, i64p, i64p, vp, vp, vp, vp, vp, vp, dims_p, ctypes.c_int,
@@ -196,17 +198,20 @@ def msda_forward_binned_workspace_bytes(dims: MsdaDims, dtype: int, spatial_shap
 
 def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
                  attention_weights, out=None, stream=None, gather="direct",
-                 spatial_shapes_host=None, workspace=None):
+                 spatial_shapes_host=None, workspace=None, reuse_order=False):
     """out[B, Q, M*D] = MSDA(...) computed by the library's forward kernels.
 
     gather: "direct" (default, msda_forward) or "binned" (msda_forward_binned: head-queries
     sorted by region, gathers from LDS-staged windows; needs the level shapes on the host,
     read from spatial_shapes when spatial_shapes_host is omitted, and a workspace, allocated
-    here when none is given)."""
+    here when none is given).  reuse_order (binned only): skip the sort and use the order an
+    earlier binned call with the same sizes left in `workspace` (msda_forward_binned_reuse)."""
     dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations,
                        attention_weights)
     if gather not in ("binned", "direct"):
         raise ValueError(f"gather {gather!r} is not 'binned' or 'direct'")
+    if reuse_order and gather != "binned":
+        raise ValueError("reuse_order applies to the binned gather only")
     shape = (dims.batch, dims.num_queries, dims.num_heads * dims.head_dim)
     if out is None:
         out = torch.empty(shape, dtype=dt, device=value.device)
@@ -221,13 +226,15 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
         return out
     host = _host_shapes(spatial_shapes, spatial_shapes_host)
     need = msda_forward_binned_workspace_bytes(dims, _DTYPES[dt], host)
+    if reuse_order and workspace is None:
+        raise ValueError("reuse_order needs the workspace of an earlier binned call")
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=value.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.msda_forward_binned(*args, host.ctypes.data, _ptr(workspace), ws_bytes,
-                                 _stream(stream))
+    fn = "msda_forward_binned_reuse" if reuse_order else "msda_forward_binned"
+    st = getattr(lib, fn)(*args, host.ctypes.data, _ptr(workspace), ws_bytes, _stream(stream))
     if st != MSDA_OK:
-        raise MsdaError(st, "msda_forward_binned")
+        raise MsdaError(st, fn)
     return out
 
 

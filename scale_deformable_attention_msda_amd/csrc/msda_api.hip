@@ -230,11 +230,17 @@ size_t msda_forward_binned_workspace_bytes(const msda_dims *dims, msda_dtype dty
   return ws;
 }
 
-msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes,
-                                const int64_t *level_start_index, const void *sampling_locations,
-                                const void *attention_weights, void *out, const msda_dims *dims,
-                                msda_dtype dtype, const int64_t *spatial_shapes_host,
-                                void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The query-binned forward, with or without the sort (reuse_order).
+msda_status forward_binned_run(const void *value, const int64_t *spatial_shapes,
+                               const int64_t *level_start_index, const void *sampling_locations,
+                               const void *attention_weights, void *out, const msda_dims *dims,
+                               msda_dtype dtype, const int64_t *spatial_shapes_host,
+                               void *workspace, size_t workspace_bytes, bool reuse_order,
+                               void *stream) {
   g_last_error[0] = '\0';
   Checked c;
   MSDA_TRY(forward_checks(value, spatial_shapes, level_start_index, sampling_locations,
@@ -247,9 +253,13 @@ msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes
     return fail(MSDA_ERR_WORKSPACE, "this forward needs %zu bytes of workspace, got %zu%s",
                 ws_need, workspace_bytes, workspace ? "" : " (NULL)");
   if (!aligned(workspace, 16)) return fail(MSDA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  const int64_t step = batches_per_launch(c);
+  if (reuse_order && c.B > step)
+    return fail(MSDA_ERR_UNSUPPORTED,
+                "reusing the query order needs the whole call in one launch (%lld batches, at "
+                "most %lld per launch here)", (long long)c.B, (long long)step);
   const auto dt = kernel_dtype(dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t step = batches_per_launch(c);
   for (int64_t b0 = 0; b0 < c.B; b0 += step) {
     const int64_t nb = c.B - b0 < step ? c.B - b0 : step;
     msda::FwdArgs fa{};
@@ -261,10 +271,36 @@ msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes
                              (int)c.elt, spatial_shapes_host))
       return fail(MSDA_ERR_UNSUPPORTED, "binned forward: no plan for %lld batches", (long long)nb);
     fa.w = msda::carve_fwd_scratch(fa.p, workspace);
-    hipError_t e = msda::launch_forward_binned(fa, dt, s);
+    hipError_t e = msda::launch_forward_binned(fa, dt, reuse_order, s);
     if (e != hipSuccess) return hip_fail(e, "binned forward launch");
   }
   return MSDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status msda_forward_binned(const void *value, const int64_t *spatial_shapes,
+                                const int64_t *level_start_index, const void *sampling_locations,
+                                const void *attention_weights, void *out, const msda_dims *dims,
+                                msda_dtype dtype, const int64_t *spatial_shapes_host,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_binned_run(value, spatial_shapes, level_start_index, sampling_locations,
+                            attention_weights, out, dims, dtype, spatial_shapes_host, workspace,
+                            workspace_bytes, false, stream);
+}
+
+msda_status msda_forward_binned_reuse(const void *value, const int64_t *spatial_shapes,
+                                      const int64_t *level_start_index,
+                                      const void *sampling_locations,
+                                      const void *attention_weights, void *out,
+                                      const msda_dims *dims, msda_dtype dtype,
+                                      const int64_t *spatial_shapes_host, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  return forward_binned_run(value, spatial_shapes, level_start_index, sampling_locations,
+                            attention_weights, out, dims, dtype, spatial_shapes_host, workspace,
+                            workspace_bytes, true, stream);
 }
 
 }  // extern "C"

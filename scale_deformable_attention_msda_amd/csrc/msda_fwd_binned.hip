@@ -358,14 +358,20 @@ struct Chunk {
   uint32_t pos;  // first sorted position within (b, m)
 };
 
+// Every field is clamped to the plan's ranges: a list written by this plan's
+// scatter pass is unchanged by that, and a list left by another plan (a
+// violated precondition of msda_forward_binned_reuse) cannot send an access
+// out of range.
 __device__ inline Chunk decode_chunk(const FwdPlan &p, const uint4 &ch) {
   Chunk c;
-  c.b = (int)ch.x / p.M;
-  c.m = (int)ch.x - c.b * p.M;
-  c.by = (int)ch.z / p.GX;
-  c.bx = (int)ch.z - c.by * p.GX;
-  c.n = (int)ch.w;
-  c.pos = ch.y;
+  const int bm = (int)min(ch.x, (uint32_t)(p.nb * p.M - 1));
+  const int e = (int)min(ch.z, (uint32_t)(p.GX * p.GY - 1));
+  c.b = bm / p.M;
+  c.m = bm - c.b * p.M;
+  c.by = e / p.GX;
+  c.bx = e - c.by * p.GX;
+  c.n = (int)min(ch.w, (uint32_t)p.quads);
+  c.pos = min(ch.y, (uint32_t)p.Q - (uint32_t)c.n);
   return c;
 }
 
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(NT) void fwd_tile_kernel(FwdArgs fa) {
   const FwdPlan &p = fa.p;
   const LaunchArgs &a = fa.a;
 
-  const uint32_t nlist = *fa.w.nchunks;
+  const uint32_t nlist = min(*fa.w.nchunks, (uint32_t)p.max_chunks);
   const uint32_t per = (nlist + 7) / 8;
   const uint32_t xcd = blockIdx.x % 8, stride = gridDim.x / 8;
   const uint32_t cend = min((xcd + 1) * per, nlist);
@@ -446,7 +452,9 @@ __global__ __launch_bounds__(NT) void fwd_tile_kernel(FwdArgs fa) {
   bool has_q = quad < C.n;
   uint32_t hq;
   {
-    const uint32_t q = has_q ? fa.w.sorted[((size_t)C.b * p.M + C.m) * p.Q + C.pos + quad] : 0u;
+    const uint32_t q =
+        has_q ? min(fa.w.sorted[((size_t)C.b * p.M + C.m) * p.Q + C.pos + quad], (uint32_t)p.Q - 1)
+              : 0u;
     hq = ((uint32_t)C.b * (uint32_t)p.Q + q) * (uint32_t)p.M + (uint32_t)C.m;
   }
   float su[NS], sv[NS], sa[NS];
@@ -493,7 +501,9 @@ __global__ __launch_bounds__(NT) void fwd_tile_kernel(FwdArgs fa) {
         N = decode_chunk(p, nd);
         nhas_q = quad < N.n;
         const uint32_t q =
-            nhas_q ? fa.w.sorted[((size_t)N.b * p.M + N.m) * p.Q + N.pos + quad] : 0u;
+            nhas_q ? min(fa.w.sorted[((size_t)N.b * p.M + N.m) * p.Q + N.pos + quad],
+                         (uint32_t)p.Q - 1)
+                   : 0u;
         nhq = ((uint32_t)N.b * (uint32_t)p.Q + q) * (uint32_t)p.M + (uint32_t)N.m;
       }
       if (has_next && i == min(2, p.L - 1)) load_slots<T, KR, NS>(p, a, nhq, nhas_q, j, nu, nv, na);
@@ -674,8 +684,30 @@ hipError_t launch_tile_nt(const FwdArgs &fa, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_binned_t(const FwdArgs &fa, hipStream_t s) {
+hipError_t launch_tile_pass(const FwdArgs &fa, hipStream_t s) {
+  const int row = fa.p.D * (int)sizeof(T);
+  hipError_t e;
+  prof_begin(s, "fwd_tile");
+  switch (row) {
+    case 64: e = launch_tile_nt<T, 16>(fa, s); break;
+    case 128: e = launch_tile_nt<T, 32>(fa, s); break;
+    case 256:
+      if constexpr (sizeof(T) == 4) {
+        e = launch_tile_nt<T, 64>(fa, s);
+        break;
+      }
+      [[fallthrough]];
+    default: e = hipErrorInvalidValue; break;
+  }
+  prof_end(s, "fwd_tile");
+  return e;
+}
+
+// reuse_order: skip the sort and walk the chunk list already in the workspace
+template <typename T>
+hipError_t launch_binned_t(const FwdArgs &fa, bool reuse_order, hipStream_t s) {
   const FwdPlan &p = fa.p;
+  if (reuse_order) return launch_tile_pass<T>(fa, s);
   const dim3 grid((unsigned)p.nqb, (unsigned)(p.nb * p.M));
   hipError_t e;
   prof_begin(s, "fwd_count");
@@ -691,21 +723,7 @@ hipError_t launch_binned_t(const FwdArgs &fa, hipStream_t s) {
   hipLaunchKernelGGL(fwd_scatter_kernel, grid, dim3(kFwdCountQ), (size_t)p.nbm * 12, s, fa);
   prof_end(s, "fwd_scatter");
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int row = p.D * (int)sizeof(T);
-  prof_begin(s, "fwd_tile");
-  switch (row) {
-    case 64: e = launch_tile_nt<T, 16>(fa, s); break;
-    case 128: e = launch_tile_nt<T, 32>(fa, s); break;
-    case 256:
-      if constexpr (sizeof(T) == 4) {
-        e = launch_tile_nt<T, 64>(fa, s);
-        break;
-      }
-      [[fallthrough]];
-    default: e = hipErrorInvalidValue; break;
-  }
-  prof_end(s, "fwd_tile");
-  return e;
+  return launch_tile_pass<T>(fa, s);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -844,11 +862,12 @@ FwdScratch carve_fwd_scratch(const FwdPlan &p, void *workspace) {
   return w;
 }
 
-hipError_t launch_forward_binned(const FwdArgs &fa, Dtype dt, hipStream_t stream) {
+hipError_t launch_forward_binned(const FwdArgs &fa, Dtype dt, bool reuse_order,
+                                 hipStream_t stream) {
   switch (dt) {
-    case Dtype::F32: return launch_binned_t<float>(fa, stream);
-    case Dtype::BF16: return launch_binned_t<bf16_t>(fa, stream);
-    case Dtype::F16: return launch_binned_t<f16_t>(fa, stream);
+    case Dtype::F32: return launch_binned_t<float>(fa, reuse_order, stream);
+    case Dtype::BF16: return launch_binned_t<bf16_t>(fa, reuse_order, stream);
+    case Dtype::F16: return launch_binned_t<f16_t>(fa, reuse_order, stream);
   }
   return hipErrorInvalidValue;
 }

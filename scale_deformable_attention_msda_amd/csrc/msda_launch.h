@@ -179,7 +179,9 @@ bool make_fwd_plan(FwdPlan &p, int64_t nb, int64_t Q, int64_t S, int M, int D, i
                    int elt, const int64_t *shapes_host);
 size_t fwd_workspace_bytes(const FwdPlan &p);
 FwdScratch carve_fwd_scratch(const FwdPlan &p, void *workspace);
-hipError_t launch_forward_binned(const FwdArgs &a, Dtype dt, hipStream_t stream);
+// reuse_order: only the tile pass, on the chunk list an earlier launch of the
+// same plan left in the workspace
+hipError_t launch_forward_binned(const FwdArgs &a, Dtype dt, bool reuse_order, hipStream_t stream);
 hipError_t launch_cast_f32_to_half(const float *src, void *dst, size_t n, Dtype dt,
                                    hipStream_t stream);
 

@@ -247,3 +247,23 @@ def test_fp16_accumulators(lib):
     assert bwd(lib, dims(), dtype=2, acc=2, scatter=0, shapes_host=SHAPES) == 3  # binned: fp32
     assert ws_bytes(lib, dims(), 2, 0, scatter=0, shapes_host=SHAPES) > 0
     assert bwd(lib, dims(), dtype=0, acc=2) == 3                   # FP32 data, FP16 accumulator
+
+
+def fwd_reuse(lib, d, dtype=0, shapes_host=None, ws=None, ws_bytes=0):
+    return lib.msda_forward_binned_reuse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d),
+                                         dtype, shapes_host, ws, ws_bytes, None)
+
+
+def test_binned_forward_reuse_rejections(lib):
+    d = dims(**ENCODER)
+    need = fwd_ws(lib, d, 0, PYRAMID)
+    assert fwd_reuse(lib, d, shapes_host=PYRAMID) == 5                  # needs the workspace
+    assert fwd_reuse(lib, d, shapes_host=PYRAMID, ws=FAKE + 4, ws_bytes=need) == 4
+    assert fwd_reuse(lib, d, shapes_host=None, ws=FAKE, ws_bytes=need) == 1
+    # five 260 MB batch images (48 heads of 64 channels): more than one launch, so
+    # no single order to reuse
+    big = msda.MsdaDims(5, 22223, 48, 64, 4, 22223, 4)
+    big_need = fwd_ws(lib, big, 0, PYRAMID)
+    assert big_need != SIZE_MAX, msda.msda_last_error()
+    assert fwd_reuse(lib, big, shapes_host=PYRAMID, ws=FAKE, ws_bytes=big_need) == 3
+    assert "one launch" in msda.msda_last_error()

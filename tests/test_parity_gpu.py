@@ -467,3 +467,43 @@ def test_graph_capture_replays_match_eager(scatter):
         check(f"replay {rep} grad_value vs eager", np_(gv_g), np_(gv_e), *TOL_BWD_FP32)
     gate(x, {k: v.double().cpu().numpy() for k, v in
              dict(out=out_g, grad_value=gv_g, grad_loc=gl_g, grad_attn=ga_g).items()}, o)
+
+
+# ------------------------------------------------- binned forward, order reused
+
+def test_binned_forward_reuse_order():
+    """msda_forward_binned_reuse walks the query order an earlier call left in the
+    workspace: on the same inputs it repeats that call bit for bit, and on other
+    inputs of the same sizes (other offsets, so other regions) it is still exact."""
+    wl = BINNED_FWD["enc_fp32"]
+    say("[parity] binned forward, order reused across inputs")
+    xa = workloads.make_inputs(wl, seed=101, with_grad=False)
+    xb = workloads.make_inputs(wl, seed=202, with_grad=False)
+    ta, tb = parity.upload(xa), parity.upload(xb)
+    d = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
+    host = xa["spatial_shapes"]
+    ws = torch.empty(msda.msda_forward_binned_workspace_bytes(d, msda.MSDA_FP32, host),
+                     dtype=torch.uint8, device="cuda")
+    kw = dict(gather="binned", spatial_shapes_host=host, workspace=ws)
+    out_a = msda.msda_forward(*parity.operands(ta), **kw)
+    out_b = msda.msda_forward(*parity.operands(tb), reuse_order=True, **kw)
+    out_a2 = msda.msda_forward(*parity.operands(ta), reuse_order=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a2, out_a), "same order and inputs must repeat bit for bit"
+    gate_forward(xb, out_b, oracle_forward(xb))
+
+
+def test_binned_forward_reuse_order_encoder_size():
+    say("[parity] binned forward, order of other inputs reused, encoder sizes")
+    wl = workloads.WORKLOADS[2]
+    x, o = workload_case(2)
+    other = workloads.make_inputs(2, seed=workloads.BASE_SEED + 77, with_grad=False)
+    d = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
+    host = x["spatial_shapes"]
+    ws = torch.empty(msda.msda_forward_binned_workspace_bytes(d, msda.MSDA_FP32, host),
+                     dtype=torch.uint8, device="cuda")
+    kw = dict(gather="binned", spatial_shapes_host=host, workspace=ws)
+    msda.msda_forward(*parity.operands(parity.upload(other)), **kw)
+    out = msda.msda_forward(*parity.operands(parity.upload(x)), reuse_order=True, **kw)
+    torch.cuda.synchronize()
+    gate_forward(x, out, o["out"])
