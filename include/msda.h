@@ -250,9 +250,10 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of device workspace msda_backward_softmax needs: the weights image
- * (B*Q*M*L*K elements of `dtype`, rounded up to 256 bytes) followed by what
- * msda_backward_workspace_bytes() reports for the same arguments; 0 when
+ * Bytes of device workspace msda_backward_softmax needs: what
+ * msda_backward_workspace_bytes() reports for the same arguments, preceded by
+ * a weights image (B*Q*M*L*K elements of `dtype`, rounded up to 256 bytes)
+ * unless the scatter is BINNED and L*K is a power of two (at most 64); 0 when
  * B*Q = 0.  SIZE_MAX when the call would be rejected.
  */
 size_t msda_backward_softmax_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
@@ -266,12 +267,13 @@ size_t msda_backward_softmax_workspace_bytes(const msda_dims *dims, msda_dtype d
  * logits.  With gA = d<out, grad_out>/dA (msda_backward's grad_attn for
  * A = softmax(z)):
  *   grad_logits[b,q,m,j] = A_j * (gA_j - sum_i A_i gA_i)   over the L*K samples.
- * Runs as three passes on `stream`: A = softmax(z) into the head of the
- * workspace, msda_backward with those weights (grad_attn written into
+ * Runs on `stream` as msda_backward with weights A (grad_attn written into
  * grad_logits), then an in-place pass that turns gA into grad_logits with A
- * recomputed from z in fp32.  grad_value and grad_loc are those of
- * msda_backward for weights A (for BF16 and FP16 data, A is rounded to the
- * data type once before the scatter, and gA once before the last pass).  scatter, accum_dtype,
+ * recomputed from z in fp32.  With the BINNED scatter and L*K a power of two
+ * (at most 64) the scatter pass forms A itself (fp32, from the lanes that hold
+ * one head-query's logits); otherwise a first pass writes A into the head of
+ * the workspace (rounded once to the data type for BF16 and FP16).  gA is
+ * rounded once to the data type before the last pass.  scatter, accum_dtype,
  * spatial_shapes_host, limits and errors as for msda_backward; workspace must
  * hold msda_backward_softmax_workspace_bytes() bytes (16-byte aligned).
  */

@@ -352,11 +352,13 @@ msda_status backward_setup(const msda_dims *dims, msda_dtype dtype, msda_dtype a
 
 // Enqueue the backward of a validated call (backward_setup + pointer checks
 // done); `workspace` is the part of the caller's workspace the scatter uses.
+// softmax_logits (binned scatter only): attention_weights holds raw logits and
+// the scatter pass forms the softmax weights.
 msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const void *value,
                          const int64_t *spatial_shapes, const int64_t *level_start_index,
                          const void *sampling_locations, const void *attention_weights,
                          const void *grad_out, void *grad_value, void *grad_loc, void *grad_attn,
-                         void *workspace, hipStream_t s) {
+                         void *workspace, hipStream_t s, bool softmax_logits = false) {
   const Checked &c = su.c;
   if (c.value_elems == 0) return MSDA_OK;
   hipError_t e;
@@ -377,6 +379,7 @@ msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const 
     a.grad_attn = grad_attn;
     a.p = su.plan;
     a.w = msda::carve_bin_scratch(su.plan, workspace);
+    a.softmax = softmax_logits;
     e = msda::launch_backward_binned(a, dt, s);
     return e == hipSuccess ? MSDA_OK : hip_fail(e, "binned backward launch");
   }
@@ -442,10 +445,20 @@ msda_status workspace_check(size_t need, void *workspace, size_t workspace_bytes
   return MSDA_OK;
 }
 
+// The softmax backward forms the weights inside the binned scatter pass when a
+// head-query's L*K samples fill an aligned lane group (L*K a power of two, at
+// most 64); otherwise a row pass writes them to the head of the workspace.
+bool softmax_in_scatter(const BackwardSetup &su) {
+  const int64_t lk = su.c.L * su.c.K;
+  return su.binned && lk <= 64 && (lk & (lk - 1)) == 0;
+}
+
 // Bytes of the softmax backward's weights image at the head of its workspace
-// (256-byte multiple, so the scatter's part keeps its alignment).
-size_t softmax_weights_bytes(const Checked &c) {
-  return ((size_t)(c.sample_elems * c.elt) + 255) / 256 * 256;
+// (256-byte multiple, so the scatter's part keeps its alignment); 0 when the
+// scatter pass forms the weights.
+size_t softmax_weights_bytes(const BackwardSetup &su) {
+  if (!su.work || softmax_in_scatter(su)) return 0;
+  return ((size_t)(su.c.sample_elems * su.c.elt) + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -488,7 +501,7 @@ size_t msda_backward_softmax_workspace_bytes(const msda_dims *dims, msda_dtype d
   BackwardSetup su;
   if (backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su) != MSDA_OK)
     return SIZE_MAX;
-  return su.work ? softmax_weights_bytes(su.c) + su.ws_need : 0;
+  return su.work ? softmax_weights_bytes(su) + su.ws_need : 0;
 }
 
 msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shapes,
@@ -506,20 +519,21 @@ msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shap
   MSDA_TRY(backward_pointer_checks(c, value, spatial_shapes, level_start_index,
                                    sampling_locations, attention_logits, "attention_logits",
                                    grad_out, grad_value, grad_loc, grad_logits, "grad_logits"));
-  const size_t wbytes = su.work ? softmax_weights_bytes(c) : 0;
+  const size_t wbytes = softmax_weights_bytes(su);
   MSDA_TRY(workspace_check(wbytes + su.ws_need, workspace, workspace_bytes, "softmax backward"));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto dt = kernel_dtype(dtype);
   const int lk = (int)(c.L * c.K);
-  void *weights = workspace;
-  if (su.work) {
-    hipError_t e = msda::launch_softmax_rows(attention_logits, weights, c.hq_elems, lk, dt, s);
+  const bool fused = su.work && softmax_in_scatter(su);
+  const void *weights = fused ? attention_logits : workspace;
+  if (su.work && !fused) {
+    hipError_t e = msda::launch_softmax_rows(attention_logits, workspace, c.hq_elems, lk, dt, s);
     if (e != hipSuccess) return hip_fail(e, "softmax launch");
   }
-  void *scatter_ws = su.work ? static_cast<char *>(workspace) + wbytes : workspace;
+  void *scatter_ws = wbytes ? static_cast<char *>(workspace) + wbytes : workspace;
   MSDA_TRY(backward_run(su, accum_dtype, value, spatial_shapes, level_start_index,
                         sampling_locations, weights, grad_out, grad_value, grad_loc, grad_logits,
-                        scatter_ws, s));
+                        scatter_ws, s, fused));
   if (su.work) {
     hipError_t e = msda::launch_softmax_grad_rows(attention_logits, grad_logits, c.hq_elems, lk,
                                                   dt, s);

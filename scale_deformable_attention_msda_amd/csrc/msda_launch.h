@@ -89,6 +89,9 @@ struct BinArgs {
   void *grad_attn;
   BinPlan p;
   BinScratch w;
+  // attn holds raw logits: the scatter pass forms each head-query's softmax
+  // weights (L*K a power of two, at most 64)
+  bool softmax = false;
 };
 
 // ------------------------------------------------ query-binned forward

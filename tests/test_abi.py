@@ -212,8 +212,13 @@ def test_softmax_backward_workspace_sizes(lib):
     assert softmax_ws_bytes(lib, d, 0, 0, 1) == 512              # fp32, atomic: 512 + 0
     assert softmax_ws_bytes(lib, d, 1, 1, 1) == 256              # bf16 data, bf16 accum
     assert softmax_ws_bytes(lib, d, 1, 0, 1) == 256 + ws_bytes(lib, d, 1, 0, scatter=1)
+    # binned with L*K = 4: the scatter pass forms the weights, no image
     binned = ws_bytes(lib, d, 0, 0, scatter=0, shapes_host=SHAPES)
-    assert softmax_ws_bytes(lib, d, 0, 0, 0, SHAPES) == 512 + binned
+    assert softmax_ws_bytes(lib, d, 0, 0, 0, SHAPES) == binned
+    # binned with L*K = 6: the image again (1*16*2*2*3 * 4 bytes = 768)
+    d6 = dims(K=3)
+    binned6 = ws_bytes(lib, d6, 0, 0, scatter=0, shapes_host=SHAPES)
+    assert softmax_ws_bytes(lib, d6, 0, 0, 0, SHAPES) == 768 + binned6
     assert softmax_ws_bytes(lib, dims(Q=3), 0, 0, 1) == 256      # 3*2*4*4 = 96 bytes, rounded
     assert softmax_ws_bytes(lib, dims(Q=0), 0, 0, 0, None) == 0
     assert softmax_ws_bytes(lib, d, 0, 0, 0, None) == SIZE_MAX   # binned needs host shapes

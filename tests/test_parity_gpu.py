@@ -324,20 +324,25 @@ def test_softmax_edge(name):
         assert np.all(g["grad_logits"] == 0.0)
 
 
-def test_softmax_extreme_logits():
+@pytest.mark.parametrize("name", ["ragged_fp32", "d16_fp32"])
+def test_softmax_extreme_logits(name):
     """Shift invariance at large magnitudes, -Inf logits (zero weight), rows of equal
-    logits and exp underflow; also that the forward is bit-identical across runs."""
-    say("[parity] softmax method: extreme logits")
-    wl = EDGE["ragged_fp32"]
+    logits and exp underflow; also that the forward is bit-identical across runs.
+    L*K = 9 takes the row pass before the binned scatter, L*K = 8 the weights
+    formed inside the scatter pass."""
+    say(f"[parity] softmax method: extreme logits, {name}")
+    wl = EDGE[name]
     x = workloads.make_inputs(wl, seed=11)
     z = x["attention_logits"]
-    z[0, 0, 0] += 3.0e4                       # one row shifted far up
-    z[0, 1, 1] -= 3.0e4                       # one far down
-    z[1, 2, 0] = 7.25                         # all equal: uniform weights
-    z[1, 3, 2, 0, 0] = -np.inf                # one sample with weight exactly 0
-    z[2, 4, 1] = 0.0
-    z[2, 4, 1, 0, 0] = 150.0                  # the others underflow in fp32 and fp64 alike
-    z[2, 5, 2] *= 60.0                        # a wide spread
+    B, Q, M = z.shape[:3]
+    row = lambda i: (i % B, (3 * i + 1) % Q, i % M)
+    z[row(0)] += 3.0e4                        # one row shifted far up
+    z[row(1)] -= 3.0e4                        # one far down
+    z[row(2)] = 7.25                          # all equal: uniform weights
+    z[row(3) + (0, 0)] = -np.inf              # one sample with weight exactly 0
+    z[row(4)] = 0.0
+    z[row(4) + (0, 0)] = 150.0                # the others underflow in fp32 and fp64 alike
+    z[row(5)] *= 60.0                         # a wide spread
     o = parity.run_oracle_softmax(x)
     assert all(np.isfinite(v).all() for v in o.values())
     g = parity.run_gpu_softmax(x)
