@@ -341,6 +341,34 @@ __device__ inline double group_sum_f64(double x) {
   return x;
 }
 
+// "softmax" method (DeformOps documentation, section "Multi-scale deformable
+// attention"): the lanes of an aligned group of lk lanes (lk a power of two, at
+// most 64) hold the lk logits of one head-query; each lane returns its weight
+// exp(z - max) / sum over the group.  A NaN or +Inf logit, or all -Inf, makes
+// the group's weights NaN, as the definition does.
+// Groups of up to 16 lanes combine by DPP moves inside a row (pairs, quads,
+// mirrored halves, mirrored rows: every lane ends with the whole group);
+// groups of 32 and 64 by lane shuffles.
+template <bool MAX>
+__device__ inline float group_reduce(float x, int lk) {
+  auto op = [](float a, float b) { return MAX ? (b > a ? b : a) : a + b; };
+  if (lk <= 16) {
+    if (lk >= 2) x = op(x, dpp_move<kDppQuadXor1>(x));
+    if (lk >= 4) x = op(x, dpp_move<kDppQuadXor2>(x));
+    if (lk >= 8) x = op(x, dpp_move<kDppRowHalfMirror>(x));
+    if (lk >= 16) x = op(x, dpp_move<kDppRowMirror>(x));
+  } else {
+    for (int off = 1; off < lk; off <<= 1) x = op(x, __shfl_xor(x, off));
+  }
+  return x;
+}
+
+__device__ inline float group_softmax(float z, int lk) {
+  const float mx = group_reduce<true>(z, lk);
+  const float e = expf(z - mx);
+  return e * (1.0f / group_reduce<false>(e, lk));
+}
+
 // ----------------------------------------------------------- lane layout
 
 // How a head row (D channels of T) is spread over a group of lanes: each lane

@@ -86,7 +86,11 @@ __device__ inline void stage_levels(Level *lv, const LaunchArgs &a) {
 // ------------------------------------------------------------------ forward
 
 // SOFTMAX: a.attn holds raw logits; the weight of sample j of head-query h is
-// exp(z_j - max_h) / sum_i exp(z_i - max_h) over the L*K samples of h.
+// exp(z_j - max_h) / sum_i exp(z_i - max_h) over the L*K samples of h.  Phase 1
+// gives lane s of each pass sample s of the block (passes start at multiples
+// of the block size), so for L*K a power of two (at most 64) a head-query's
+// logits sit in an aligned lane group and each lane forms its weight there;
+// otherwise phase 0 stages the logits in LDS first.
 template <typename T, int D, bool SOFTMAX>
 __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   using RL = RowLayout<T, D>;
@@ -104,11 +108,13 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   const int nhq = (int)min((int64_t)hqb, total_hq - hq0);
   stage_levels(lv, a);
 
-  // phase 0 (softmax): the block's logits, [hqb][L*K + 1] in LDS, become
-  // exp(z - max) in place, with 1 / sum per head-query beside them
+  // phase 0 (softmax, L*K not a power of two): the block's logits,
+  // [hqb][L*K + 1] in LDS, become exp(z - max) in place, with 1 / sum per
+  // head-query beside them
   float *zb = reinterpret_cast<float *>(geo + LK * gs_stride);
   float *inv = zb + hqb * (LK + 1);
-  if constexpr (SOFTMAX) {
+  const bool in_lanes = LK <= 64 && (LK & (LK - 1)) == 0;
+  if (SOFTMAX && !in_lanes) {
     const int zs = LK + 1;
     for (int s = threadIdx.x; s < nhq * LK; s += blockDim.x) {
       const int hl = s / LK;
@@ -140,7 +146,11 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
     const int m = (int)(hq % M);
     const int64_t b = hq / M / a.Q;
     const float u = ld<T>(a.loc, 2 * gs), v = ld<T>(a.loc, 2 * gs + 1);
-    const float w = SOFTMAX ? zb[hl * (LK + 1) + j] * inv[hl] : ld<T>(a.attn, gs);
+    float w;
+    if constexpr (SOFTMAX)
+      w = in_lanes ? group_softmax(ld<T>(a.attn, gs), LK) : zb[hl * (LK + 1) + j] * inv[hl];
+    else
+      w = ld<T>(a.attn, gs);
     Corners cs;
     float lx, ly;
     sample_corners(u, v, lv[j / K], (uint32_t)(b * a.S), row_stride,
@@ -549,13 +559,15 @@ template <typename T, int D>
 hipError_t fwd_launch(const LaunchArgs &a, bool softmax, hipStream_t stream) {
   using RL = RowLayout<T, D>;
   const int LK = (int)(a.L * a.K);
-  // softmax: one more fp32 per sample (the logit) and one per head-query (1 / sum)
-  const int hqb = pick_hqb(RL::G, LK, (int)sizeof(Corners) + (softmax ? 8 : 0));
+  // softmax staged in LDS (L*K not a power of two): one more fp32 per sample
+  // (the logit) and one per head-query (1 / sum)
+  const bool staged = softmax && !(LK <= 64 && (LK & (LK - 1)) == 0);
+  const int hqb = pick_hqb(RL::G, LK, (int)sizeof(Corners) + (staged ? 8 : 0));
   const int64_t total_hq = a.nb * a.Q * a.M;
   const int64_t blocks = padded_grid((total_hq + hqb - 1) / hqb);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   size_t lds = (size_t)LK * (hqb + 1) * sizeof(Corners);
-  if (softmax) lds += ((size_t)hqb * (LK + 1) + hqb) * sizeof(float);
+  if (staged) lds += ((size_t)hqb * (LK + 1) + hqb) * sizeof(float);
   prof_begin(stream, softmax ? "fwd_softmax" : "fwd");
   if (softmax)
     hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
