@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kRowThreads) void softmax_rows_kernel(const T *__re
     const int nr = (int)min((int64_t)p.rows, p.n_rows - r0);
     stage_rows<T>(logits + r0 * p.lk, zrow, nr * p.lk, p);
     __syncthreads();
-    if (threadIdx.x < nr) {
+    if ((int)threadIdx.x < nr) {
       float *z = zrow + threadIdx.x * p.zs;
       float a[LKMAX];
       softmax_row<LKMAX>(z, p.lk, a);
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kRowThreads) void softmax_grad_rows_kernel(
     stage_rows<T>(logits + r0 * p.lk, zrow, nr * p.lk, p);
     stage_rows<T>(g + r0 * p.lk, grow, nr * p.lk, p);
     __syncthreads();
-    if (threadIdx.x < nr) {
+    if ((int)threadIdx.x < nr) {
       float *gr = grow + threadIdx.x * p.zs;
       float a[LKMAX], ga[LKMAX];
       softmax_row<LKMAX>(zrow + threadIdx.x * p.zs, p.lk, a);
