@@ -379,8 +379,9 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): every box here has "
-              "one GPU; see DESIGN.md for how the operator would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the operator has no "
+              "multi-GPU path; a sharded run would give each GPU its own batch slice.",
+              file=sys.stderr)
         return 2
 
     import torch
