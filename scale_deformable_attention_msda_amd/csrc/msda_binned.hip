@@ -22,7 +22,9 @@
 //            atomic, write a 16-byte record (id, location, weight) of every
 //            sample in bin order, so the tile pass reads its samples
 //            contiguously instead of gathering 8- and 4-byte pieces;
-//   tile     one block per chunk: stage the (T+1)^2 value rows of the tile
+//   tile     persistent blocks, one chunk at a time (the next chunk's records
+//            and value rows are loaded while the current one writes its
+//            results): stage the (T+1)^2 value rows of the tile
 //            (plus rim) in LDS, counting-sort the chunk's samples by their
 //            bilinear cell (integer LDS atomics), then one lane group per
 //            cell keeps the cell's four corner rows and four accumulators in
@@ -382,7 +384,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
       a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
     }
   }
-  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *a.w.nchunks = pre_tot[1] + tot[1];
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+    a.w.nchunks[0] = pre_tot[1] + tot[1];
+    a.w.nchunks[1] = 0;  // the tile pass's chunk counter
+  }
 }
 
 // ------------------------------------------------------------- scatter pass
@@ -512,6 +517,8 @@ constexpr int kMaxItems = kCells;   // stage slots, one per item
 //   istart [kCells + 1] u32        first item of each cell; istart[kCells] = items in all
 //   items  [kMaxItems] u32         first | (len - 1) << 10 | cell << 20 of each item
 //   sched  [kMaxItems] u32         items by decreasing number of batches
+//   next   u32                     the block's next chunk, claimed by thread 0
+//   lvl    [kMaxLevels] LevelTab   level table for decoding the bins of later chunks
 template <int D>
 struct TileSmem {
   static constexpr int RS = TileLayout<D>::RS;
@@ -527,7 +534,9 @@ struct TileSmem {
   static constexpr size_t istart = cstart + (size_t)(kCells + 1) * 4;
   static constexpr size_t items = istart + (size_t)(kCells + 1) * 4;
   static constexpr size_t sched = items + (size_t)kMaxItems * 4;
-  static constexpr size_t bytes = sched + (size_t)kMaxItems * 4;
+  static constexpr size_t next = sched + (size_t)kMaxItems * 4;
+  static constexpr size_t lvl = next + 16;
+  static constexpr size_t bytes = lvl + (size_t)kMaxLevels * sizeof(LevelTab);
 };
 static_assert(kChunk <= 1024, "item packing keeps 10-bit first / length fields");
 
@@ -562,6 +571,31 @@ __device__ inline BinPos decode_bin(const BinPlan &p, int bin) {
   r.tx = t - r.ty * ntx;
   r.H = H;
   r.W = W;
+  r.ntx = ntx;
+  return r;
+}
+
+// decode_bin from the level table in LDS: inside the tile kernel's chunk loop
+// the plan's per-level arrays would otherwise stay in scalar registers for the
+// whole loop.  bin is wave-uniform, and so are the results.
+__device__ inline BinPos decode_bin_lds(const BinPlan &p, const LevelTab *lt, int bin) {
+  const int BM = (int)p.B * p.M;
+  int l = 0;
+  while (l + 1 < p.L && !(bin >= lt[l].bin_base && bin < lt[l].bin_base + BM * lt[l].ntiles)) ++l;
+  l = __builtin_amdgcn_readfirstlane(l);
+  const int base = __builtin_amdgcn_readfirstlane(lt[l].bin_base);
+  const int nt = __builtin_amdgcn_readfirstlane(lt[l].ntiles);
+  const int ntx = __builtin_amdgcn_readfirstlane(lt[l].ntx);
+  BinPos r;
+  const int rem = bin - base;
+  const int bm = rem / nt, t = rem - bm * nt;
+  r.l = l;
+  r.b = bm / p.M;
+  r.m = bm - r.b * p.M;
+  r.ty = t / ntx;
+  r.tx = t - r.ty * ntx;
+  r.H = __builtin_amdgcn_readfirstlane(lt[l].H);
+  r.W = __builtin_amdgcn_readfirstlane(lt[l].W);
   r.ntx = ntx;
   return r;
 }
@@ -708,50 +742,68 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   uint32_t *istart = reinterpret_cast<uint32_t *>(smem + SM::istart);
   uint32_t *items = reinterpret_cast<uint32_t *>(smem + SM::items);
   uint32_t *sched = reinterpret_cast<uint32_t *>(smem + SM::sched);
+  uint32_t *next_slot = reinterpret_cast<uint32_t *>(smem + SM::next);
+  LevelTab *lt = reinterpret_cast<LevelTab *>(smem + SM::lvl);
 
   const BinPlan &p = a.p;
-  // the chunk count, this block's chunk entry and the level starts do not
-  // depend on each other: issue the loads together
+  // the chunk count and this block's first chunk entry do not depend on each
+  // other: issue the loads together
   const uint32_t nchunks = *a.w.nchunks;
-  const uint4 ck = a.w.chunks[blockIdx.x];
-  int64_t lstart[kMaxLevels];
-#pragma unroll
-  for (int k = 0; k < kMaxLevels; ++k) lstart[k] = a.starts[min(k, p.L - 1)];
+  uint4 ck = a.w.chunks[blockIdx.x];
   if (blockIdx.x >= nchunks) return;
-  const int bin = (int)ck.x;
-  const uint32_t first = ck.y, count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
-  const BinPos bp = decode_bin(p, bin);
-  const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
-  int64_t start = lstart[0];
-#pragma unroll
-  for (int k = 1; k < kMaxLevels; ++k)
-    if (k == l) start = lstart[k];
-  const int px0 = tx * kTile, py0 = ty * kTile;
-  const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
-  const int grp = threadIdx.x / G, lane = threadIdx.x % G;
 
-  // ---- loads first: the chunk's sample records and the tile's value rows,
-  // all branch-free (clamped indices) so they are in flight together
-  for (int c = threadIdx.x; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
+  // The block is persistent: after its first chunk (= blockIdx.x) it claims
+  // chunks gridDim.x, gridDim.x + 1, ... from a counter, one at a time, until
+  // they run out.  A chunk's records and value rows are loaded into registers
+  // while the previous chunk writes its results and rows, so their latency
+  // hides behind that work.
   uint4 rc[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const uint32_t i = threadIdx.x + r * 256;
-    rc[r] = a.w.recs[count > 0 ? first + min(i, count - 1) : 0u];
-  }
   float vrow[kRowIters][VEC];
   bool vin[kRowIters];
+  int64_t loaded_start;  // first pyramid row of the loaded chunk's level
+  // all branch-free (clamped indices), so the loads are in flight together
+  auto load_chunk = [&](const uint4 &c, const BinPos &q, uint32_t tid) {
+    const int grp = (int)tid / G, lane = (int)tid % G;
+    const uint32_t f = c.y, n = min(c.z, (uint32_t)kChunk);
+    const int64_t st = a.starts[q.l];
+    loaded_start = st;
 #pragma unroll
-  for (int k = 0; k < kRowIters; ++k) {
-    const int r = grp + k * NG;
-    const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
-    const int py = py0 + iy, px = px0 + ix;
-    const int64_t prow = start + (int64_t)py * W + px;  // pyramid row inside the batch image
-    vin[k] = count > 0 && r < NROWS && py < H && px < W && prow >= 0 && prow < p.S;
-    // branch-free: rows outside the map load the level's first row and are zeroed below
-    const int64_t row = vin[k] ? prow : (start >= 0 && start < p.S ? start : 0);
-    load_vec<T, VEC>(a.value, (((int64_t)b * p.S + row) * p.M + m) * D + lane * VEC, vrow[k]);
-  }
+    for (int r = 0; r < kPer; ++r) {
+      const uint32_t i = tid + r * 256;
+      rc[r] = a.w.recs[n > 0 ? f + min(i, n - 1) : 0u];
+    }
+#pragma unroll
+    for (int k = 0; k < kRowIters; ++k) {
+      const int r = grp + k * NG;
+      const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
+      const int py = q.ty * kTile + iy, px = q.tx * kTile + ix;
+      const int64_t prow = st + (int64_t)py * q.W + px;  // pyramid row inside the batch image
+      vin[k] = n > 0 && r < NROWS && py < q.H && px < q.W && prow >= 0 && prow < p.S;
+      // rows outside the map load the level's first row and are zeroed when staged
+      const int64_t row = vin[k] ? prow : (st >= 0 && st < p.S ? st : 0);
+      load_vec<T, VEC>(a.value, (((int64_t)q.b * p.S + row) * p.M + q.m) * D + lane * VEC, vrow[k]);
+    }
+  };
+  BinPos loaded_pos = decode_bin(p, (int)ck.x);
+  load_chunk(ck, loaded_pos, threadIdx.x);
+  stage_level_tab(p, lt);  // read after the first barrier below
+
+  for (;;) {
+  // the thread index, made opaque to the compiler once per chunk: otherwise it
+  // hoists the index arithmetic of every phase out of the loop, and those
+  // values would hold registers through the item loop
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int grp = (int)tid / G, lane = (int)tid % G;
+  const int bin = (int)ck.x;
+  const uint32_t count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
+  const BinPos bp = loaded_pos;
+  const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
+  const int64_t start = loaded_start;
+  const int px0 = tx * kTile, py0 = ty * kTile;
+  const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
+
+  for (int c = tid; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
 #pragma unroll
   for (int k = 0; k < kRowIters; ++k) {
     const int r = grp + k * NG;
@@ -759,12 +811,18 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) vt[r * RS + lane * VEC + i] = vin[k] ? vrow[k][i] : 0.0f;
   }
+  if (tid == 0)
+    *next_slot = gridDim.x + __hip_atomic_fetch_add(a.w.nchunks + 1, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  // the next chunk's entry: needed only for the prefetch after the item loop
+  const uint32_t cn = __builtin_amdgcn_readfirstlane(*next_slot);
+  const uint4 ck_next = a.w.chunks[min(cn, nchunks - 1)];
 
   // ---- phase A: cell of each sample and its rank inside the cell
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const uint32_t i = threadIdx.x + r * 256;
+    const uint32_t i = tid + r * 256;
     if (i >= count) break;
     uint32_t t = kDropped;
     const uint32_t id = rc[r].x;
@@ -787,13 +845,13 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     tag[i] = t;
   }
   __syncthreads();
-  if (threadIdx.x < 64) cell_starts(cnt, cstart);
+  if (tid < 64) cell_starts(cnt, cstart);
   __syncthreads();
   // wave 0 plans the items while the other waves put the records in cell order
-  if (threadIdx.x < 64) {
+  if (tid < 64) {
     plan_items(cnt, cstart, istart, items, sched);
   } else {
-    for (uint32_t i = threadIdx.x - 64; i < count; i += blockDim.x - 64) {
+    for (uint32_t i = tid - 64; i < count; i += blockDim.x - 64) {
       const uint32_t t = tag[i];
       if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
     }
@@ -964,10 +1022,16 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   }
   __syncthreads();
 
+  // the next chunk's records and value rows: in flight during the two passes
+  // below (after the last chunk this loads a chunk again and leaves it unused,
+  // which keeps the registers of the loads out of the item loop)
+  loaded_pos = decode_bin_lds(p, lt, (int)ck_next.x);
+  load_chunk(ck_next, loaded_pos, tid);
+
   // ---- per-sample results back in record order: the scatter pass wrote a
   // bin's records in sample order, so neighbouring lanes store neighbouring
   // ids and the stores of a sample's points merge
-  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+  for (uint32_t i = tid; i < count; i += blockDim.x) {
     const uint32_t t = tag[i];
     if (t == kDropped) continue;
     const uint4 r = reinterpret_cast<const uint4 *>(sorted)[cstart[t & 0xffu] + (t >> 8)];
@@ -1014,6 +1078,10 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) dst[i] = v[i];
     }
+  }
+  if (cn >= nchunks) break;
+  __syncthreads();  // the next chunk reuses every LDS array
+  ck = ck_next;
   }
 }
 
@@ -1119,10 +1187,19 @@ size_t tile_lds_bytes() {
 template <typename T, int D>
 hipError_t launch_tile_and_merge(const BinArgs &a, hipStream_t s) {
   const size_t lds = tile_lds_bytes<T, D>();
+  // persistent tile blocks: as many as fit on the device at once, at most one per chunk
+  auto kernel = tile_kernel<T, D>;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds);
+  if (e != hipSuccess) return e;
+  const int64_t resident = (int64_t)std::max(1, cus * std::max(1, per_cu));
+  const int64_t grid = std::min(resident, (int64_t)a.p.max_chunks);
   prof_begin(s, "bin_tile");
-  hipLaunchKernelGGL((tile_kernel<T, D>), dim3(a.p.max_chunks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, s, a);
   prof_end(s, "bin_tile");
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_begin(s, "bin_merge");
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.p.nbins), dim3(256), 0, s, a);

@@ -71,7 +71,7 @@ struct BinScratch {
   uint32_t *bin_start;  // [nbins] first sorted position of a bin
   uint32_t *bin_nch;    // [nbins] chunks of a bin
   uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
-  uint32_t *nchunks;    // [1] chunks in use
+  uint32_t *nchunks;    // [2] chunks in use; the tile pass's counter of claimed chunks
   uint4 *chunks;        // [max_chunks] (bin, first position, count, slot or ~0) in chunk order
   uint4 *recs;          // [total] (id, u, v, A) of every live sample, sorted by bin
   float *rim;           // [nbins][4*tile][D] edge rows and halo of single-chunk tiles
