@@ -789,299 +789,300 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   stage_level_tab(p, lt);  // read after the first barrier below
 
   for (;;) {
-  // the thread index, made opaque to the compiler once per chunk: otherwise it
-  // hoists the index arithmetic of every phase out of the loop, and those
-  // values would hold registers through the item loop
-  uint32_t tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int grp = (int)tid / G, lane = (int)tid % G;
-  const int bin = (int)ck.x;
-  const uint32_t count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
-  const BinPos bp = loaded_pos;
-  const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
-  const int64_t start = loaded_start;
-  const int px0 = tx * kTile, py0 = ty * kTile;
-  const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
+    // the thread index, made opaque to the compiler once per chunk: otherwise it
+    // hoists the index arithmetic of every phase out of the loop, and those
+    // values would hold registers through the item loop
+    uint32_t tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int grp = (int)tid / G, lane = (int)tid % G;
+    const int bin = (int)ck.x;
+    const uint32_t count = min(ck.z, (uint32_t)kChunk), slot = ck.w;
+    const BinPos bp = loaded_pos;
+    const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
+    const int64_t start = loaded_start;
+    const int px0 = tx * kTile, py0 = ty * kTile;
+    const int64_t row0 = (int64_t)b * p.S + start;  // first pyramid row of this level and batch
 
-  for (int c = tid; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
+    for (int c = tid; c < kCells + 1; c += blockDim.x) cnt[c] = 0;
 #pragma unroll
-  for (int k = 0; k < kRowIters; ++k) {
-    const int r = grp + k * NG;
-    if (r < NROWS + 1)
+    for (int k = 0; k < kRowIters; ++k) {
+      const int r = grp + k * NG;
+      if (r < NROWS + 1)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) vt[r * RS + lane * VEC + i] = vin[k] ? vrow[k][i] : 0.0f;
-  }
-  if (tid == 0)
-    *next_slot = gridDim.x + __hip_atomic_fetch_add(a.w.nchunks + 1, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  // the next chunk's entry: needed only for the prefetch after the item loop
-  const uint32_t cn = __builtin_amdgcn_readfirstlane(*next_slot);
-  const uint4 ck_next = a.w.chunks[min(cn, nchunks - 1)];
+        for (int i = 0; i < VEC; ++i) vt[r * RS + lane * VEC + i] = vin[k] ? vrow[k][i] : 0.0f;
+    }
+    if (tid == 0)
+      *next_slot = gridDim.x + __hip_atomic_fetch_add(a.w.nchunks + 1, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    // the next chunk's entry: needed only for the prefetch after the item loop
+    const uint32_t cn = __builtin_amdgcn_readfirstlane(*next_slot);
+    const uint4 ck_next = a.w.chunks[min(cn, nchunks - 1)];
 
-  // ---- phase A: cell of each sample and its rank inside the cell
+    // ---- phase A: cell of each sample and its rank inside the cell
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const uint32_t i = tid + r * 256;
-    if (i >= count) break;
-    uint32_t t = kDropped;
-    const uint32_t id = rc[r].x;
-    const float su = __uint_as_float(rc[r].y), sv = __uint_as_float(rc[r].z);
-    if (id < p.total) {
-      const uint32_t hq = fdiv(id, p.div_lk);
-      const uint32_t j = id - hq * (uint32_t)(p.L * p.K);
-      Cell c;
-      if ((int)fdiv(j, p.div_k) == l && cell_of(su, sv, H, W, c)) {
-        const int cy = c.y0 - py0 + 1, cx = c.x0 - px0 + 1;
-        if (cy >= 0 && cy < kEdge && cx >= 0 && cx < kEdge) {
-          const uint32_t cell = (uint32_t)(cy * kEdge + cx);
-          const uint32_t rank = __hip_atomic_fetch_add(&cnt[cell], 1u, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-          raw[i] = SampleRec{id, __uint_as_float(rc[r].w), su, sv};
-          t = cell | (rank << 8);
-        }
-      }
-    }
-    tag[i] = t;
-  }
-  __syncthreads();
-  if (tid < 64) cell_starts(cnt, cstart);
-  __syncthreads();
-  // wave 0 plans the items while the other waves put the records in cell order
-  if (tid < 64) {
-    plan_items(cnt, cstart, istart, items, sched);
-  } else {
-    for (uint32_t i = tid - 64; i < count; i += blockDim.x - 64) {
-      const uint32_t t = tag[i];
-      if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
-    }
-  }
-  __syncthreads();
-
-  // ---- item loop: lane group g takes the schedule's entries g, 2NG-1-g,
-  // 2NG+g, ... (largest items first, snaking so the groups of a wave get items
-  // of similar size); an item's four corner rows (fp64) and its four corner
-  // sums (fp32) stay in registers
-  const uint32_t nitems = istart[kCells];
-  for (int round = 0; round * NG < (int)nitems; ++round) {
-    const int r = round * NG + ((round & 1) ? NG - 1 - grp : grp);
-    if (r >= (int)nitems) continue;
-    const int item = (int)sched[r];
-    const uint32_t desc = items[item];
-    const uint32_t s0 = desc & 0x3ffu, n = ((desc >> 10) & 0x3ffu) + 1, cell = desc >> 20;
-    const int cy = (int)cell / kEdge, cx = (int)cell - ((int)cell / kEdge) * kEdge;
-    const double x0 = (double)(px0 + cx - 1), y0 = (double)(py0 + cy - 1);
-    double V[4][VEC];
-    float acc[4][VEC];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // corner q of cell (cy, cx) is tile-local pixel (cy - 1 + q/2, cx - 1 + q%2)
-      const int iy = cy - 1 + (q >> 1), ix = cx - 1 + (q & 1);
-      const bool in = iy >= 0 && ix >= 0 && py0 + iy < H && px0 + ix < W;
-      const float *src = vt + (in ? iy * kEdge + ix : kZeroRow) * RS + lane * VEC;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        V[q][i] = (double)src[i];
-        acc[q][i] = 0.0f;
-      }
-    }
-    if constexpr (G == 4) {
-      // transposed batches of kU = 4 samples: slot t of lane j holds sample
-      // k0 + (j ^ t), so after the lane-wise partial dots one quad permutation
-      // per slot hands lane j the full p_c of sample k0 + j, and every lane
-      // does the per-sample work (weights, grad_attn, grad_loc) for its own
-      // sample instead of all four lanes repeating it
-      static_assert(kU == 4, "one sample per lane of a group");
-      uint4 own[1];          // record of the lane's own sample
-      uint32_t ids[1][4];    // sample ids of the four slots
-      float g[1][4][VEC];    // grad_out rows (this lane's channels) of the four slots
-      auto fetch = [&](uint32_t k0, int buf) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t pos = s0 + min(k0 + (uint32_t)(lane ^ t), n - 1);
-          if (t == 0) {
-            own[buf] = reinterpret_cast<const uint4 *>(sorted)[pos];
-            ids[buf][0] = own[buf].x;
-          } else {
-            ids[buf][t] = sorted[pos].id;
+    for (int r = 0; r < kPer; ++r) {
+      const uint32_t i = tid + r * 256;
+      if (i >= count) break;
+      uint32_t t = kDropped;
+      const uint32_t id = rc[r].x;
+      const float su = __uint_as_float(rc[r].y), sv = __uint_as_float(rc[r].z);
+      if (id < p.total) {
+        const uint32_t hq = fdiv(id, p.div_lk);
+        const uint32_t j = id - hq * (uint32_t)(p.L * p.K);
+        Cell c;
+        if ((int)fdiv(j, p.div_k) == l && cell_of(su, sv, H, W, c)) {
+          const int cy = c.y0 - py0 + 1, cx = c.x0 - px0 + 1;
+          if (cy >= 0 && cy < kEdge && cx >= 0 && cx < kEdge) {
+            const uint32_t cell = (uint32_t)(cy * kEdge + cx);
+            const uint32_t rank = __hip_atomic_fetch_add(&cnt[cell], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+            raw[i] = SampleRec{id, __uint_as_float(rc[r].w), su, sv};
+            t = cell | (rank << 8);
           }
-          load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(ids[buf][t], p.div_lk) * D + lane * VEC,
-                           g[buf][t]);
         }
-      };
-      auto consume = [&](uint32_t k0, int buf) {
-        double P[4];
+      }
+      tag[i] = t;
+    }
+    __syncthreads();
+    if (tid < 64) cell_starts(cnt, cstart);
+    __syncthreads();
+    // wave 0 plans the items while the other waves put the records in cell order
+    if (tid < 64) {
+      plan_items(cnt, cstart, istart, items, sched);
+    } else {
+      for (uint32_t i = tid - 64; i < count; i += blockDim.x - 64) {
+        const uint32_t t = tag[i];
+        if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
+      }
+    }
+    __syncthreads();
+
+    // ---- item loop: lane group g takes the schedule's entries g, 2NG-1-g,
+    // 2NG+g, ... (largest items first, snaking so the groups of a wave get items
+    // of similar size); an item's four corner rows (fp64) and its four corner
+    // sums (fp32) stay in registers
+    const uint32_t nitems = istart[kCells];
+    for (int round = 0; round * NG < (int)nitems; ++round) {
+      const int r = round * NG + ((round & 1) ? NG - 1 - grp : grp);
+      if (r >= (int)nitems) continue;
+      const int item = (int)sched[r];
+      const uint32_t desc = items[item];
+      const uint32_t s0 = desc & 0x3ffu, n = ((desc >> 10) & 0x3ffu) + 1, cell = desc >> 20;
+      const int cy = (int)cell / kEdge, cx = (int)cell - ((int)cell / kEdge) * kEdge;
+      const double x0 = (double)(px0 + cx - 1), y0 = (double)(py0 + cy - 1);
+      double V[4][VEC];
+      float acc[4][VEC];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          double pd[4];
+      for (int q = 0; q < 4; ++q) {
+        // corner q of cell (cy, cx) is tile-local pixel (cy - 1 + q/2, cx - 1 + q%2)
+        const int iy = cy - 1 + (q >> 1), ix = cx - 1 + (q & 1);
+        const bool in = iy >= 0 && ix >= 0 && py0 + iy < H && px0 + ix < W;
+        const float *src = vt + (in ? iy * kEdge + ix : kZeroRow) * RS + lane * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          V[q][i] = (double)src[i];
+          acc[q][i] = 0.0f;
+        }
+      }
+      if constexpr (G == 4) {
+        // transposed batches of kU = 4 samples: slot t of lane j holds sample
+        // k0 + (j ^ t), so after the lane-wise partial dots one quad permutation
+        // per slot hands lane j the full p_c of sample k0 + j, and every lane
+        // does the per-sample work (weights, grad_attn, grad_loc) for its own
+        // sample instead of all four lanes repeating it
+        static_assert(kU == 4, "one sample per lane of a group");
+        uint4 own[1];          // record of the lane's own sample
+        uint32_t ids[1][4];    // sample ids of the four slots
+        float g[1][4][VEC];    // grad_out rows (this lane's channels) of the four slots
+        auto fetch = [&](uint32_t k0, int buf) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            double sum = 0.0;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) sum = fma((double)g[buf][t][i], V[q][i], sum);
-            pd[t] = sum;
+            const uint32_t pos = s0 + min(k0 + (uint32_t)(lane ^ t), n - 1);
+            if (t == 0) {
+              own[buf] = reinterpret_cast<const uint4 *>(sorted)[pos];
+              ids[buf][0] = own[buf].x;
+            } else {
+              ids[buf][t] = sorted[pos].id;
+            }
+            load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(ids[buf][t], p.div_lk) * D + lane * VEC,
+                             g[buf][t]);
           }
-          P[q] = (pd[0] + dpp_move_f64<kDppQuadXor1>(pd[1])) +
-                 (dpp_move_f64<kDppQuadXor2>(pd[2]) + dpp_move_f64<kDppQuadXor3>(pd[3]));
-        }
-        const bool valid = k0 + (uint32_t)lane < n;
-        const uint32_t id = own[buf].x;
-        const float av = __uint_as_float(own[buf].y);
-        const double lx = ((double)__uint_as_float(own[buf].z) * (double)W - 0.5) - x0;
-        const double ly = ((double)__uint_as_float(own[buf].w) * (double)H - 0.5) - y0;
-        const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
-        const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
-        if (valid) {
-          const double ga = w0 * P[0] + w1 * P[1] + w2 * P[2] + w3 * P[3];
-          const double gx = (1.0 - ly) * (P[1] - P[0]) + ly * (P[3] - P[2]);
-          const double gy = (1.0 - lx) * (P[2] - P[0]) + lx * (P[3] - P[1]);
-          // the record has been read for good: it now holds the sample's results
-          reinterpret_cast<uint4 *>(sorted)[s0 + k0 + lane] =
-              make_uint4(id, __float_as_uint((float)ga),
-                         __float_as_uint((float)((double)av * (double)W * gx)),
-                         __float_as_uint((float)((double)av * (double)H * gy)));
-        }
-        const float as = valid ? av : 0.0f;
-        const float aw[4] = {as * (float)w0, as * (float)w1, as * (float)w2, as * (float)w3};
+        };
+        auto consume = [&](uint32_t k0, int buf) {
+          double P[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float at[4] = {aw[q], dpp_move<kDppQuadXor1>(aw[q]), dpp_move<kDppQuadXor2>(aw[q]),
-                               dpp_move<kDppQuadXor3>(aw[q])};
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(at[t], g[buf][t][i], acc[q][i]);
-        }
-      };
-      for (uint32_t k0 = 0; k0 < n; k0 += kU) {
-        fetch(k0, 0);
-        consume(k0, 0);
-      }
-    } else {
-      // batches of kU samples; the records and grad_out rows of the next batch
-      // are loaded before the current one is processed
-      SampleRec rec[2][kU];
-      float g[2][kU][VEC];
-      auto fetch = [&](uint32_t k0, int buf) {
-  #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          rec[buf][u] = sorted[s0 + min(k0 + u, n - 1)];
-          load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(rec[buf][u].id, p.div_lk) * D + lane * VEC,
-                           g[buf][u]);
-        }
-      };
-      auto consume = [&](uint32_t k0, int buf) {
-  #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          if (k0 + u >= n) break;
-          const SampleRec &sr = rec[buf][u];
-          const float(&gu)[VEC] = g[buf][u];
-          // fp64 partial dot products <g, V_c> over this lane's channels (exact products)
-          double pc[4];
-  #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            double sum = 0.0;
-  #pragma unroll
-            for (int i = 0; i < VEC; ++i) sum = fma((double)gu[i], V[q][i], sum);
-            pc[q] = sum;
+            double pd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              double sum = 0.0;
+#pragma unroll
+              for (int i = 0; i < VEC; ++i) sum = fma((double)g[buf][t][i], V[q][i], sum);
+              pd[t] = sum;
+            }
+            P[q] = (pd[0] + dpp_move_f64<kDppQuadXor1>(pd[1])) +
+                   (dpp_move_f64<kDppQuadXor2>(pd[2]) + dpp_move_f64<kDppQuadXor3>(pd[3]));
           }
-          const double lx = ((double)sr.u * (double)W - 0.5) - x0;
-          const double ly = ((double)sr.v * (double)H - 0.5) - y0;
+          const bool valid = k0 + (uint32_t)lane < n;
+          const uint32_t id = own[buf].x;
+          const float av = __uint_as_float(own[buf].y);
+          const double lx = ((double)__uint_as_float(own[buf].z) * (double)W - 0.5) - x0;
+          const double ly = ((double)__uint_as_float(own[buf].w) * (double)H - 0.5) - y0;
           const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
           const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
-          // grad_attn = sum_c w_c p_c ; grad_loc = (A W d/dlx, A H d/dly), all linear in the p_c
-          const double ga = group_sum_f64<G>(w0 * pc[0] + w1 * pc[1] + w2 * pc[2] + w3 * pc[3]);
-          const double gx = group_sum_f64<G>((1.0 - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
-          const double gy = group_sum_f64<G>((1.0 - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
-          const float av = sr.a;
-          if (lane == 0)
-            reinterpret_cast<uint4 *>(sorted)[s0 + k0 + u] =
-                make_uint4(sr.id, __float_as_uint((float)ga),
+          if (valid) {
+            const double ga = w0 * P[0] + w1 * P[1] + w2 * P[2] + w3 * P[3];
+            const double gx = (1.0 - ly) * (P[1] - P[0]) + ly * (P[3] - P[2]);
+            const double gy = (1.0 - lx) * (P[2] - P[0]) + lx * (P[3] - P[1]);
+            // the record has been read for good: it now holds the sample's results
+            reinterpret_cast<uint4 *>(sorted)[s0 + k0 + lane] =
+                make_uint4(id, __float_as_uint((float)ga),
                            __float_as_uint((float)((double)av * (double)W * gx)),
                            __float_as_uint((float)((double)av * (double)H * gy)));
-          const float aw[4] = {av * (float)w0, av * (float)w1, av * (float)w2, av * (float)w3};
-  #pragma unroll
-          for (int q = 0; q < 4; ++q)
-  #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw[q], gu[i], acc[q][i]);
+          }
+          const float as = valid ? av : 0.0f;
+          const float aw[4] = {as * (float)w0, as * (float)w1, as * (float)w2, as * (float)w3};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float at[4] = {aw[q], dpp_move<kDppQuadXor1>(aw[q]),
+                                 dpp_move<kDppQuadXor2>(aw[q]), dpp_move<kDppQuadXor3>(aw[q])};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+              for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(at[t], g[buf][t][i], acc[q][i]);
+          }
+        };
+        for (uint32_t k0 = 0; k0 < n; k0 += kU) {
+          fetch(k0, 0);
+          consume(k0, 0);
         }
-      };
-      fetch(0, 0);
-      for (uint32_t k0 = 0; k0 < n; k0 += 2 * kU) {
-        if (k0 + kU < n) fetch(k0 + kU, 1);
-        consume(k0, 0);
-        if (k0 + kU >= n) break;
-        if (k0 + 2 * kU < n) fetch(k0 + 2 * kU, 0);
-        consume(k0 + kU, 1);
+      } else {
+        // batches of kU samples; the records and grad_out rows of the next batch
+        // are loaded before the current one is processed
+        SampleRec rec[2][kU];
+        float g[2][kU][VEC];
+        auto fetch = [&](uint32_t k0, int buf) {
+    #pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            rec[buf][u] = sorted[s0 + min(k0 + u, n - 1)];
+            load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(rec[buf][u].id, p.div_lk) * D + lane * VEC,
+                             g[buf][u]);
+          }
+        };
+        auto consume = [&](uint32_t k0, int buf) {
+    #pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            if (k0 + u >= n) break;
+            const SampleRec &sr = rec[buf][u];
+            const float(&gu)[VEC] = g[buf][u];
+            // fp64 partial dot products <g, V_c> over this lane's channels (exact products)
+            double pc[4];
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              double sum = 0.0;
+    #pragma unroll
+              for (int i = 0; i < VEC; ++i) sum = fma((double)gu[i], V[q][i], sum);
+              pc[q] = sum;
+            }
+            const double lx = ((double)sr.u * (double)W - 0.5) - x0;
+            const double ly = ((double)sr.v * (double)H - 0.5) - y0;
+            const double w0 = (1.0 - lx) * (1.0 - ly), w1 = lx * (1.0 - ly);
+            const double w2 = (1.0 - lx) * ly, w3 = lx * ly;
+            // grad_attn = sum_c w_c p_c ; grad_loc = (A W d/dlx, A H d/dly), all linear in the p_c
+            const double ga = group_sum_f64<G>(w0 * pc[0] + w1 * pc[1] + w2 * pc[2] + w3 * pc[3]);
+            const double gx = group_sum_f64<G>((1.0 - ly) * (pc[1] - pc[0]) + ly * (pc[3] - pc[2]));
+            const double gy = group_sum_f64<G>((1.0 - lx) * (pc[2] - pc[0]) + lx * (pc[3] - pc[1]));
+            const float av = sr.a;
+            if (lane == 0)
+              reinterpret_cast<uint4 *>(sorted)[s0 + k0 + u] =
+                  make_uint4(sr.id, __float_as_uint((float)ga),
+                             __float_as_uint((float)((double)av * (double)W * gx)),
+                             __float_as_uint((float)((double)av * (double)H * gy)));
+            const float aw[4] = {av * (float)w0, av * (float)w1, av * (float)w2, av * (float)w3};
+    #pragma unroll
+            for (int q = 0; q < 4; ++q)
+    #pragma unroll
+              for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(aw[q], gu[i], acc[q][i]);
+          }
+        };
+        fetch(0, 0);
+        for (uint32_t k0 = 0; k0 < n; k0 += 2 * kU) {
+          if (k0 + kU < n) fetch(k0 + kU, 1);
+          consume(k0, 0);
+          if (k0 + kU >= n) break;
+          if (k0 + 2 * kU < n) fetch(k0 + 2 * kU, 0);
+          consume(k0 + kU, 1);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) stage[(item * 4 + q) * RS + lane * VEC + i] = acc[q][i];
+    }
+    __syncthreads();
+
+    // the next chunk's records and value rows: in flight during the two passes
+    // below (after the last chunk this loads a chunk again and leaves it unused,
+    // which keeps the registers of the loads out of the item loop)
+    loaded_pos = decode_bin_lds(p, lt, (int)ck_next.x);
+    load_chunk(ck_next, loaded_pos, tid);
+
+    // ---- per-sample results back in record order: the scatter pass wrote a
+    // bin's records in sample order, so neighbouring lanes store neighbouring
+    // ids and the stores of a sample's points merge
+    for (uint32_t i = tid; i < count; i += blockDim.x) {
+      const uint32_t t = tag[i];
+      if (t == kDropped) continue;
+      const uint4 r = reinterpret_cast<const uint4 *>(sorted)[cstart[t & 0xffu] + (t >> 8)];
+      store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + r.x, __uint_as_float(r.y));
+      store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)r.x, __uint_as_float(r.z),
+                    __uint_as_float(r.w));
+    }
+
+    // ---- every pixel of the tile and its rim sums the items of the cells it is
+    // a corner of, then goes to grad_value (interior), the rim (edge / halo) or
+    // the chunk's slot
+    for (int r = grp; r < NROWS; r += NG) {
+      const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
+      const int py = py0 + iy, px = px0 + ix;
+      if (py >= H || px >= W) continue;
+      float v[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
+      // pixel (iy, ix) is corner 00 of cell (iy+1, ix+1), 01 of (iy+1, ix),
+      // 10 of (iy, ix+1) and 11 of (iy, ix)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cy = iy + 1 - (q >> 1), cx = ix + 1 - (q & 1);
+        if (cy >= kEdge || cx >= kEdge) continue;
+        const int c = cy * kEdge + cx;
+        for (uint32_t it = istart[c]; it < istart[c + 1]; ++it) {
+          const float *src = stage + (it * 4 + q) * RS + lane * VEC;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) v[i] += src[i];
+        }
+      }
+      if (slot != kNoSlot) {
+        float *dst = a.w.slots + ((int64_t)slot * NROWS + r) * D + lane * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) dst[i] = v[i];
+      } else if (iy > 0 && ix > 0 && iy < kTile && ix < kTile) {
+        const int64_t prow = start + (int64_t)py * W + px;
+        if (prow < 0 || prow >= p.S) continue;  // inconsistent level_start_index: skip
+        T *dst = reinterpret_cast<T *>(a.grad_value) +
+                 ((row0 + (int64_t)py * W + px) * p.M + m) * D + lane * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) store_scalar<T>(dst + i, v[i]);
+      } else {
+        float *dst = a.w.rim + ((int64_t)bin * 4 * kTile + rim_row(iy, ix)) * D + lane * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) dst[i] = v[i];
       }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) stage[(item * 4 + q) * RS + lane * VEC + i] = acc[q][i];
-  }
-  __syncthreads();
-
-  // the next chunk's records and value rows: in flight during the two passes
-  // below (after the last chunk this loads a chunk again and leaves it unused,
-  // which keeps the registers of the loads out of the item loop)
-  loaded_pos = decode_bin_lds(p, lt, (int)ck_next.x);
-  load_chunk(ck_next, loaded_pos, tid);
-
-  // ---- per-sample results back in record order: the scatter pass wrote a
-  // bin's records in sample order, so neighbouring lanes store neighbouring
-  // ids and the stores of a sample's points merge
-  for (uint32_t i = tid; i < count; i += blockDim.x) {
-    const uint32_t t = tag[i];
-    if (t == kDropped) continue;
-    const uint4 r = reinterpret_cast<const uint4 *>(sorted)[cstart[t & 0xffu] + (t >> 8)];
-    store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + r.x, __uint_as_float(r.y));
-    store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)r.x, __uint_as_float(r.z),
-                  __uint_as_float(r.w));
-  }
-
-  // ---- every pixel of the tile and its rim sums the items of the cells it is
-  // a corner of, then goes to grad_value (interior), the rim (edge / halo) or
-  // the chunk's slot
-  for (int r = grp; r < NROWS; r += NG) {
-    const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
-    const int py = py0 + iy, px = px0 + ix;
-    if (py >= H || px >= W) continue;
-    float v[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
-    // pixel (iy, ix) is corner 00 of cell (iy+1, ix+1), 01 of (iy+1, ix), 10 of (iy, ix+1), 11 of (iy, ix)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cy = iy + 1 - (q >> 1), cx = ix + 1 - (q & 1);
-      if (cy >= kEdge || cx >= kEdge) continue;
-      const int c = cy * kEdge + cx;
-      for (uint32_t it = istart[c]; it < istart[c + 1]; ++it) {
-        const float *src = stage + (it * 4 + q) * RS + lane * VEC;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) v[i] += src[i];
-      }
-    }
-    if (slot != kNoSlot) {
-      float *dst = a.w.slots + ((int64_t)slot * NROWS + r) * D + lane * VEC;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) dst[i] = v[i];
-    } else if (iy > 0 && ix > 0 && iy < kTile && ix < kTile) {
-      const int64_t prow = start + (int64_t)py * W + px;
-      if (prow < 0 || prow >= p.S) continue;  // inconsistent level_start_index: skip
-      T *dst = reinterpret_cast<T *>(a.grad_value) + ((row0 + (int64_t)py * W + px) * p.M + m) * D +
-               lane * VEC;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) store_scalar<T>(dst + i, v[i]);
-    } else {
-      float *dst = a.w.rim + ((int64_t)bin * 4 * kTile + rim_row(iy, ix)) * D + lane * VEC;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) dst[i] = v[i];
-    }
-  }
-  if (cn >= nchunks) break;
-  __syncthreads();  // the next chunk reuses every LDS array
-  ck = ck_next;
+    if (cn >= nchunks) break;
+    __syncthreads();  // the next chunk reuses every LDS array
+    ck = ck_next;
   }
 }
 
