@@ -157,6 +157,34 @@ def test_empty_queries_zero_grad_value(scatter):
     assert torch.count_nonzero(gv).item() == 0
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("scatter", ["binned", "atomic"])
+def test_keys_past_the_pyramid(dtype, scatter):
+    """num_keys above the pyramid's pixel count (a padded value tensor): the extra key rows are
+    never sampled, so every output matches the unpadded call and their gradient rows are zero."""
+    wl = workloads.custom(3, 37, 3, 32, ((7, 9), (4, 5), (1, 3)), 3, dtype=dtype)
+    extra = 13
+    say(f"[parity] {extra} key rows past the pyramid (S = {wl.S} + {extra}), {dtype}, {scatter}")
+    x = workloads.make_inputs(wl, seed=31)
+    pad = np.random.default_rng(32).standard_normal((wl.B, extra, wl.M, wl.D)).astype(np.float32)
+    if dtype == "bf16":
+        pad = workloads.round_to_bf16(pad)
+    x["value"] = np.concatenate([x["value"], pad], axis=1)
+    o = parity.run_oracle(x)
+    assert np.all(o["grad_value"][:, -extra:] == 0)
+    # garbage in the gradient buffer first: the padded rows must be written, not skipped
+    t = parity.upload(x)
+    gv = torch.full_like(t["value"], float("nan"))
+    out = msda.msda_forward(*parity.operands(t))
+    gv, gl, ga = msda.msda_backward(*parity.operands(t), t["grad_out"], grad_value=gv,
+                                    scatter=scatter, spatial_shapes_host=x["spatial_shapes"])
+    torch.cuda.synchronize()
+    g = {k: v.double().cpu().numpy() for k, v in
+         dict(out=out, grad_value=gv, grad_loc=gl, grad_attn=ga).items()}
+    assert np.all(g["grad_value"][:, -extra:] == 0)
+    gate(x, g, o)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("scatter", ["binned", "atomic"])
 def test_outputs_are_overwritten_and_deterministic(dtype, scatter):
