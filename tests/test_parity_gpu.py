@@ -157,6 +157,43 @@ def test_empty_queries_zero_grad_value(scatter):
     assert torch.count_nonzero(gv).item() == 0
 
 
+def test_batches_split_across_launches():
+    """Five 268 MB batch images (48 heads of 64 channels, fp32): more than 2^30 bytes of value,
+    so the library runs the batch in two launches (4 + 1 images), for both scatters.  Each
+    image is checked against the oracle on its own; the pyramid is smaller than num_keys, so
+    the rows past it are zeroed in both launches."""
+    wl = workloads.custom(5, 40, 48, 64, ((128, 128), (64, 64)), 4)
+    extra = 21845 - wl.S
+    say(f"[parity] batch over two launches: B=5, S={wl.S}+{extra}, M=48, D=64 (inputs and oracle)")
+    x = workloads.make_inputs(wl, seed=41)
+    pad = np.random.default_rng(42).standard_normal((wl.B, extra, wl.M, wl.D))
+    x["value"] = np.concatenate([x["value"], pad.astype(np.float32)], axis=1)
+    assert x["value"].nbytes > 2**30 and 4 * x["value"][0].nbytes < 2**30
+    per_image = []
+    for b in range(wl.B):
+        xb = {k: (v[b:b + 1] if k in parity.FLOAT_KEYS else v) for k, v in x.items()}
+        per_image.append((xb, parity.run_oracle(xb)))
+    t = parity.upload(x)
+    for scatter in ("binned", "atomic"):
+        say(f"  scatter={scatter}")
+        gv = torch.full_like(t["value"], float("nan"))
+        out = msda.msda_forward(*parity.operands(t))
+        gv, gl, ga = msda.msda_backward(*parity.operands(t), t["grad_out"], grad_value=gv,
+                                        scatter=scatter, spatial_shapes_host=x["spatial_shapes"])
+        torch.cuda.synchronize()
+        for b, (xb, o) in enumerate(per_image):
+            g = {k: v[b:b + 1].double().cpu().numpy() for k, v in
+                 dict(out=out, grad_value=gv, grad_loc=gl, grad_attn=ga).items()}
+            assert np.all(g["grad_value"][:, -extra:] == 0)
+            # grad_value on the (pixel, head) rows either side touches; every other element
+            # is zero on both sides, so this is the full element-by-element comparison
+            rows = (np.any(o["grad_value"] != 0, axis=(0, 3)) |
+                    np.any(g["grad_value"] != 0, axis=(0, 3)))
+            g["grad_value"] = g["grad_value"][:, rows]
+            gate(xb, g, dict(o, grad_value=o["grad_value"][:, rows]))
+        del gv, out, gl, ga
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("scatter", ["binned", "atomic"])
 def test_keys_past_the_pyramid(dtype, scatter):
