@@ -159,7 +159,8 @@ def test_empty_queries_zero_grad_value(scatter):
 
 def test_batches_split_across_launches():
     """Five 268 MB batch images (48 heads of 64 channels, fp32): more than 2^30 bytes of value,
-    so the library runs the batch in two launches (4 + 1 images), for both scatters.  Each
+    so the library runs the batch in two launches (4 + 1 images), for both scatters and the
+    softmax method.  Each
     image is checked against the oracle on its own; the pyramid is smaller than num_keys, so
     the rows past it are zeroed in both launches."""
     wl = workloads.custom(5, 40, 48, 64, ((128, 128), (64, 64)), 4)
@@ -192,6 +193,23 @@ def test_batches_split_across_launches():
             g["grad_value"] = g["grad_value"][:, rows]
             gate(xb, g, dict(o, grad_value=o["grad_value"][:, rows]))
         del gv, out, gl, ga
+    # the softmax method over the same two launches (binned scatter, L*K = 8: the scatter
+    # pass forms the weights itself)
+    say("  softmax method")
+    ops = (t["value"], t["spatial_shapes"], t["level_start_index"], t["sampling_locations"],
+           t["attention_logits"])
+    out = msda.msda_forward_softmax(*ops)
+    gv, gl, gz = msda.msda_backward_softmax(*ops, t["grad_out"],
+                                            spatial_shapes_host=x["spatial_shapes"])
+    torch.cuda.synchronize()
+    for b, (xb, _) in enumerate(per_image):
+        o = parity.run_oracle_softmax(xb)
+        g = {k: v[b:b + 1].double().cpu().numpy() for k, v in
+             dict(out=out, grad_value=gv, grad_loc=gl, grad_logits=gz).items()}
+        rows = (np.any(o["grad_value"] != 0, axis=(0, 3)) |
+                np.any(g["grad_value"] != 0, axis=(0, 3)))
+        g["grad_value"] = g["grad_value"][:, rows]
+        gate_softmax(xb, g, dict(o, grad_value=o["grad_value"][:, rows]))
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
