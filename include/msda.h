@@ -40,7 +40,9 @@
  *     the call returns.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
  *     null stream) and the call returns without waiting for it.  Buffers must
- *     stay valid until that work completes.
+ *     stay valid until that work completes.  A workspace holds the call's
+ *     intermediate state until then: calls whose work may overlap (on
+ *     different streams) need workspaces of their own.
  *   - Outputs are overwritten, never accumulated into.
  *   - Errors: a non-OK status is returned before anything is enqueued when the
  *     arguments are rejected; msda_last_error() then describes the reason.
