@@ -636,9 +636,35 @@ def main(argv=None) -> int:
             "adds_per_s": round(adds / (atomic_us * 1e-6), 1),
             "ceiling_adds_per_s": round(src.numel() / (ceil_us * 1e-6), 1),
             "frac_of_ceiling": round(adds / (atomic_us * 1e-6) / (src.numel() / (ceil_us * 1e-6)), 4),
-            "how": "msda_backward with the atomic scatter (fp32 atomics into grad_value), median "
-                   "of 5 calls; ceiling = torch index_add_ of 2^22 random 32-float rows into "
-                   "2^18 rows, median of 5"}
+            "how": "msda_backward with the atomic scatter (fp32 atomics into grad_value, or into "
+                   "an fp32 workspace then a cast for half-precision data), median of 5 calls; "
+                   "ceiling = torch index_add_ of 2^22 random 32-float rows into 2^18 rows, "
+                   "median of 5"}
+        if wl.dtype != "fp32":
+            # the same scatter with the data type as accumulator: packed two-element
+            # atomics straight into grad_value instead of an fp32 workspace and a cast
+            log("[bench] atomic scatter with the packed half-precision accumulator")
+            gv_p = torch.empty_like(t0["value"])
+
+            def bwd_packed(t):
+                msda.msda_backward(*ops(t), t["grad_out"], grad_value=gv_p, grad_loc=gl,
+                                   grad_attn=ga, accum_dtype=t0["value"].dtype,
+                                   scatter="atomic", stream=stream)
+
+            packed_us = call_us(bwd_packed, n=5)
+            bwd_atomic(t0)
+            bwd_packed(t0)
+            torch.cuda.synchronize()
+            ref = gv_a.double()
+            rel_l2 = ((gv_p.double() - ref).norm() / ref.norm()).item()
+            extras["atomic_scatter"]["packed_accumulator"] = {
+                "bwd_us": packed_us,
+                "pair_adds_per_s": round(adds / 2 / (packed_us * 1e-6), 1),
+                "rel_l2_vs_fp32_accumulator": rel_l2,
+                "how": f"msda_backward with the atomic scatter and accum_dtype = {wl.dtype} "
+                       "(packed two-element atomics), median of 5 calls; rel_l2 = |gv_packed - "
+                       "gv_fp32| / |gv_fp32| over grad_value on one batch"}
+            del gv_p
         del rows, idx, src, gv_a
 
         log("[bench] HIP graph replay of a small (launch-bound) step")

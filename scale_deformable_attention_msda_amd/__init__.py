@@ -339,8 +339,8 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
     """Gradients of <out, grad_out> w.r.t. value, sampling_locations, attention_weights.
 
     scatter: "binned" (default; destination-sorted, LDS accumulation, fp32) or "atomic"
-    (device-scope atomics).  accum_dtype: torch.float32 (default) or torch.bfloat16
-    (atomic scatter of bf16 data only: packed-bf16 atomics).  spatial_shapes_host: the
+    (device-scope atomics).  accum_dtype: torch.float32 (default) or the data type
+    (atomic scatter of bf16 or fp16 data only: packed two-element atomics).  spatial_shapes_host: the
     level shapes on the host (array-like [L, 2]); read from spatial_shapes when omitted.
     A workspace is allocated here when none is given."""
     return _backward("msda_backward", value, spatial_shapes, level_start_index,
