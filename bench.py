@@ -47,11 +47,16 @@ def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
     For the encoder workloads every pyramid pixel is the reference point of a
     query and offsets are a few pixels, so every value row is touched and the
     whole value tensor counts.  Per-sample figures: loc 2 elements, attn 1
-    element; the binned path also writes and reads one 16-byte record
-    (id, location, weight) per sample.  The fill kernel clears the grad_value
-    accumulator on the atomic path and the per-bin counters (8 stripes, one
-    64-byte line each, per 8x8 tile of every batch and head, plus 24 bytes per
-    256 bins of plan status) on the binned path."""
+    element.  Only the operator's own tensors are compulsory: the forward reads
+    value, loc and attn and writes out (28 B per sample at the encoder size);
+    the backward reads value, loc, attn and grad_out and writes grad_value,
+    grad_loc and grad_attn (48 B per sample).  The binned backward's dominant
+    kernel (bin_tile) is charged the whole backward's compulsory bytes; the
+    16-byte records it and the scatter pass exchange through the workspace are
+    reported apart ("bin_records"), as are the fill kernel's bytes (the
+    grad_value accumulator on the atomic path; on the binned path the per-bin
+    counters: 8 stripes, one 64-byte line each, per 8x8 tile of every batch and
+    head, plus 24 bytes per 256 bins of plan status)."""
     elt = 4 if wl.dtype == "fp32" else 2
     B, S, Q, M, D, L, K = wl.B, wl.S, wl.num_queries, wl.M, wl.D, wl.L, wl.K
     n = B * Q * M * L * K
@@ -79,55 +84,91 @@ def bytes_model(wl: workloads.Workload, scatter: str = "binned") -> dict:
         "fwd_softmax": value + loc + attn + out,
         "softmax_rows": 2 * attn,
         "softmax_grad_rows": 3 * attn,
-        # atomic backward: value, loc, attn, grad_out read; grad_value, grad_loc, grad_attn written
+        # the backward's compulsory bytes: value, loc, attn, grad_out read; grad_value,
+        # grad_loc, grad_attn written
+        "bwd": value + loc + attn + out + value + loc + attn,
         "bwd_atomic": value + loc + attn + out + value + loc + attn,
         "zero": value if scatter == "atomic" else counters,
-        # binned passes
+        # binned passes (bin_tile: the whole backward's compulsory bytes)
         "bin_count": loc,
-        "bin_scatter": loc + attn + recs,
-        "bin_tile": value + recs + out + value + loc + attn,
+        "bin_scatter": loc + attn,
+        "bin_tile": value + loc + attn + out + value + loc + attn,
         "bin_merge": 0,
         "bin_plan": 0,
+        "bin_records": recs,
+        "corner_rows": n * 4 * D * elt,
         "value": value,
     }
 
 
+KERNEL_SOURCES = ("msda_kernels.hip", "msda_binned.hip", "msda_fwd_binned.hip", "msda_device.h",
+                  "msda_launch.h")
+
+
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources: measured traffic is void once they change."""
+    """Digest of the operator's kernel sources: measured traffic is void once they change."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scale_deformable_attention_msda_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(path: str, workload: str, scatter: str, kernel: str):
-    """HBM bytes per launch of `kernel` from a profiles/ summary, or None.
+def read_counters(path: str, workload: str, scatter: str) -> dict:
+    """Per-kernel counter figures from a profiles/ summary: {kernel: {"traffic": bytes per
+    launch, "l2_hit": fraction}}, or {} when the summary is missing or was taken from other
+    kernel sources than the current ones.
 
-    The summary holds lines `sources: <digest>` and
-    `traffic <workload>/<scatter>/<kernel>: <bytes>`; figures taken from other
-    sources than the current ones are ignored."""
+    The summary holds lines `sources: <digest>`, `traffic <workload>/<scatter>/<kernel>: <bytes>`
+    and `l2hit <workload>/<scatter>/<kernel>: <fraction>`."""
     if not os.path.exists(path):
-        return None
-    digest, key, value = None, f"traffic {workload}/{scatter}/{kernel}:", None
+        return {}
+    digest, out = None, {}
     for line in open(path):
         line = line.strip()
         if line.startswith("sources:"):
             digest = line.split(":", 1)[1].strip()
-        elif line.startswith(key):
-            try:
-                value = int(float(line.split(":", 1)[1].split()[0]))
-            except (ValueError, IndexError):
-                value = None
-    if digest != kernel_source_digest():
-        return None
-    return value
+            continue
+        for tag, field, conv in (("traffic", "traffic", lambda v: int(float(v))),
+                                 ("l2hit", "l2_hit", float)):
+            pre = f"{tag} {workload}/{scatter}/"
+            if line.startswith(pre) and ":" in line:
+                kernel, val = line[len(pre):].split(":", 1)
+                try:
+                    out.setdefault(kernel.strip(), {})[field] = conv(val.split()[0])
+                except (ValueError, IndexError):
+                    pass
+    return out if digest == kernel_source_digest() else {}
 
 
-def cpu_baseline(x: dict, budget_s: float = 10.0) -> dict:
+# stated tolerances (rtol, atol): forward and backward fp32, bf16, fp16
+TOLERANCES = {"fp32": {"out": (1e-5, 1e-6), "grad": (1e-4, 1e-5)},
+              "bf16": {"out": (2e-2, 2e-2), "grad": (2e-2, 2e-2)},
+              "fp16": {"out": (2.5e-3, 2.5e-3), "grad": (2.5e-3, 2.5e-3)}}
+
+
+def parity_report(gpu: dict, ref: dict, dtype: str) -> dict:
+    """Largest errors of the GPU outputs against the oracle's, and the count of elements
+    outside the stated tolerance (|gpu - oracle| <= atol + rtol |oracle|)."""
+    rep = {}
+    for name, want in ref.items():
+        got = np.asarray(gpu[name], dtype=np.float64).ravel()
+        want = np.asarray(want, dtype=np.float64).ravel()
+        rtol, atol = TOLERANCES[dtype]["out" if name == "out" else "grad"]
+        err = np.abs(got - want)
+        bad = ~(err <= atol + rtol * np.abs(want))
+        rel = err / np.maximum(np.abs(want), atol)
+        rep[name] = {"max_abs_err": float(np.max(err)), "max_rel_err": float(np.max(rel)),
+                     "outside_tol": int(bad.sum()), "elements": int(got.size),
+                     "rtol": rtol, "atol": atol}
+    return rep
+
+
+def cpu_baseline(x: dict, budget_s: float = 10.0, gpu: dict | None = None) -> dict:
+    """The oracle timed on the host over the whole workload; with `gpu` (the library's
+    outputs for the same inputs) the oracle's results also give the run's parity figures."""
     import oracle
 
     orc = oracle.default()
@@ -135,11 +176,13 @@ def cpu_baseline(x: dict, budget_s: float = 10.0) -> dict:
             x["attention_weights"])
     times = []
     t_end = time.perf_counter() + budget_s
+    res = None
     while not times or (time.perf_counter() < t_end and len(times) < 20):
         t0 = time.perf_counter()
-        orc.forward(*args)
-        orc.backward(*args, x["grad_out"])
+        out = orc.forward(*args)
+        grads = orc.backward(*args, x["grad_out"])
         times.append(time.perf_counter() - t0)
+        res = (out, grads)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -148,10 +191,59 @@ def cpu_baseline(x: dict, budget_s: float = 10.0) -> dict:
                 break
     except OSError:
         pass
-    return {"value": float(np.mean(times)) * 1e6, "unit": "us/call", "cores": orc.threads(),
+    base = {"value": float(np.mean(times)) * 1e6, "unit": "us/call", "cores": orc.threads(),
             "kind": "oracle",
             "sample": f"the whole workload, fp64 oracle forward+backward, {len(times)} calls "
                       f"(host: {cpu}, {os.cpu_count()} logical CPUs, {platform.machine()})"}
+    if gpu is not None:
+        out, (gv, gl, ga) = res
+        base["parity"] = parity_report(gpu, {"out": out, "grad_value": gv, "grad_loc": gl,
+                                             "grad_attn": ga}, x["dtype"])
+    return base
+
+
+CLOCK_GHZ = 2.4  # MI355X peak engine clock
+CUS = 256
+
+
+def microbenchmarks(msda, dev, stream) -> dict:
+    """Ceilings of the memory paths on this machine, from the library's microbenchmarks
+    (include/msda_bench.h): streaming read and copy of 1 GiB, fp32 and packed-bf16 global
+    atomics over whole 128-byte rows (random over 256 MiB, and piled on a 64 KiB hot set),
+    gathers of random 128-byte rows from the vector L1 (16 KiB span), an L2-sized span
+    (2 MiB), a value-tensor-sized span (64 MiB, L2 / MALL) and HBM (1 GiB), from LDS, and
+    LDS fp32 atomics.  B/clk/CU uses the 2.4 GHz peak clock and 256 CUs."""
+    import torch
+
+    buf = torch.empty(2 ** 30 + 2 ** 20, dtype=torch.uint8, device=dev)
+
+    def run(kind, span=0, reps=10):
+        ms, units = msda.msda_microbench_run(kind, buf, span=span, reps=reps, stream=stream)
+        return units / (ms * 1e-3)
+
+    r = {}
+    r["read_gbps"] = round(run("read") / 1e9, 1)
+    r["copy_gbps"] = round(run("copy") / 1e9, 1)
+    r["atomic_f32_spread_gops"] = round(run("atomic_f32", 2 ** 28) / 1e9, 1)
+    r["atomic_f32_hot_gops"] = round(run("atomic_f32", 2 ** 16) / 1e9, 1)
+    r["atomic_pk_bf16_spread_gpairs"] = round(run("atomic_pk_bf16", 2 ** 28) / 1e9, 1)
+    r["atomic_pk_bf16_hot_gpairs"] = round(run("atomic_pk_bf16", 2 ** 16) / 1e9, 1)
+    per_clk = CUS * CLOCK_GHZ * 1e9
+    for name, span in (("l1", 2 ** 14), ("l2", 2 ** 21), ("value_span", 2 ** 26), ("hbm", 2 ** 30)):
+        bps = run("gather_global", span)
+        r[f"gather_{name}_gbps"] = round(bps / 1e9, 1)
+        r[f"gather_{name}_b_per_clk_cu"] = round(bps / per_clk, 1)
+    bps = run("gather_lds")
+    r["gather_lds_gbps"] = round(bps / 1e9, 1)
+    r["gather_lds_b_per_clk_cu"] = round(bps / per_clk, 1)
+    r["lds_atomic_f32_per_clk_cu"] = round(run("lds_atomic_f32") / per_clk, 3)
+    r["how"] = ("msda_microbench_run (libmsda.so), mean of 10 launches after one warm-up; "
+                "read / copy of 1 GiB (L2 and MALL hold 288 MB, so both stream from HBM); "
+                "atomics: whole 128-byte rows per instruction, rows random over 256 MiB "
+                "(spread) or 64 KiB (hot); gathers: 8 lanes x 16 B per random 128-byte row, "
+                "8 rows in flight per lane, 4 FMAs per 16 B")
+    del buf
+    return r
 
 
 def cpu_baseline_single_thread(workload_id: int, seed: int, budget_s: float = 30.0) -> dict | None:
@@ -550,29 +642,23 @@ def main(argv=None) -> int:
                                             batches=args.rotate),
                              "warm": dict(percentiles(warm), steps=20),
                              "cold": dict(percentiles(cold), steps=20)}
-        # achievable HBM rates on this machine: a streaming read (sum of 1 GiB) and a copy
-        src = torch.randn(2 ** 28, device=dev)
-        dst = torch.empty_like(src)
+        # per-kernel durations with L2 and MALL evicted before every step
+        msda.msda_profile_select(None)
+        msda.msda_profile_start(64 * 10)
+        for i in range(10):
+            scratch.fill_(1.0)
+            step(i)
+        torch.cuda.synchronize()
+        cold_k = {}
+        for name, ms in msda.msda_profile_stop(64 * 10):
+            cold_k.setdefault(name, []).append(ms)
+        extras["regimes"]["cold"]["kernels_us"] = {n: round(float(np.mean(v)) * 1e3, 3)
+                                                   for n, v in cold_k.items()}
+        del scratch
 
-        def rate(fn, nbytes):
-            ts = []
-            for _ in range(6):
-                scratch.fill_(0.0)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                e1.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e-3)
-            return nbytes / float(np.median(ts[1:])) / 1e9
-
-        rows = src.view(2 ** 17, -1)
-        extras["achievable"] = {"read_gbps": round(rate(lambda: rows.sum(1), src.numel() * 4), 1),
-                                "copy_gbps": round(rate(lambda: dst.copy_(src), src.numel() * 8), 1),
-                                "how": "torch row sums of 1 GiB fp32 in 131072 rows (read; the "
-                                       "fastest torch reduction shape measured) and a copy of 1 GiB "
-                                       "(read + write), L2/MALL evicted before each, median of 5"}
-        del scratch, src, dst
+        # what the box's memory paths reach (the library's own microbenchmarks)
+        log("[bench] memory-path microbenchmarks")
+        extras["achievable"] = microbenchmarks(msda, dev, stream)
 
         # the softmax method, fused against unfused: each call alone, over the rotated batches
         def call_us(fn, n=20, bl=None):
@@ -626,20 +712,17 @@ def main(argv=None) -> int:
                                scatter="atomic", stream=stream)
 
         atomic_us = call_us(bwd_atomic, n=5)
-        rows = torch.zeros(2 ** 18, 32, device=dev)
-        idx = torch.randint(0, rows.shape[0], (2 ** 22,), device=dev)
-        src = torch.ones(idx.numel(), 32, device=dev)
-        ceil_us = call_us(lambda t: rows.index_add_(0, idx, src), n=5)
+        ceil = extras["achievable"]["atomic_f32_spread_gops"] * 1e9
         extras["atomic_scatter"] = {
             "bwd_us": atomic_us,
             "element_adds": adds,
             "adds_per_s": round(adds / (atomic_us * 1e-6), 1),
-            "ceiling_adds_per_s": round(src.numel() / (ceil_us * 1e-6), 1),
-            "frac_of_ceiling": round(adds / (atomic_us * 1e-6) / (src.numel() / (ceil_us * 1e-6)), 4),
+            "ceiling_adds_per_s": round(ceil, 1),
+            "frac_of_ceiling": round(adds / (atomic_us * 1e-6) / ceil, 4),
             "how": "msda_backward with the atomic scatter (fp32 atomics into grad_value, or into "
                    "an fp32 workspace then a cast for half-precision data), median of 5 calls; "
-                   "ceiling = torch index_add_ of 2^22 random 32-float rows into 2^18 rows, "
-                   "median of 5"}
+                   "ceiling = the atomic_f32 microbenchmark (whole 128-byte rows, random over "
+                   "256 MiB)"}
         if wl.dtype != "fp32":
             # the same scatter with the data type as accumulator: packed two-element
             # atomics straight into grad_value instead of an fp32 workspace and a cast
@@ -665,7 +748,7 @@ def main(argv=None) -> int:
                        "(packed two-element atomics), median of 5 calls; rel_l2 = |gv_packed - "
                        "gv_fp32| / |gv_fp32| over grad_value on one batch"}
             del gv_p
-        del rows, idx, src, gv_a
+        del gv_a
 
         log("[bench] HIP graph replay of a small (launch-bound) step")
         extras["graph"] = {"tiny": graph_comparison(dev, 0), "decoder": graph_comparison(dev, 1)}
@@ -713,9 +796,17 @@ def main(argv=None) -> int:
     dom_us = float(np.mean(dom_ms)) * 1e3  # live, over the timed region
     dom["us_timed_region"] = round(dom_us, 3)
     achieved = dom["alg_bytes"] / (dom_us * 1e-6) / 1e9
-    traffic = read_traffic(args.traffic_file, wl.name, args.scatter, dom_name)
+    counters = read_counters(args.traffic_file, wl.name, args.scatter)
+    for name, k in kernels.items():
+        c = counters.get(name, {})
+        if "traffic" in c:
+            k["measured_bytes"] = c["traffic"]
+            k["measured_gbps"] = round(c["traffic"] / (k["us"] * 1e-6) / 1e9, 1)
+        if "l2_hit" in c:
+            k["l2_hit"] = c["l2_hit"]
+    traffic = counters.get(dom_name, {}).get("traffic")
     traffic_gbps = round(traffic / (dom_us * 1e-6) / 1e9, 1) if traffic else None
-    step_bytes = bm["fwd"] + (bm["bwd_atomic"] if args.scatter == "atomic" else bm["bin_tile"])
+    step_bytes = bm["fwd"] + bm["bwd"]
     res = {
         "metric": METRIC,
         "value": round(ms_per_step * 1e3, 3),
@@ -743,6 +834,14 @@ def main(argv=None) -> int:
         "queries_per_s": round(wl.B * wl.num_queries / (ms_per_step * 1e-3), 1),
         "fwd_hbm_gbps": round(bm["fwd"] / (fwd_us * 1e-6) / 1e9, 1),
         "fwd_hbm_frac": round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        # the forward's target is 40% of the HBM peak: this is its fraction of that target
+        "fwd_frac_of_target": round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBPS / 0.40, 4),
+        "bwd_hbm_gbps": round(bm["bwd"] / (bwd_us * 1e-6) / 1e9, 1),
+        "bwd_hbm_frac": round(bm["bwd"] / (bwd_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_model": {"fwd": bm["fwd"], "bwd": bm["bwd"], "samples": bm["samples"],
+                        "fwd_per_sample": round(bm["fwd"] / bm["samples"], 2),
+                        "bwd_per_sample": round(bm["bwd"] / bm["samples"], 2),
+                        "corner_rows": bm["corner_rows"], "bin_records": bm["bin_records"]},
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": dom_name, "kernel_us": round(dom_us, 3),
                      "launches": len(dom_ms), "achieved": round(achieved, 1),
@@ -752,11 +851,30 @@ def main(argv=None) -> int:
     }
     res.update(extras)
     if "achievable" in extras:
-        res["fwd_frac_of_read"] = round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 /
-                                        extras["achievable"]["read_gbps"], 4)
+        ach = extras["achievable"]
+        res["fwd_frac_of_read"] = round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 / ach["read_gbps"], 4)
+        # the forward's corner-row gather against the gather ceilings of the box
+        rate = bm["corner_rows"] / (fwd_us * 1e-6) / 1e9
+        res["fwd_corner_gather"] = {
+            "gbps": round(rate, 1),
+            "b_per_clk_cu": round(rate * 1e9 / (CUS * CLOCK_GHZ * 1e9), 1),
+            "frac_of_l1_gather": round(rate / ach["gather_l1_gbps"], 4),
+            "frac_of_lds_gather": round(rate / ach["gather_lds_gbps"], 4),
+            "us_at_l1_gather": round(bm["corner_rows"] / (ach["gather_l1_gbps"] * 1e9) * 1e6, 1),
+            "us_at_lds_gather": round(bm["corner_rows"] / (ach["gather_lds_gbps"] * 1e9) * 1e6, 1)}
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(host[0])
+        # the library's outputs for batch 0, compared with the oracle's in the same leg
+        t = batches[0]
+        if args.method == "softmax":
+            gpu_out = None
+        else:
+            fwd_plain(t)
+            bwd_plain(t)
+            torch.cuda.synchronize()
+            gpu_out = {"out": out.double().cpu().numpy(), "grad_value": gv.double().cpu().numpy(),
+                       "grad_loc": gl.double().cpu().numpy(), "grad_attn": ga.double().cpu().numpy()}
+        res["cpu_baseline"] = cpu_baseline(host[0], gpu=gpu_out)
         one = cpu_baseline_single_thread(args.workload, workloads.BASE_SEED + args.workload)
         if one is not None:
             res["cpu_baseline"]["single_thread"] = one

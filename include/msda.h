@@ -62,7 +62,8 @@
  *     none of whose four corners lies inside its level contributes nothing
  *     and receives zero gradients.
  *   - Reentrant and thread-safe: no global mutable state apart from the
- *     thread-local error string.
+ *     thread-local error string (and the thread-local test hook of
+ *     msda_bench.h).
  */
 #ifndef MSDA_H
 #define MSDA_H
@@ -201,7 +202,9 @@ typedef enum {
 
 /*
  * Bytes of device workspace msda_backward needs for these sizes, dtype,
- * accumulator and scatter:
+ * accumulator and scatter (the pages' own backward needs none: the DeformOps
+ * page, introduction, "Zero-buffer kernels"; the binned scatter trades this
+ * buffer for having no floating-point atomics):
  *   BINNED:            bin tables, sorted sample ids and tile-rim partials
  *                      (planned from spatial_shapes_host, [L,2] on the host);
  *   ATOMIC, BF16 or
@@ -216,7 +219,14 @@ size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
                                      const int64_t *spatial_shapes_host);
 
 /*
- * Backward of <out, grad_out>.  Writes (overwrites) all three gradients:
+ * Backward of <out, grad_out>.  The gradients are those of the operator of
+ * "1. Deformable attention, from scratch" (sections "The equation, term by
+ * term" and "Bilinear interpolation: reading between the pixels"); the pages
+ * do not print them, they follow by differentiating its sum.  grad_value is
+ * the scattered accumulation "Efficient Multi-Scale Deformable Attention on
+ * GPUs" describes in section "The backward pass is an atomics problem"; the
+ * fp32 accumulator switch is the one of the DeformOps page, section "Backend
+ * selection".  Writes (overwrites) all three gradients:
  *   grad_value[b, row, m, :] = sum over the samples whose bilinear corner is
  *                              `row` of A * corner_weight * grad_out[b,q,m,:]
  *                              (zero for rows no sample touches);
@@ -242,6 +252,11 @@ size_t msda_backward_workspace_bytes(const msda_dims *dims, msda_dtype dtype,
  * workspace must hold at least msda_backward_workspace_bytes() bytes
  * (16-byte aligned; NULL when that is 0).  Its contents on entry do not
  * matter and are clobbered.
+ * Device-side checks (BINNED only; the host cannot see device data without a
+ * sync): the kernels compare spatial_shapes and level_start_index with the
+ * plan made from spatial_shapes_host, and the plan pass bounds its waits on
+ * earlier blocks.  When a check fails, all three gradients are written as NaN
+ * and msda_backward_flags() reports which check failed.
  */
 msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           const int64_t *level_start_index, const void *sampling_locations,
@@ -288,38 +303,37 @@ msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shap
                                   const int64_t *spatial_shapes_host, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
-/*
- * Kernel timing for benchmarks.  Between msda_profile_start() and
- * msda_profile_stop() on one thread, every kernel this library enqueues from
- * that thread is bracketed by two HIP events recorded on its stream.
- * msda_profile_stop() waits for the last recorded event, copies at most `max`
- * records (kernel name, milliseconds between its events) into `out`, ends the
- * session and returns the number of kernels recorded (which may exceed `max`),
- * or -1 when a HIP event call failed.  Records past `capacity` are dropped.
- * The events are created by the library (host-side HIP objects, no device
- * memory) and kept for reuse until the process ends.
- */
-typedef struct {
-    const char *name; /* static string, e.g. "fwd_kernel<f32,32>" */
-    float ms;
-} msda_kernel_time;
 
-msda_status msda_profile_start(int capacity);
-int msda_profile_stop(msda_kernel_time *out, int max);
-/*
- * Restrict the sessions of this thread to the kernels named `name` (the names
- * msda_profile_stop reports); NULL or "" records every kernel again.  Kernels
- * left out get no events at all, so a session can time one kernel while
- * disturbing the others as little as possible.  The events are created with
- * hipEventDisableSystemFence: recording one does not write back or invalidate
- * caches.
- */
-void msda_profile_select(const char *name);
+/* Flags of msda_backward_flags(). */
+#define MSDA_BWD_SHAPES_MISMATCH 1u /* device spatial_shapes or level_start_index differ from
+                                       spatial_shapes_host (or its prefix sums) */
+#define MSDA_BWD_PLAN_EXPIRED 2u    /* a plan block stopped waiting for an earlier one */
 
-/* Static description of a status code. */
+/*
+ * The device-side check flags a BINNED msda_backward (softmax_method = 0) or
+ * msda_backward_softmax (softmax_method = 1) call left in its workspace: 0 when
+ * its gradients are valid, else MSDA_BWD_* bits (its gradients are then NaN).
+ * Arguments as for the call being checked (the same dims, dtypes, scatter,
+ * spatial_shapes_host and workspace).  Enqueues a 4-byte copy on `stream`,
+ * after the call's work, and waits for it.  With the ATOMIC scatter, or a call
+ * without samples, *flags is 0 and nothing is enqueued.  Errors as for the
+ * workspace-size functions, or MSDA_ERR_HIP.
+ */
+msda_status msda_backward_flags(const msda_dims *dims, msda_dtype dtype, msda_dtype accum_dtype,
+                                msda_scatter scatter, int softmax_method,
+                                const int64_t *spatial_shapes_host, const void *workspace,
+                                size_t workspace_bytes, void *stream, uint32_t *flags);
+
+/*
+ * Static description of a status code.  As the DeformOps page (section
+ * "Backend selection") lists every rejected candidate with its reason, every
+ * rejected call here returns a status and leaves its reason for
+ * msda_last_error().
+ */
 const char *msda_status_string(msda_status status);
 
-/* Thread-local detail of this thread's last non-OK return ("" if none). */
+/* Thread-local detail of this thread's last non-OK return ("" if none): which
+ * argument or limit rejected the call (DeformOps page, "Backend selection"). */
 const char *msda_last_error(void);
 
 #ifdef __cplusplus

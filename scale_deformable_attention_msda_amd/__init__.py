@@ -17,8 +17,12 @@ The functions keep the C names:
                   -> (grad_value, grad_loc, grad_attn)
     msda_backward_workspace_bytes(dims, dtype, accum_dtype, scatter,
                                   spatial_shapes_host) -> int
+    msda_backward_flags(dims, dtype, accum_dtype, scatter, softmax_method,
+                        spatial_shapes_host, workspace, stream=None) -> int
     msda_status_string(status) -> str
     msda_last_error() -> str
+Measurement hooks (include/msda_bench.h): msda_profile_start / _select / _stop,
+msda_microbench_run, msda_test_set_plan_wait_limit.
 Shapes follow chapter 1 of the msda-triton course ("The equation, term by
 term"): value (B, S, M, D), spatial_shapes (L, 2) rows (H, W),
 level_start_index (L,), sampling_locations (B, Q, M, L, K, 2),
@@ -106,6 +110,16 @@ def load_library(path: str = LIB_PATH):
     lib.msda_profile_stop.restype = ctypes.c_int
     lib.msda_profile_select.argtypes = [ctypes.c_char_p]
     lib.msda_profile_select.restype = None
+    lib.msda_backward_flags.argtypes = [dims_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, vp, vp, ctypes.c_size_t, vp,
+                                        ctypes.POINTER(ctypes.c_uint32)]
+    lib.msda_backward_flags.restype = ctypes.c_int
+    lib.msda_test_set_plan_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.msda_test_set_plan_wait_limit.restype = None
+    lib.msda_microbench_run.argtypes = [ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_size_t,
+                                        ctypes.c_int, vp, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double)]
+    lib.msda_microbench_run.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -137,6 +151,31 @@ def msda_profile_stop(max_records: int = 1 << 16) -> list:
     if n < 0:
         raise RuntimeError("msda_profile_stop: a HIP event call failed")
     return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(min(n, max_records))]
+
+
+MSDA_BWD_SHAPES_MISMATCH = 1
+MSDA_BWD_PLAN_EXPIRED = 2
+MICROBENCH = {"read": 0, "copy": 1, "atomic_f32": 2, "atomic_pk_bf16": 3, "gather_global": 4,
+              "gather_lds": 5, "lds_atomic_f32": 6}
+
+
+def msda_test_set_plan_wait_limit(polls: int) -> None:
+    """Test hook: later binned backward plans on this thread give up waiting after `polls`."""
+    load_library().msda_test_set_plan_wait_limit(polls)
+
+
+def msda_microbench_run(kind: str, buf: torch.Tensor, span: int = 0, reps: int = 10,
+                        stream=None) -> tuple[float, float]:
+    """Run one memory-path microbenchmark on device buffer `buf` (overwritten);
+    returns (milliseconds per launch, units per launch)."""
+    _check(buf, "buf")
+    ms, units = ctypes.c_double(), ctypes.c_double()
+    rc = load_library().msda_microbench_run(MICROBENCH[kind], buf.data_ptr(),
+                                            buf.numel() * buf.element_size(), span, reps,
+                                            _stream(stream), ctypes.byref(ms), ctypes.byref(units))
+    if rc != 0:
+        raise RuntimeError(f"msda_microbench_run({kind!r}) returned {rc}")
+    return ms.value, units.value
 
 
 def _dims_of(value: torch.Tensor, spatial_shapes: torch.Tensor,
@@ -229,7 +268,7 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
     if reuse_order and workspace is None:
         raise ValueError("reuse_order needs the workspace of an earlier binned call")
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=value.device)
+        workspace = _scratch(need, value.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = "msda_forward_binned_reuse" if reuse_order else "msda_forward_binned"
     st = getattr(lib, fn)(*args, host.ctypes.data, _ptr(workspace), ws_bytes, _stream(stream))
@@ -254,6 +293,42 @@ def msda_forward_softmax(value, spatial_shapes, level_start_index, sampling_loca
     if st != MSDA_OK:
         raise MsdaError(st, "msda_forward_softmax")
     return out
+
+
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace the library uses only inside one call's enqueued work.
+
+    It is allocated on the caller's current stream; when the kernels run on another
+    stream, record_stream keeps the caching allocator from handing the block out again
+    before that stream's work has finished."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else None
+        cur = torch.cuda.current_stream(device)
+        if s is None:
+            s = torch.cuda.ExternalStream(_stream(stream), device=device)
+        if s.cuda_stream != cur.cuda_stream:
+            ws.record_stream(s)
+    return ws
+
+
+def msda_backward_flags(dims: MsdaDims, dtype: int, accum_dtype: int, scatter: int,
+                        softmax_method: bool, spatial_shapes_host, workspace: torch.Tensor,
+                        stream=None) -> int:
+    """Device-side check flags a binned backward call left in `workspace` (waits for them):
+    0 when its gradients are valid, else MSDA_BWD_* bits (the gradients are then NaN)."""
+    import numpy as np
+
+    host = np.ascontiguousarray(np.asarray(spatial_shapes_host, dtype=np.int64))
+    flags = ctypes.c_uint32()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().msda_backward_flags(ctypes.byref(dims), dtype, accum_dtype, scatter,
+                                            int(bool(softmax_method)), host.ctypes.data,
+                                            workspace.data_ptr(), ws_bytes, _stream(stream),
+                                            ctypes.byref(flags))
+    if st != MSDA_OK:
+        raise MsdaError(st, "msda_backward_flags")
+    return int(flags.value)
 
 
 def _host_shapes(spatial_shapes, spatial_shapes_host):
@@ -320,7 +395,7 @@ def _backward(fn_name, value, spatial_shapes, level_start_index, sampling_locati
     _check(grad_weights, "grad of the weights", dt, weights.shape)
     need = _backward_ws_bytes(fn_name + "_workspace_bytes", dims, _DTYPES[dt], acc, sc, host)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(load_library(), fn_name)(
         _ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),

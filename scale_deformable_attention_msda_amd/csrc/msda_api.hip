@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued; a rejected call
 // leaves the stream untouched and records the reason for msda_last_error().
 #include "msda.h"
+#include "msda_bench.h"
 #include "msda_launch.h"
 
 #include <cstdarg>
@@ -201,6 +202,10 @@ msda_status forward_direct(const void *value, const int64_t *spatial_shapes,
 
 }  // namespace
 
+namespace msda {
+void set_last_error(const char *msg) { snprintf(g_last_error, sizeof(g_last_error), "%s", msg); }
+}  // namespace msda
+
 extern "C" {
 
 msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
@@ -370,6 +375,7 @@ msda_status backward_run(const BackwardSetup &su, msda_dtype accum_dtype, const 
   if (su.binned) {
     msda::BinArgs a{};
     a.value = value;
+    a.shapes = spatial_shapes;
     a.starts = level_start_index;
     a.loc = sampling_locations;
     a.attn = attention_weights;
@@ -541,6 +547,31 @@ msda_status msda_backward_softmax(const void *value, const int64_t *spatial_shap
   }
   return MSDA_OK;
 }
+
+msda_status msda_backward_flags(const msda_dims *dims, msda_dtype dtype, msda_dtype accum_dtype,
+                                msda_scatter scatter, int softmax_method,
+                                const int64_t *spatial_shapes_host, const void *workspace,
+                                size_t workspace_bytes, void *stream, uint32_t *flags) {
+  g_last_error[0] = '\0';
+  if (!flags) return fail(MSDA_ERR_NULL_POINTER, "flags is NULL");
+  *flags = 0;
+  BackwardSetup su;
+  MSDA_TRY(backward_setup(dims, dtype, accum_dtype, scatter, spatial_shapes_host, &su));
+  if (!su.binned || !su.work) return MSDA_OK;  // only the binned scatter checks on the device
+  const size_t head = softmax_method ? softmax_weights_bytes(su) : 0;
+  MSDA_TRY(workspace_check(head + su.ws_need, const_cast<void *>(workspace), workspace_bytes,
+                           "check"));
+  const char *word = static_cast<const char *>(workspace) + head + msda::binned_error_offset(su.plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the error word");
+  *flags = v;
+  return MSDA_OK;
+}
+
+void msda_test_set_plan_wait_limit(uint32_t polls) { msda::set_plan_spin_limit(polls); }
 
 const char *msda_status_string(msda_status status) {
   switch (status) {

@@ -46,11 +46,26 @@
 namespace msda {
 namespace {
 
-constexpr int kTile = 8;               // tile edge in pixels
-constexpr int kEdge = kTile + 1;       // tile plus its one-pixel rim, per side
-constexpr int kCells = kEdge * kEdge;  // bilinear cells whose top-left corner is in [-1, T)
-constexpr int kChunk = 1024;           // samples per tile-kernel block at most
-constexpr int kCountSamples = 4096;    // samples per count / scatter block
+// Tuning constants (the sweep builds variants with -D overrides).
+#ifndef MSDA_BIN_TILE
+#define MSDA_BIN_TILE 8
+#endif
+#ifndef MSDA_BIN_CHUNK
+#define MSDA_BIN_CHUNK 1024
+#endif
+#ifndef MSDA_COUNT_SAMPLES
+#define MSDA_COUNT_SAMPLES 4096
+#endif
+constexpr int kTile = MSDA_BIN_TILE;          // tile edge in pixels
+constexpr int kEdge = kTile + 1;              // tile plus its one-pixel rim, per side
+constexpr int kCells = kEdge * kEdge;         // bilinear cells whose top-left corner is in [-1, T)
+constexpr int kChunk = MSDA_BIN_CHUNK;        // samples per tile-kernel block at most
+constexpr int kCountSamples = MSDA_COUNT_SAMPLES;  // samples per count / scatter block
+// wave 0 of the tile kernel plans with two cells per lane; the item fields hold
+// 10-bit positions; count and scatter threads own whole rounds of 256 samples
+static_assert(kTile >= 2 && kCells <= 128, "tile edge 2..10");
+static_assert(kChunk % 256 == 0 && kChunk <= 1024, "chunk a multiple of 256, at most 1024");
+static_assert(kCountSamples % 256 == 0 && kCountSamples <= 16384, "count block of 256..16384");
 constexpr int kHistLdsBytes = 48 * 1024;
 // Per-bin counters are striped over kStripes addresses (block index modulo
 // kStripes): a coarse-level bin collects counts from ~100 blocks, and integer
@@ -186,6 +201,13 @@ __global__ __launch_bounds__(256) void count_kernel(BinArgs a) {
   const uint32_t per_head = (uint32_t)p.Q * (uint32_t)(p.L * p.K);  // samples of one (batch, head)
   const uint32_t t0 = blockIdx.x * kCountSamples + threadIdx.x;
   for (int e = threadIdx.x; e < p.tiles_bm; e += blockDim.x) hist[e] = 0;
+  // the plan was made from the host's copy of the level shapes: block (0, 0)
+  // compares it with the device's spatial_shapes and level_start_index
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < (unsigned)p.L) {
+    const int l = threadIdx.x;
+    if (a.shapes[2 * l] != p.H[l] || a.shapes[2 * l + 1] != p.W[l] || a.starts[l] != p.start[l])
+      __hip_atomic_fetch_or(a.w.error, kBinErrShapes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   // all kPer loads in flight together (samples past the head's end reload its
   // first one); each sample is binned as soon as its own load has arrived
@@ -319,9 +341,12 @@ __device__ inline void block_scan3(uint32_t (&v)[3], uint32_t (&tot)[3], uint32_
   lds_barrier();  // wsum may be reused right away
 }
 
-// Bound on the polls of one predecessor's published totals.  Predecessors
-// always publish (see above); the bound only guarantees that every wave ends.
+// Default bound on the polls of one predecessor's published totals.
+// Predecessors always publish (see above); the bound only guarantees that
+// every wave ends.  A block that stops waiting raises kBinErrPlanWait, and the
+// later passes then write NaN gradients instead of using overlapping ranges.
 constexpr uint32_t kPlanSpinLimit = 1u << 24;
+thread_local uint32_t g_spin_limit = kPlanSpinLimit;
 
 __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
   __shared__ uint32_t wsum[3 * (kPlanBlock / 64)];
@@ -354,17 +379,21 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // add the totals of all earlier blocks
   uint32_t pre[3] = {0, 0, 0};
+  bool expired = false;
   for (int b = threadIdx.x; b < (int)blockIdx.x; b += kPlanBlock)
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       unsigned long long x = 0;
-      for (uint32_t spin = 0; spin < kPlanSpinLimit; ++spin) {
+      for (uint32_t spin = 0; spin < p.spin_limit; ++spin) {
         x = __hip_atomic_load(&status[3 * b + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (x & 1ull) break;
         __builtin_amdgcn_s_sleep(1);
       }
+      expired |= !(x & 1ull);
       pre[k] += (uint32_t)(x >> 1);
     }
+  if (expired)
+    __hip_atomic_fetch_or(a.w.error, kBinErrPlanWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t pre_tot[3];
   block_scan3(pre, pre_tot, wsum);
   if (live) {
@@ -400,6 +429,7 @@ template <typename T, bool SOFTMAX>
 __global__ __launch_bounds__(256) void scatter_kernel(BinArgs a) {
   extern __shared__ uint32_t hist[];
   const BinPlan &p = a.p;
+  if (*a.w.error) return;  // a failed check: the merge pass writes NaN gradients
   const int bm = blockIdx.y;  // batch * M + head
   const int b = bm / p.M, m = bm - b * p.M;
   const int stripe = (int)((blockIdx.x + blockIdx.y * gridDim.x) % kStripes);
@@ -749,8 +779,9 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   // the chunk count and this block's first chunk entry do not depend on each
   // other: issue the loads together
   const uint32_t nchunks = *a.w.nchunks;
+  const uint32_t failed = *a.w.error;
   uint4 ck = a.w.chunks[blockIdx.x];
-  if (blockIdx.x >= nchunks) return;
+  if (blockIdx.x >= nchunks || failed) return;
 
   // The block is persistent: after its first chunk (= blockIdx.x) it claims
   // chunks gridDim.x, gridDim.x + 1, ... from a counter, one at a time, until
@@ -1118,12 +1149,29 @@ __device__ inline void add_part(const BinArgs &a, int nb, int iy, int ix, int la
   }
 }
 
+// After a failed check (BinScratch::error) every gradient of the call is NaN.
+template <typename T>
+__device__ void poison_gradients(const BinArgs &a) {
+  const BinPlan &p = a.p;
+  const float nan = __int_as_float(0x7fc00000);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nv = p.B * p.S * p.M * p.D, ns = (int64_t)p.total;
+  for (int64_t i = t0; i < nv; i += stride) store_scalar<T>(reinterpret_cast<T *>(a.grad_value) + i, nan);
+  for (int64_t i = t0; i < 2 * ns; i += stride) store_scalar<T>(reinterpret_cast<T *>(a.grad_loc) + i, nan);
+  for (int64_t i = t0; i < ns; i += stride) store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + i, nan);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(BinArgs a) {
   using TL = TileLayout<D>;
   constexpr int VEC = TL::VEC, G = TL::G;
   constexpr int NG = 256 / G;
   const BinPlan &p = a.p;
+  if (*a.w.error) {
+    poison_gradients<T>(a);
+    return;
+  }
   const int bin = blockIdx.x;
   const BinPos bp = decode_bin(p, bin);
   const int l = bp.l, b = bp.b, m = bp.m, ty = bp.ty, tx = bp.tx, H = bp.H, W = bp.W;
@@ -1215,9 +1263,12 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t status_offset(const BinPlan &p) {
   return align256(counter_index(p.nbins, 0) * sizeof(uint32_t));
 }
-size_t counts_and_status_bytes(const BinPlan &p) {
+size_t error_offset_in_counts(const BinPlan &p) {
   const size_t blocks = ((size_t)p.nbins + kPlanBlock - 1) / kPlanBlock;
-  return align256(status_offset(p) + blocks * 3 * sizeof(unsigned long long));
+  return status_offset(p) + blocks * 3 * sizeof(unsigned long long);
+}
+size_t counts_and_status_bytes(const BinPlan &p) {
+  return align256(error_offset_in_counts(p) + 16);
 }
 
 template <typename T>
@@ -1292,9 +1343,11 @@ bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, in
     p.W[l] = (int)w;
     p.ntx[l] = (int)((w + kTile - 1) / kTile);
     p.ntiles[l] = (int)(((h + kTile - 1) / kTile) * p.ntx[l]);
+    p.start[l] = rows;
     rows += h * w;
     tiles += p.ntiles[l];
   }
+  p.spin_limit = g_spin_limit;
   if (rows > S) {
     *why = "the levels hold more pixels than num_keys";
     return false;
@@ -1359,6 +1412,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
   if (w) {
     w->counts = reinterpret_cast<uint32_t *>(cc);
     w->plan_status = reinterpret_cast<unsigned long long *>(cc + status_offset(p));
+    w->error = reinterpret_cast<uint32_t *>(cc + error_offset_in_counts(p));
     w->cursor = reinterpret_cast<uint32_t *>(cu);
     w->bin_start = reinterpret_cast<uint32_t *>(bs);
     w->bin_nch = reinterpret_cast<uint32_t *>(bn);
@@ -1373,6 +1427,12 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
 }
 
 size_t binned_workspace_bytes(const BinPlan &p) { return layout(p, nullptr, nullptr); }
+
+// the counts region is the first one the layout carves
+size_t binned_error_offset(const BinPlan &p) { return error_offset_in_counts(p); }
+
+void set_plan_spin_limit(uint32_t polls) { g_spin_limit = polls; }
+uint32_t plan_spin_limit() { return g_spin_limit; }
 
 BinScratch carve_bin_scratch(const BinPlan &p, void *workspace) {
   BinScratch w{};

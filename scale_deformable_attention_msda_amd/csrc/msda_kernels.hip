@@ -40,7 +40,13 @@
 namespace msda {
 namespace {
 
-constexpr int kMaxBlock = 256;
+// lanes per forward / atomic-backward block at most (the sweep builds variants)
+#ifndef MSDA_FWD_BLOCK
+#define MSDA_FWD_BLOCK 256
+#endif
+constexpr int kMaxBlock = MSDA_FWD_BLOCK;
+static_assert(kMaxBlock == 128 || kMaxBlock == 256 || kMaxBlock == 512 || kMaxBlock == 1024,
+              "block of 128..1024 lanes");
 constexpr int kGeoLdsBudget = 64 * 1024;
 
 // Per-sample data the backward needs beyond the corners.
@@ -64,12 +70,8 @@ __device__ inline float ld(const void *base, int64_t i) {
 constexpr int kXcds = 8;
 
 __device__ inline int64_t logical_block() {
-#ifdef MSDA_NO_XCD_REMAP
-  return blockIdx.x;
-#else
   const uint32_t per = gridDim.x / kXcds;
   return (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-#endif
 }
 
 inline int64_t padded_grid(int64_t blocks) { return (blocks + kXcds - 1) / kXcds * kXcds; }
@@ -91,7 +93,10 @@ __device__ inline void stage_levels(Level *lv, const LaunchArgs &a) {
 // of the block size), so for L*K a power of two (at most 64) a head-query's
 // logits sit in an aligned lane group and each lane forms its weight there;
 // otherwise phase 0 stages the logits in LDS first.
-template <typename T, int D, bool SOFTMAX>
+// PIPE: samples whose corner loads a lane keeps in flight (4 * PIPE buffer
+// loads); the loop runs over L*K rounded up to a multiple of PIPE, the padding
+// samples reading nothing (offset past the buffer end, weight 0).
+template <typename T, int D, bool SOFTMAX, int PIPE>
 __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   using RL = RowLayout<T, D>;
   constexpr int G = RL::G;
@@ -169,20 +174,47 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   float acc[RL::VEC];
 #pragma unroll
   for (int i = 0; i < RL::VEC; ++i) acc[i] = 0.0f;
-#pragma unroll 2
-  for (int j = 0; j < LK; ++j) {
-    const Corners cs = geo[j * gs_stride + grp];
-    uint32_t raw[4][RL::WORDS];
+  // software pipeline: buffer u holds the four corner rows of one sample; it
+  // is consumed, then refilled with the sample PIPE further on, so a lane
+  // always has 4 * (PIPE - 1) to 4 * PIPE loads outstanding
+  const int lk_pad = (LK + PIPE - 1) / PIPE * PIPE;
+  uint32_t raw[PIPE][4][RL::WORDS];
+  float wt[PIPE][4];
+  auto issue = [&](int u, int j) {
+    Corners cs = geo[min(j, LK - 1) * gs_stride + grp];
+    if (j >= LK) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[c]);
+      for (int c = 0; c < 4; ++c) {
+        cs.off[c] = kOutside;
+        cs.w[c] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[u][c]);
+      wt[u][c] = cs.w[c];
+    }
+  };
+  auto consume = [&](int u) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float x[RL::VEC];
-      unpack<T, RL::WORDS>(raw[c], x);
+      unpack<T, RL::WORDS>(raw[u][c], x);
 #pragma unroll
-      for (int i = 0; i < RL::VEC; ++i) acc[i] = fmaf(cs.w[c], x[i], acc[i]);
+      for (int i = 0; i < RL::VEC; ++i) acc[i] = fmaf(wt[u][c], x[i], acc[i]);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < PIPE; ++u) issue(u, u);
+  for (int j0 = 0; j0 + PIPE < lk_pad; j0 += PIPE) {
+#pragma unroll
+    for (int u = 0; u < PIPE; ++u) {
+      consume(u);
+      issue(u, j0 + PIPE + u);
     }
   }
+#pragma unroll
+  for (int u = 0; u < PIPE; ++u) consume(u);
   uint32_t ow[RL::WORDS];
   pack<T, RL::WORDS>(acc, ow);
   char *out = reinterpret_cast<char *>(a.out) + (hq0 + grp) * (int64_t)RL::kRowBytes + lane_off;
@@ -555,6 +587,34 @@ int pick_hqb(int G, int LK, int bytes_per_sample) {
   return hqb;
 }
 
+// Samples in flight per lane in the forward gather: the deepest compiled depth
+// (at most MSDA_FWD_PIPE) whose padding adds at most a quarter to the L*K
+// rounds, else 2 (L*K = 16 takes MSDA_FWD_PIPE, 12 takes 4, 9 takes 2).
+#ifndef MSDA_FWD_PIPE
+#define MSDA_FWD_PIPE 2
+#endif
+constexpr int kFwdPipe = MSDA_FWD_PIPE;
+static_assert(kFwdPipe == 2 || kFwdPipe == 4 || kFwdPipe == 8, "forward pipeline depth 2, 4 or 8");
+
+int fwd_pipe_depth(int lk) {
+  for (int p = kFwdPipe; p > 2; p /= 2)
+    if ((lk + p - 1) / p * p * 4 <= lk * 5) return p;
+  return 2;
+}
+
+template <typename T, int D, bool SOFTMAX>
+void launch_fwd_pipe(int pipe, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                     const LaunchArgs &a, int hqb) {
+  if (kFwdPipe >= 8 && pipe == 8)
+    hipLaunchKernelGGL((fwd_kernel<T, D, SOFTMAX, (kFwdPipe >= 8 ? 8 : 2)>), grid, block, lds,
+                       stream, a, hqb);
+  else if (kFwdPipe >= 4 && pipe == 4)
+    hipLaunchKernelGGL((fwd_kernel<T, D, SOFTMAX, (kFwdPipe >= 4 ? 4 : 2)>), grid, block, lds,
+                       stream, a, hqb);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, SOFTMAX, 2>), grid, block, lds, stream, a, hqb);
+}
+
 template <typename T, int D>
 hipError_t fwd_launch(const LaunchArgs &a, bool softmax, hipStream_t stream) {
   using RL = RowLayout<T, D>;
@@ -569,12 +629,11 @@ hipError_t fwd_launch(const LaunchArgs &a, bool softmax, hipStream_t stream) {
   size_t lds = (size_t)LK * (hqb + 1) * sizeof(Corners);
   if (staged) lds += ((size_t)hqb * (LK + 1) + hqb) * sizeof(float);
   prof_begin(stream, softmax ? "fwd_softmax" : "fwd");
+  const int pipe = fwd_pipe_depth(LK);
   if (softmax)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
-                       stream, a, hqb);
+    launch_fwd_pipe<T, D, true>(pipe, dim3((unsigned)blocks), dim3(hqb * RL::G), lds, stream, a, hqb);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3((unsigned)blocks), dim3(hqb * RL::G), lds,
-                       stream, a, hqb);
+    launch_fwd_pipe<T, D, false>(pipe, dim3((unsigned)blocks), dim3(hqb * RL::G), lds, stream, a, hqb);
   prof_end(stream, softmax ? "fwd_softmax" : "fwd");
   return hipGetLastError();
 }

@@ -54,6 +54,8 @@ struct BinPlan {
   int max_slots;               // 2 * ceil(total / chunk)
   int64_t pyramid_rows;        // sum_l H_l * W_l
   uint32_t total;              // B*Q*M*L*K samples
+  int64_t start[kMaxLevels];   // first pyramid row of level l (prefix sum of H*W)
+  uint32_t spin_limit;         // polls of one predecessor's totals before the plan gives up
   FastDiv div_lk, div_k;       // by L*K and K
   // a stride of 256 samples of one (batch, head), t = q (L K) + j: the points
   // it advances (256 % (L K)), the sample ids it advances without and the
@@ -67,6 +69,7 @@ struct BinPlan {
 struct BinScratch {
   uint32_t *counts;     // [nbins][stripes] samples per bin, per block stripe, one 64-byte line each
   unsigned long long *plan_status;  // [plan blocks][3] published totals (value << 1 | 1)
+  uint32_t *error;      // [1] kBinErr* flags of this call (cleared with the counts)
   uint32_t *cursor;     // [nbins][stripes] fill cursor of the record scatter, one 64-byte line each
   uint32_t *bin_start;  // [nbins] first sorted position of a bin
   uint32_t *bin_nch;    // [nbins] chunks of a bin
@@ -78,8 +81,15 @@ struct BinScratch {
   float *slots;         // [max_slots][(tile+1)^2][D] whole partial tiles of split bins
 };
 
+// Error flags the binned backward leaves in its workspace (BinScratch::error).
+// A call that sets one writes NaN into all three gradients.
+constexpr uint32_t kBinErrShapes = 1u;    // device spatial_shapes / level_start_index differ
+                                          // from the host plan
+constexpr uint32_t kBinErrPlanWait = 2u;  // a plan block stopped waiting for a predecessor
+
 struct BinArgs {
   const void *value;
+  const int64_t *shapes;  // device spatial_shapes
   const int64_t *starts;  // device level_start_index
   const void *loc;
   const void *attn;
@@ -151,6 +161,9 @@ struct FwdArgs {
 void prof_begin(hipStream_t stream, const char *name);
 void prof_end(hipStream_t stream, const char *name);
 
+// Set the thread's msda_last_error() text (entry points outside msda_api.hip).
+void set_last_error(const char *msg);
+
 enum class Dtype { F32, BF16, F16 };
 // grad_value accumulator of the atomic scatter: fp32, or packed 16-bit atomics
 // in the data type (BF16 or F16 data only)
@@ -174,6 +187,12 @@ bool make_bin_plan(BinPlan &p, int64_t B, int64_t Q, int64_t S, int M, int D, in
                    const int64_t *shapes_host, const char **why);
 size_t binned_workspace_bytes(const BinPlan &p);
 BinScratch carve_bin_scratch(const BinPlan &p, void *workspace);
+// Byte offset of the error word inside the workspace.
+size_t binned_error_offset(const BinPlan &p);
+// Polls of one predecessor before a plan block gives up (this thread's later
+// plans; a test hook, the default never expires on a working device).
+void set_plan_spin_limit(uint32_t polls);
+uint32_t plan_spin_limit();
 hipError_t launch_backward_binned(const BinArgs &a, Dtype dt, hipStream_t stream);
 // Query-binned forward: plan from host-side level shapes for a launch of
 // `nb` batches (false when the sizes do not suit it: the caller then runs

@@ -1,5 +1,5 @@
 // Optional per-kernel timing with HIP events (see msda_profile_start in msda.h).
-#include "msda.h"
+#include "msda_bench.h"
 #include "msda_launch.h"
 
 #include <cstring>

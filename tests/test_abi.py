@@ -1,4 +1,4 @@
-"""The C-ABI library on the host: it loads, exports every symbol include/msda.h
+"""The C-ABI library on the host: it loads, exports every symbol include/*.h
 declares, and rejects bad arguments with a status code before any launch.
 No call here reaches a kernel, so these run without a GPU."""
 import ctypes
@@ -11,6 +11,8 @@ import scale_deformable_attention_msda_amd as msda
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msda.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,10 +23,12 @@ def lib():
     return msda.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msda_[a-z0-9_]+)\s*\(", text)))
+def declared_functions(headers=HEADERS):
+    names = set()
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(msda_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -32,8 +36,11 @@ def test_header_declares_the_entry_points():
     for n in ("msda_forward", "msda_forward_binned", "msda_forward_binned_workspace_bytes",
               "msda_forward_softmax", "msda_backward", "msda_backward_workspace_bytes",
               "msda_backward_softmax", "msda_backward_softmax_workspace_bytes",
-              "msda_status_string", "msda_last_error"):
-        assert n in names
+              "msda_status_string", "msda_last_error", "msda_backward_flags"):
+        assert n in declared_functions([HEADER])
+    for n in ("msda_profile_start", "msda_profile_stop", "msda_profile_select",
+              "msda_microbench_run", "msda_test_set_plan_wait_limit"):
+        assert n in names and n not in declared_functions([HEADER])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -272,3 +279,40 @@ def test_binned_forward_reuse_rejections(lib):
     assert big_need != SIZE_MAX, msda.msda_last_error()
     assert fwd_reuse(lib, big, shapes_host=PYRAMID, ws=FAKE, ws_bytes=big_need) == 3
     assert "one launch" in msda.msda_last_error()
+
+
+def test_backward_flags_host_side(lib):
+    """msda_backward_flags: argument checks, and no device access for calls without
+    device checks (atomic scatter, no samples)."""
+    flags = ctypes.c_uint32(7)
+    shapes = (ctypes.c_int64 * 4)(8, 8, 4, 4)
+    dims = msda.MsdaDims(1, 80, 2, 8, 2, 16, 2)
+    st = lib.msda_backward_flags(ctypes.byref(dims), msda.MSDA_FP32, msda.MSDA_FP32,
+                                 msda.MSDA_SCATTER_ATOMIC, 0, shapes, None, 0, None,
+                                 ctypes.byref(flags))
+    assert st == msda.MSDA_OK and flags.value == 0
+    empty = msda.MsdaDims(1, 80, 2, 8, 2, 0, 2)
+    flags.value = 7
+    st = lib.msda_backward_flags(ctypes.byref(empty), msda.MSDA_FP32, msda.MSDA_FP32,
+                                 msda.MSDA_SCATTER_BINNED, 0, shapes, None, 0, None,
+                                 ctypes.byref(flags))
+    assert st == msda.MSDA_OK and flags.value == 0
+    # a binned call with samples needs its workspace
+    st = lib.msda_backward_flags(ctypes.byref(dims), msda.MSDA_FP32, msda.MSDA_FP32,
+                                 msda.MSDA_SCATTER_BINNED, 0, shapes, None, 0, None,
+                                 ctypes.byref(flags))
+    assert st == 5  # MSDA_ERR_WORKSPACE
+    st = lib.msda_backward_flags(ctypes.byref(dims), msda.MSDA_FP32, msda.MSDA_FP32,
+                                 msda.MSDA_SCATTER_BINNED, 0, shapes, None, 0, None, None)
+    assert st == 1  # MSDA_ERR_NULL_POINTER
+
+
+def test_microbench_rejects_bad_arguments(lib):
+    ms, units = ctypes.c_double(), ctypes.c_double()
+    # NULL buffer, too small, bad kind: rejected before any launch
+    assert lib.msda_microbench_run(0, None, 1 << 21, 0, 1, None, ctypes.byref(ms),
+                                   ctypes.byref(units)) == 1
+    assert lib.msda_microbench_run(0, 256, 1024, 0, 1, None, ctypes.byref(ms),
+                                   ctypes.byref(units)) == 1
+    assert lib.msda_microbench_run(0, 256, 1 << 21, 0, 0, None, ctypes.byref(ms),
+                                   ctypes.byref(units)) == 1
