@@ -267,6 +267,31 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * msda_backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and arguments without the workspace, which comes from a
+ * static device array of the library instead.  That array holds
+ * msda_noalloc_scratch_bytes() bytes (256 MiB) on every GPU the entry point
+ * has run on, from its first call there until the process ends; calls whose
+ * workspace would need more return MSDA_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on a GPU uses that GPU's one array, so calls whose work
+ * may overlap on one GPU (other streams, other threads) race and give wrong
+ * gradients: serialise them.  Each call clears what it needs cleared itself.
+ * No hipMalloc / hipFree.  Errors as for msda_backward, plus MSDA_ERR_HIP when
+ * the array's address cannot be looked up.
+ */
+msda_status msda_backward_noalloc(const void *value, const int64_t *spatial_shapes,
+                                  const int64_t *level_start_index,
+                                  const void *sampling_locations, const void *attention_weights,
+                                  const void *grad_out, void *grad_value, void *grad_loc,
+                                  void *grad_attn, const msda_dims *dims, msda_dtype dtype,
+                                  msda_dtype accum_dtype, msda_scatter scatter,
+                                  const int64_t *spatial_shapes_host, void *stream);
+
+/* Bytes of the static array msda_backward_noalloc takes its workspace from. */
+size_t msda_noalloc_scratch_bytes(void);
+
+/*
  * Bytes of device workspace msda_backward_softmax needs: what
  * msda_backward_workspace_bytes() reports for the same arguments, preceded by
  * a weights image (B*Q*M*L*K elements of `dtype`, rounded up to 256 bytes)

@@ -114,6 +114,10 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.c_int, vp, vp, ctypes.c_size_t, vp,
                                         ctypes.POINTER(ctypes.c_uint32)]
     lib.msda_backward_flags.restype = ctypes.c_int
+    lib.msda_backward_noalloc.argtypes = lib.msda_backward.argtypes[:14] + [vp]
+    lib.msda_backward_noalloc.restype = ctypes.c_int
+    lib.msda_noalloc_scratch_bytes.argtypes = []
+    lib.msda_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.msda_test_set_plan_wait_limit.argtypes = [ctypes.c_uint32]
     lib.msda_test_set_plan_wait_limit.restype = None
     lib.msda_microbench_run.argtypes = [ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_size_t,
@@ -421,6 +425,37 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
     return _backward("msda_backward", value, spatial_shapes, level_start_index,
                      sampling_locations, attention_weights, grad_out, grad_value, grad_loc,
                      grad_attn, accum_dtype, scatter, spatial_shapes_host, workspace, stream)
+
+
+def msda_noalloc_scratch_bytes() -> int:
+    return int(load_library().msda_noalloc_scratch_bytes())
+
+
+def msda_backward_noalloc(value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, grad_out, grad_value, grad_loc, grad_attn,
+                          accum_dtype=None, scatter="binned", spatial_shapes_host=None,
+                          stream=None):
+    """msda_backward without a workspace argument: the library takes it from its static
+    per-GPU scratch array (msda_noalloc_scratch_bytes()).  The outputs must be given; no
+    device memory is allocated here or in the library.  Calls overlapping on one GPU race."""
+    dims, dt = _common(value, spatial_shapes, level_start_index, sampling_locations,
+                       attention_weights)
+    B, Q, M, D = dims.batch, dims.num_queries, dims.num_heads, dims.head_dim
+    _check(grad_out, "grad_out", dt, (B, Q, M * D))
+    _check(grad_value, "grad_value", dt, value.shape)
+    _check(grad_loc, "grad_loc", dt, sampling_locations.shape)
+    _check(grad_attn, "grad_attn", dt, attention_weights.shape)
+    acc = _DTYPES[accum_dtype if accum_dtype is not None else torch.float32]
+    sc = _SCATTER[scatter]
+    host = _host_shapes(spatial_shapes, spatial_shapes_host) if sc == MSDA_SCATTER_BINNED else None
+    st = load_library().msda_backward_noalloc(
+        _ptr(value), _ptr(spatial_shapes), _ptr(level_start_index), _ptr(sampling_locations),
+        _ptr(attention_weights), _ptr(grad_out), _ptr(grad_value), _ptr(grad_loc),
+        _ptr(grad_attn), ctypes.byref(dims), _DTYPES[dt], acc, sc,
+        None if host is None else host.ctypes.data, _stream(stream))
+    if st != MSDA_OK:
+        raise MsdaError(st, "msda_backward_noalloc")
+    return grad_value, grad_loc, grad_attn
 
 
 def msda_backward_softmax(value, spatial_shapes, level_start_index, sampling_locations,

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libmsda.so")
 SOURCES = ["msda_api.hip", "msda_kernels.hip", "msda_binned.hip", "msda_fwd_binned.hip",
-           "msda_profile.hip", "msda_microbench.hip"]
+           "msda_profile.hip", "msda_microbench.hip", "msda_noalloc.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.
