@@ -57,6 +57,16 @@ void msda_profile_select(const char *name);
  */
 void msda_test_set_plan_wait_limit(uint32_t polls);
 
+/*
+ * Test hook: the schedule of later forward launches (msda_forward,
+ * msda_forward_softmax) on this thread.  0 (default): the LDS-window gather
+ * when the launch has enough queries per (batch, head) for its staging to pay
+ * off, else the direct gather; 1: always the direct gather; 2: the LDS-window
+ * gather whenever the device's LDS holds its tables.  Both compute the same
+ * sums; only the order of the fp32 additions may differ.
+ */
+void msda_test_set_forward_schedule(int schedule);
+
 /* Memory-path microbenchmarks (msda_microbench_run). */
 typedef enum {
     /* streaming read of the buffer (16-byte loads); units = bytes read */

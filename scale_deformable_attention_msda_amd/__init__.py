@@ -118,6 +118,8 @@ def load_library(path: str = LIB_PATH):
     lib.msda_backward_noalloc.restype = ctypes.c_int
     lib.msda_noalloc_scratch_bytes.argtypes = []
     lib.msda_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.msda_test_set_forward_schedule.argtypes = [ctypes.c_int]
+    lib.msda_test_set_forward_schedule.restype = None
     lib.msda_test_set_plan_wait_limit.argtypes = [ctypes.c_uint32]
     lib.msda_test_set_plan_wait_limit.restype = None
     lib.msda_microbench_run.argtypes = [ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_size_t,
@@ -161,6 +163,15 @@ MSDA_BWD_SHAPES_MISMATCH = 1
 MSDA_BWD_PLAN_EXPIRED = 2
 MICROBENCH = {"read": 0, "copy": 1, "atomic_f32": 2, "atomic_pk_bf16": 3, "gather_global": 4,
               "gather_lds": 5, "lds_atomic_f32": 6}
+
+
+FORWARD_SCHEDULE = {"auto": 0, "direct": 1, "window": 2}
+
+
+def msda_test_set_forward_schedule(schedule: str) -> None:
+    """Test hook: forward schedule of later calls on this thread ("auto", "direct" or
+    "window")."""
+    load_library().msda_test_set_forward_schedule(FORWARD_SCHEDULE[schedule])
 
 
 def msda_test_set_plan_wait_limit(polls: int) -> None:

@@ -573,6 +573,8 @@ msda_status msda_backward_flags(const msda_dims *dims, msda_dtype dtype, msda_dt
 
 void msda_test_set_plan_wait_limit(uint32_t polls) { msda::set_plan_spin_limit(polls); }
 
+void msda_test_set_forward_schedule(int schedule) { msda::set_forward_schedule(schedule); }
+
 const char *msda_status_string(msda_status status) {
   switch (status) {
     case MSDA_OK: return "MSDA_OK";

@@ -221,6 +221,485 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
   global_store<RL::WORDS>(out, ow);
 }
 
+// ---------------------------------------------- forward, LDS-resident levels
+//
+// The corner rows of the coarse levels are read over and over: every query
+// samples every level, and the coarsest levels hold few pixels, so on the
+// encoder workloads half the samples fall on levels 2 and 3 (1.3 K of the
+// pyramid's 22 K pixels).  Every row the direct gather reads passes the
+// vector L1 / texture path, which returns at most ~60 B per clock per CU on
+// this GPU, while LDS returns ~110 B per clock per CU: both paths work at once
+// when the coarse levels are read from LDS and the fine ones from the L1.
+//
+// A block owns one (batch b, head m) and a run of queries [q0, q0 + nq).  It
+// keeps in LDS, for head m of image b:
+//   - every level whose rows fit whole (smallest levels first), and
+//   - for the first level that does not fit, a window of the rows left room
+//     for: the consecutive rows that hold the most of the block's samples on
+//     that level (a histogram of their cell rows, taken before staging);
+// all other levels, and samples whose cell leaves the window, are gathered
+// from global memory as in fwd_kernel.  The choice only decides where a row
+// is read from, never the result: each corner still gets its value and weight.
+// After staging, every wavefront walks its own chunks of 64 / G head-queries
+// with fwd_kernel's two phases (geometry one lane per sample into the wave's
+// LDS table; gather one lane group per head-query), with no block barrier, so
+// the geometry of one wave overlaps the gathers of the others.  LDS-mode corners carry kLdsFlag in their offset; an invalid
+// corner of an LDS-mode sample reads the zero row at the window area's head.
+constexpr uint32_t kLdsFlag = 0x40000000u;   // bit 30 set, bit 31 clear: an LDS offset
+constexpr int kWinThreads = 1024;
+constexpr int kWinMinRows = 4;               // a window level holds at least this many rows
+constexpr int kWinHistMax = 4096;            // rows a window level may have
+
+struct WinLevel {
+  int mode;  // 0 global, 1 whole level in LDS, 2 window of rows
+  int rows;  // rows held
+  int y0;    // first row held
+  int lds;   // byte offset of the level's first held row in the window area
+};
+
+// Window-area placement of the levels for this launch's shapes (one thread):
+// whole levels smallest first while they fit, then one window level.
+template <int RB>
+__device__ inline void plan_windows(const Level *lv, int L, uint32_t budget, WinLevel *wl) {
+  uint32_t used = RB;  // the zero row
+  bool done = false;
+  uint32_t taken = 0;  // bit l: level l placed
+  for (int n = 0; n < L; ++n) {
+    int best = -1;
+    for (int l = 0; l < L; ++l)
+      if (!(taken >> l & 1u) &&
+          (best < 0 || (int64_t)lv[l].H * lv[l].W < (int64_t)lv[best].H * lv[best].W))
+        best = l;
+    taken |= 1u << best;
+    const int H = lv[best].H, W = lv[best].W;
+    const uint64_t row = (uint64_t)W * RB;
+    WinLevel w{0, 0, 0, 0};
+    if (!done && H >= 1 && W >= 1) {
+      if ((uint64_t)H * row <= budget - used) {
+        w = WinLevel{1, H, 0, (int)used};
+        used += (uint32_t)(H * row);
+      } else {
+        // the window level's area first holds the histogram of its H + 1 cell rows
+        const uint64_t fit = (budget - used) / row;
+        if (fit >= (uint64_t)kWinMinRows && H <= kWinHistMax &&
+            (uint64_t)(H + 1) * 4u <= budget - used)
+          w = WinLevel{2, (int)fit, 0, (int)used};
+        done = true;  // larger levels get nothing
+      }
+    }
+    wl[best] = w;
+  }
+}
+
+// 32-bit LDS addresses: the byte offset of a __shared__ location in the
+// workgroup's LDS, and a load of WORDS dwords from such an offset.
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ inline uint32_t lds_offset_of(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_char_t *)p;
+}
+template <int WORDS>
+__device__ inline void lds_load_at(uint32_t addr, uint32_t (&w)[WORDS]) {
+  typedef uint32_t vec_t __attribute__((ext_vector_type(WORDS)));
+  const vec_t x = *(const __attribute__((address_space(3))) vec_t *)(uintptr_t)addr;
+#pragma unroll
+  for (int i = 0; i < WORDS; ++i) w[i] = x[i];
+}
+
+template <int WORDS>
+__device__ inline void lds_load(const char *base, uint32_t off, uint32_t (&w)[WORDS]) {
+  if constexpr (WORDS == 4) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(base + off);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else if constexpr (WORDS == 2) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(base + off);
+    w[0] = x.x; w[1] = x.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t *>(base + off);
+  }
+}
+
+// Geometry of one sample for the window schedule, one path for every level
+// (the lanes of a wave hold samples of several levels): LDS offsets with
+// kLdsFlag when the level is held and both of the cell's rows inside the
+// level are among the held rows (an invalid corner reads the zero row), else
+// the global offsets of sample_corners.  The coordinate and its floor are
+// taken in fp64, exactly as sample_corners does.
+__device__ inline void sample_corners_any(float u, float v, const Level &lv, const WinLevel &wl,
+                                          uint32_t RB, uint32_t row_base, uint32_t row_stride,
+                                          uint32_t head_off, Corners &cs) {
+  const double x = (double)u * (double)lv.W - 0.5;
+  const double y = (double)v * (double)lv.H - 0.5;
+  const double xf = floor(x), yf = floor(y);
+  const bool any = xf >= -1.0 && xf < (double)lv.W && yf >= -1.0 && yf < (double)lv.H;
+  const int x0 = any ? (int)xf : 0, y0 = any ? (int)yf : 0;
+  const float fx = any ? (float)(x - xf) : 0.0f, fy = any ? (float)(y - yf) : 0.0f;
+  const bool xin0 = any && x0 >= 0, xin1 = any && x0 + 1 < lv.W;
+  const bool yin0 = any && y0 >= 0, yin1 = any && y0 + 1 < lv.H;
+  const bool held0 = !yin0 || (y0 >= wl.y0 && y0 < wl.y0 + wl.rows);
+  const bool held1 = !yin1 || (y0 + 1 >= wl.y0 && y0 + 1 < wl.y0 + wl.rows);
+  const bool lds = wl.mode != 0 && held0 && held1;
+  // corner 00 and the steps to corners 01 and 10, in LDS or global bytes
+  const uint32_t b00 = lds ? (uint32_t)wl.lds + (uint32_t)((y0 - wl.y0) * lv.W + x0) * RB
+                           : (row_base + (uint32_t)lv.start + (uint32_t)(y0 * lv.W + x0)) *
+                                 row_stride + head_off;
+  const uint32_t sx = lds ? RB : row_stride;
+  const uint32_t sy = (uint32_t)lv.W * sx;
+  const uint32_t flag = lds ? kLdsFlag : 0u;
+  const uint32_t none = lds ? kLdsFlag : kOutside;  // the zero row, or past the buffer end
+  cs.off[0] = (xin0 && yin0) ? (b00 | flag) : none;
+  cs.off[1] = (xin1 && yin0) ? ((b00 + sx) | flag) : none;
+  cs.off[2] = (xin0 && yin1) ? ((b00 + sy) | flag) : none;
+  cs.off[3] = (xin1 && yin1) ? ((b00 + sy + sx) | flag) : none;
+  cs.w[0] = (xin0 && yin0) ? (1.0f - fx) * (1.0f - fy) : 0.0f;
+  cs.w[1] = (xin1 && yin0) ? fx * (1.0f - fy) : 0.0f;
+  cs.w[2] = (xin0 && yin1) ? (1.0f - fx) * fy : 0.0f;
+  cs.w[3] = (xin1 && yin1) ? fx * fy : 0.0f;
+}
+
+struct WinArgs {
+  int nwaves;         // waves per block; each walks its own chunks of 64 / G head-queries
+  int qb;             // queries per block
+  int nsplit;         // blocks per (batch, head)
+  uint32_t geo_bytes; // LDS bytes before the window area (the waves' geometry tables)
+  uint32_t win_bytes; // LDS bytes of the window area
+  FastDiv div_lk, div_k;  // by L*K and by K
+};
+
+// Ordering of LDS traffic between the lanes of one wavefront: LDS operations
+// of a wave complete in order, so a compiler barrier is all that is needed.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bytes of one wave's LDS tables: geometry [L*K][64/G + 1] and, for the softmax
+// method with L*K not a power of two, the chunk's logits and 1 / sum.
+__host__ __device__ inline uint32_t win_wave_bytes(int lk, int g, bool staged) {
+  const int hpw = 64 / g;
+  uint32_t b = (uint32_t)lk * (hpw + 1) * (uint32_t)sizeof(Corners);
+  if (staged) b += (uint32_t)(hpw * (lk + 1) + hpw) * 4u;
+  return (b + 15u) / 16u * 16u;
+}
+
+template <typename T, int D, bool SOFTMAX, int PIPE>
+__global__ __launch_bounds__(kWinThreads) void fwd_win_kernel(LaunchArgs a, WinArgs wa) {
+  using RL = RowLayout<T, D>;
+  constexpr int G = RL::G;
+  constexpr int RB = RL::kRowBytes;
+  constexpr int HPW = 64 / G;  // head-queries per wave chunk
+  __shared__ Level lv[kMaxLevels];
+  __shared__ WinLevel wl[kMaxLevels];
+  __shared__ uint8_t jlist[2][64];       // sample indices j on global / LDS-held levels
+  __shared__ int jcount[2];
+  __shared__ int best_shared;
+  extern __shared__ __align__(16) char smem[];
+  char *win = smem + wa.geo_bytes;
+
+  const int K = (int)a.K, LK = (int)(a.L * a.K), M = (int)a.M, L = (int)a.L;
+  const int64_t lb = logical_block();
+  if (lb >= a.nb * a.M * wa.nsplit) return;
+  const int bm = (int)(lb / wa.nsplit), split = (int)(lb - (int64_t)bm * wa.nsplit);
+  const int b = bm / M, m = bm - b * M;
+  const int64_t q0 = (int64_t)split * wa.qb;
+  if (q0 >= a.Q) return;
+  const int nq = (int)min((int64_t)wa.qb, a.Q - q0);
+  stage_levels(lv, a);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    plan_windows<RB>(lv, L, wa.win_bytes, wl);
+    int n[2] = {0, 0};
+    for (int j = 0; j < LK; ++j) {
+      const int c = wl[j / K].mode != 0 ? 1 : 0;
+      jlist[c][n[c]++] = (uint8_t)j;
+    }
+    jcount[0] = n[0];
+    jcount[1] = n[1];
+  }
+  __syncthreads();
+
+  const uint32_t row_stride = (uint32_t)(M * RB);
+  const uint32_t head_off = (uint32_t)(m * RB);
+  const uint32_t row_base = (uint32_t)(b * a.S);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.value, a.value_bytes);
+  constexpr int P = RB / 16;  // 16-byte pieces per head row (RB >= 16)
+
+  // Stage the held rows of the levels in mode `only`, eight 16-byte loads in
+  // flight per thread (the level loop is uniform, so nothing waits per load).
+  auto stage = [&](int only) {
+    constexpr int kBatch = 8;
+    for (int l = 0; l < L; ++l) {
+      if (wl[l].mode != only) continue;
+      const int W = lv[l].W, n = wl[l].rows * W * P;
+      const uint32_t first = row_base + (uint32_t)lv[l].start + (uint32_t)(wl[l].y0 * W);
+      for (int c0 = 0; c0 < n; c0 += kBatch * (int)blockDim.x) {
+        uint32_t w[kBatch][4];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int c = min(c0 + k * (int)blockDim.x + (int)threadIdx.x, n - 1);
+          const int p = c / P, piece = c - p * P;
+          buffer_load<4>(rsrc, (first + (uint32_t)p) * row_stride + head_off + (uint32_t)(piece * 16),
+                         w[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int c = c0 + k * (int)blockDim.x + (int)threadIdx.x;
+          if (c < n)
+            *reinterpret_cast<uint4 *>(win + wl[l].lds + c * 16) =
+                make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+        }
+      }
+    }
+  };
+
+  // the zero row, and the levels held whole
+  for (int i = threadIdx.x; i < RB / 4; i += blockDim.x) reinterpret_cast<uint32_t *>(win)[i] = 0u;
+  stage(1);
+
+  // the window level's rows: histogram of the block's cell rows on it (staged
+  // past the whole levels), then the R consecutive rows that hold the most
+  // samples whole
+  int wlev = -1;
+  for (int l = 0; l < L; ++l)
+    if (wl[l].mode == 2) wlev = l;
+  if (wlev >= 0) {
+    const int H = lv[wlev].H, W = lv[wlev].W, R = wl[wlev].rows;
+    uint32_t *hist = reinterpret_cast<uint32_t *>(win + wl[wlev].lds);  // H + 1 bins: row y0 + 1
+    for (int i = threadIdx.x; i <= H; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    constexpr int kBatch = 4;
+    for (int t0 = 0; t0 < nq * K; t0 += kBatch * (int)blockDim.x) {
+      float u[kBatch], v[kBatch];
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        int t = t0 + r * (int)blockDim.x + (int)threadIdx.x;
+        t = t < nq * K ? t : 0;
+        const int i = t / K, k = t - i * K;
+        const int64_t gs = (((int64_t)b * a.Q + q0 + i) * M + m) * LK + wlev * K + k;
+        u[r] = ld<T>(a.loc, 2 * gs);
+        v[r] = ld<T>(a.loc, 2 * gs + 1);
+      }
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        if (t0 + r * (int)blockDim.x + (int)threadIdx.x >= nq * K) break;
+        const double xf = floor((double)u[r] * (double)W - 0.5);
+        const double yf = floor((double)v[r] * (double)H - 0.5);
+        if (xf >= -1.0 && xf < (double)W && yf >= -1.0 && yf < (double)H)
+          __hip_atomic_fetch_add(&hist[(int)yf + 1], 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // inclusive prefix sums of hist, in place (one wave, 64 bins a round)
+      uint32_t carry = 0;
+      for (int base = 0; base <= H; base += 64) {
+        const int i = base + (int)threadIdx.x;
+        uint32_t x = i <= H ? hist[i] : 0u;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(x, o);
+          if ((int)threadIdx.x >= o) x += y;
+        }
+        if (i <= H) hist[i] = x + carry;
+        carry += __shfl(x, 63);
+      }
+      // coverage of the rows [w0, w0 + R): cells y0 in [w0, w0 + R - 2], plus
+      // y0 = -1 when w0 = 0 and y0 = H - 1 when w0 = H - R
+      uint32_t best = 0;
+      int best_w0 = 0;
+      for (int w0 = threadIdx.x; w0 <= H - R; w0 += 64) {
+        uint32_t cov = hist[w0 + R - 1] - hist[w0];
+        if (w0 == 0) cov += hist[0];
+        if (w0 == H - R) cov += hist[H] - hist[H - 1];
+        if (cov > best) {
+          best = cov;
+          best_w0 = w0;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t ob = __shfl_xor(best, o);
+        const int ow = __shfl_xor(best_w0, o);
+        if (ob > best || (ob == best && ow < best_w0)) {
+          best = ob;
+          best_w0 = ow;
+        }
+      }
+      if (threadIdx.x == 0) best_shared = best_w0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) wl[wlev].y0 = best_shared;
+    __syncthreads();
+    stage(2);
+  }
+  __syncthreads();
+
+  // Every wave walks chunks of HPW head-queries on its own (chunks wave,
+  // wave + nwaves, ...): geometry into its own LDS table, then the gather; no
+  // block barrier, so one wave's geometry overlaps the others' gathers.
+  const int wave = (int)threadIdx.x / 64, wlane = (int)threadIdx.x % 64;
+  const bool in_lanes = LK <= 64 && (LK & (LK - 1)) == 0;
+  const bool staged = SOFTMAX && !in_lanes;
+  const int gs_stride = HPW + 1;
+  char *wbase = smem + (uint32_t)wave * win_wave_bytes(LK, G, staged);
+  Corners *geo = reinterpret_cast<Corners *>(wbase);
+  float *zb = reinterpret_cast<float *>(geo + LK * gs_stride);  // [HPW][L*K + 1]
+  float *inv = zb + HPW * (LK + 1);
+  const int grp = wlane / G, lane = wlane % G;
+  const uint32_t lane_off = (uint32_t)(lane * RL::kLaneBytes);
+
+  for (int h0 = wave * HPW; h0 < nq; h0 += wa.nwaves * HPW) {
+    const int nh = min(HPW, nq - h0);
+    const int64_t hq_first = ((int64_t)b * a.Q + q0 + h0) * M + m;  // hq of chunk entry 0
+    if (staged) {
+      // the chunk's logits; lane hl < nh turns its row into exp(z - max) and 1 / sum
+      const int zs = LK + 1;
+      for (int s = wlane; s < nh * LK; s += 64) {
+        const int hl = s / LK;
+        zb[hl * zs + s - hl * LK] = ld<T>(a.attn, (hq_first + (int64_t)hl * M) * LK + s - hl * LK);
+      }
+      wave_lds_sync();
+      if (wlane < nh) {
+        float *z = zb + wlane * zs;
+        float mx = z[0];
+        for (int j = 1; j < LK; ++j) mx = z[j] > mx ? z[j] : mx;
+        float sum = 0.0f;
+        for (int j = 0; j < LK; ++j) {
+          const float e = expf(z[j] - mx);
+          z[j] = e;
+          sum += e;
+        }
+        inv[wlane] = 1.0f / sum;
+      }
+      wave_lds_sync();
+    }
+    // geometry, one lane per sample (32-bit sample offsets from the chunk's first)
+    const T *locp = reinterpret_cast<const T *>(a.loc) + 2 * hq_first * LK;
+    const T *attp = reinterpret_cast<const T *>(a.attn) + hq_first * LK;
+    for (int s = wlane; s < nh * LK; s += 64) {
+      const int hl = (int)fdiv((uint32_t)s, wa.div_lk);
+      const int j = s - hl * LK;
+      const uint32_t gs = (uint32_t)hl * (uint32_t)(M * LK) + (uint32_t)j;
+      float u, v;
+      if constexpr (sizeof(T) == 4) {
+        const float2 uv = reinterpret_cast<const float2 *>(locp)[gs];
+        u = uv.x;
+        v = uv.y;
+      } else {
+        const uint32_t uv = reinterpret_cast<const uint32_t *>(locp)[gs];
+        u = Half<T>::lo(uv);
+        v = Half<T>::hi(uv);
+      }
+      float w;
+      if constexpr (SOFTMAX)
+        w = in_lanes ? group_softmax(to_float<T>(attp[gs]), LK) : zb[hl * (LK + 1) + j] * inv[hl];
+      else
+        w = to_float<T>(attp[gs]);
+      const int l = (int)fdiv((uint32_t)j, wa.div_k);
+      Corners cs;
+      sample_corners_any(u, v, lv[l], wl[l], (uint32_t)RB, row_base, row_stride, head_off, cs);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cs.w[c] *= w;
+      geo[j * gs_stride + hl] = cs;
+    }
+    wave_lds_sync();
+
+    // gather, in two passes, so that the registers LDS reads fill are never
+    // targets of global loads still in flight (no LDS read then waits for them):
+    //   1. samples on global levels, buffer loads, PIPE samples in flight (a
+    //      sample's buffer u is consumed and refilled with the sample PIPE on);
+    //   2. samples on LDS-held levels.
+    // Each head-query adds its samples in the same order in every block.
+    if (grp < nh) {
+      float acc[RL::VEC];
+#pragma unroll
+      for (int i = 0; i < RL::VEC; ++i) acc[i] = 0.0f;
+      auto fma_rows = [&](const uint32_t (&raw)[4][RL::WORDS], const float (&w)[4]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float x[RL::VEC];
+          unpack<T, RL::WORDS>(raw[c], x);
+#pragma unroll
+          for (int i = 0; i < RL::VEC; ++i) acc[i] = fmaf(w[c], x[i], acc[i]);
+        }
+      };
+      // pass 1: whole rounds of PIPE samples pipelined, then the tail one by one
+      {
+        const int n = jcount[0];
+        const int n_main = n / PIPE * PIPE;
+        uint32_t raw[PIPE][4][RL::WORDS];
+        float wt[PIPE][4];
+        auto issue = [&](int u, int t) {
+          const Corners cs = geo[(int)jlist[0][t] * gs_stride + grp];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[u][c]);
+            wt[u][c] = cs.w[c];
+          }
+        };
+        if (n_main > 0) {
+#pragma unroll
+          for (int u = 0; u < PIPE; ++u) issue(u, u);
+          for (int t0 = PIPE; t0 < n_main; t0 += PIPE) {
+#pragma unroll
+            for (int u = 0; u < PIPE; ++u) {
+              fma_rows(raw[u], wt[u]);
+              issue(u, t0 + u);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < PIPE; ++u) fma_rows(raw[u], wt[u]);
+        }
+        for (int t = n_main; t < n; ++t) {
+          issue(0, t);
+          fma_rows(raw[0], wt[0]);
+        }
+      }
+      // pass 2, in the samples' order: LDS reads, or for a sample whose cell
+      // leaves the held rows (rare), global loads in its place, so that the
+      // order of the additions does not depend on which samples fall back
+      const int n = jcount[1];
+      // an LDS-mode offset carries kLdsFlag: adding (window + lane - kLdsFlag)
+      // yields the LDS address
+      const uint32_t lane_win_flag = lds_offset_of(win) + lane_off - kLdsFlag;
+      auto rows = [&](int t, uint32_t (&raw)[4][RL::WORDS], float (&wt)[4]) {
+        const Corners cs = geo[(int)jlist[1][t] * gs_stride + grp];
+        if ((cs.off[0] >> 30) == 1u) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) lds_load_at<RL::WORDS>(cs.off[c] + lane_win_flag, raw[c]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) buffer_load<RL::WORDS>(rsrc, cs.off[c] + lane_off, raw[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wt[c] = cs.w[c];
+      };
+      int t = 0;
+      for (; t + 2 <= n; t += 2) {
+        uint32_t raw[2][4][RL::WORDS];
+        float wt[2][4];
+        rows(t, raw[0], wt[0]);
+        rows(t + 1, raw[1], wt[1]);
+        fma_rows(raw[0], wt[0]);
+        fma_rows(raw[1], wt[1]);
+      }
+      if (t < n) {
+        uint32_t raw[4][RL::WORDS];
+        float wt[4];
+        rows(t, raw, wt);
+        fma_rows(raw, wt);
+      }
+      uint32_t ow[RL::WORDS];
+      pack<T, RL::WORDS>(acc, ow);
+      char *out = reinterpret_cast<char *>(a.out) +
+                  (hq_first + (int64_t)grp * M) * (int64_t)RL::kRowBytes + lane_off;
+      global_store<RL::WORDS>(out, ow);
+    }
+    wave_lds_sync();  // the next chunk rewrites this wave's tables
+  }
+}
+
 // ----------------------------------------------------------------- backward
 
 // Scatter of a * w_c * g into the grad_value accumulator for one corner.
@@ -656,13 +1135,96 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The LDS-window forward's launch shape: head-queries per sub-batch (the
+// geometry table, at most kWinGeoMax bytes), the LDS split, queries per block
+// (about two blocks per CU over the launch).  False when it does not suit the
+// launch: too few queries per (batch, head) for the staging to pay off, or
+// too little LDS; the direct gather runs then.
+constexpr size_t kWinGeoMax = 75 * 1024;  // the waves' geometry tables together
+#ifndef MSDA_WIN_PIPE
+#define MSDA_WIN_PIPE 2
+#endif
+#ifndef MSDA_WIN_BLOCKS_PER_CU
+#define MSDA_WIN_BLOCKS_PER_CU 2
+#endif
+constexpr int kWinPipe = MSDA_WIN_PIPE;              // samples in flight per lane
+constexpr int kWinBlocksPerCu = MSDA_WIN_BLOCKS_PER_CU;  // blocks per CU over the launch
+constexpr size_t kWinStaticReserve = 1024;  // the kernel's static LDS (levels, plan)
+
+struct WinLaunch {
+  WinArgs wa;
+  int threads;
+  size_t lds;
+  int64_t blocks;
+};
+
+// 0: the window schedule when it suits the launch; 1: always the direct gather;
+// 2: the window schedule whenever the LDS holds it (a test hook, per thread)
+thread_local int g_fwd_schedule = 0;
+
+template <typename T, int D>
+bool plan_win_launch(const LaunchArgs &a, bool softmax, WinLaunch &w) {
+  if (g_fwd_schedule == 1) return false;
+  using RL = RowLayout<T, D>;
+  const int LK = (int)(a.L * a.K);
+  const bool staged = softmax && !(LK <= 64 && (LK & (LK - 1)) == 0);
+  const size_t per_wave = win_wave_bytes(LK, RL::G, staged);
+  const int nwaves = (int)std::min<size_t>(kWinThreads / 64, kWinGeoMax / per_wave);
+  // the block is the CU's only one (its LDS): with fewer than 16 waves it hides
+  // too little latency (measured slower than the direct gather: bf16 rows with
+  // L*K = 12 or 32 get 11 and 4 waves), unless a test forces the schedule
+  if (nwaves < (g_fwd_schedule == 2 ? 4 : kWinThreads / 64)) return false;
+  int dev = 0, max_lds = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  const size_t total = (size_t)max_lds > kWinStaticReserve ? (size_t)max_lds - kWinStaticReserve : 0;
+  const size_t geo = per_wave * nwaves;
+  // the window area must hold the zero row and the cell-row histogram of a window level
+  if (total < geo + 32 * 1024) return false;
+  const int64_t bm = a.nb * a.M;
+  int64_t nsplit = std::max<int64_t>(1, (kWinBlocksPerCu * (int64_t)cus + bm - 1) / bm);
+  int64_t qb = (a.Q + nsplit - 1) / nsplit;
+  const int64_t hq_block = (int64_t)nwaves * (64 / RL::G);
+  if (qb < 4 * hq_block && g_fwd_schedule != 2) return false;
+  nsplit = (a.Q + qb - 1) / qb;
+  w.wa.div_lk = make_fastdiv((uint32_t)LK);
+  w.wa.div_k = make_fastdiv((uint32_t)a.K);
+  w.wa.nwaves = nwaves;
+  w.wa.qb = (int)qb;
+  w.wa.nsplit = (int)nsplit;
+  w.wa.geo_bytes = (uint32_t)geo;
+  w.wa.win_bytes = (uint32_t)((total - geo) / 16 * 16);
+  w.threads = nwaves * 64;
+  w.lds = geo + w.wa.win_bytes;
+  w.blocks = padded_grid(bm * nsplit);
+  return w.blocks <= 0x7fffffff;
+}
+
+template <typename T, int D>
+hipError_t fwd_launch_any(const LaunchArgs &a, bool softmax, hipStream_t stream) {
+  WinLaunch w;
+  if (!plan_win_launch<T, D>(a, softmax, w)) return fwd_launch<T, D>(a, softmax, stream);
+  const char *name = softmax ? "fwd_softmax" : "fwd";
+  prof_begin(stream, name);
+  if (softmax)
+    hipLaunchKernelGGL((fwd_win_kernel<T, D, true, kWinPipe>), dim3((unsigned)w.blocks),
+                       dim3(w.threads), w.lds, stream, a, w.wa);
+  else
+    hipLaunchKernelGGL((fwd_win_kernel<T, D, false, kWinPipe>), dim3((unsigned)w.blocks),
+                       dim3(w.threads), w.lds, stream, a, w.wa);
+  prof_end(stream, name);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t fwd_dispatch_d(const LaunchArgs &a, bool softmax, hipStream_t s) {
   switch (a.D) {
-    case 8: return fwd_launch<T, 8>(a, softmax, s);
-    case 16: return fwd_launch<T, 16>(a, softmax, s);
-    case 32: return fwd_launch<T, 32>(a, softmax, s);
-    case 64: return fwd_launch<T, 64>(a, softmax, s);
+    case 8: return fwd_launch_any<T, 8>(a, softmax, s);
+    case 16: return fwd_launch_any<T, 16>(a, softmax, s);
+    case 32: return fwd_launch_any<T, 32>(a, softmax, s);
+    case 64: return fwd_launch_any<T, 64>(a, softmax, s);
   }
   return hipErrorInvalidValue;
 }
@@ -679,6 +1241,8 @@ hipError_t bwd_dispatch_d(const LaunchArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+void set_forward_schedule(int schedule) { g_fwd_schedule = schedule; }
 
 hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream, bool softmax) {
   if (a.nb * a.Q * a.M == 0) return hipSuccess;

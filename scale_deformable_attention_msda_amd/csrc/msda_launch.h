@@ -169,6 +169,9 @@ enum class Dtype { F32, BF16, F16 };
 // in the data type (BF16 or F16 data only)
 enum class Accum { F32, PACKED };
 
+// Forward schedule for later launches on this thread (test hook): 0 automatic,
+// 1 always the direct gather, 2 the LDS-window gather whenever it fits.
+void set_forward_schedule(int schedule);
 // softmax: a.attn holds raw logits, normalised per head-query inside the kernel
 hipError_t launch_forward(const LaunchArgs &a, Dtype dt, hipStream_t stream, bool softmax = false);
 // Row passes of the softmax method over n_rows rows of lk logits each:

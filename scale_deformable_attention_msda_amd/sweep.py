@@ -220,7 +220,10 @@ def _counter_csv_rows(d: str) -> list[dict]:
 
 
 def _kernel_base(name: str) -> str:
-    base = name.split("(")[0].split("<")[0]
+    """'void msda::(anonymous namespace)::tile_kernel<float, 32>(msda::BinArgs)' -> 'tile_kernel'."""
+    base = name.split("<")[0]
+    if "(" in base.split("::")[-1]:  # a kernel without template arguments
+        base = base[:base.rindex("(")]
     return base.split("::")[-1].strip()
 
 
