@@ -9,9 +9,10 @@ independent outer loops); this module only builds it with gcc, converts the
 operands to contiguous fp64 / int64 arrays (exact upcasts from fp32 or bf16)
 and calls it through ctypes.  What it computes, and where the pages define it,
 is stated in the C file: chapter 1 of the msda-triton course ("Deformable
-attention, from scratch"), sections "The equation, term by term",
-"Bilinear interpolation: reading between the pixels" and "The simplest
-possible implementation"; the gradients are derived there by hand.
+attention, from scratch"), sections "The equation, term by term" (the
+attention-weighted sum of level samples) and "Bilinear interpolation: reading
+between the pixels" (the tent-weighted pixels around a point); the gradients
+are derived there by hand.
 
 Every function of the oracle is pinned by ``tests/test_oracle_pins.py``
 (brute-force tent sums, closed forms, library routines, finite differences).

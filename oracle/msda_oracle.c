@@ -10,18 +10,25 @@
  *
  * Source of the definition: "1. Deformable attention, from scratch" (the
  * msda-triton course, chapter 1):
- *   - section "The equation, term by term": the tensor shapes
+ *   - section "The equation, term by term": the output of head m of query q is
+ *     the sum over levels l and points k of the attention weight A[b,q,m,l,k]
+ *     times the value of level l sampled at the point's location, with shapes
  *       value               (B, S, M, D)   flattened pyramid, per head
  *       spatial_shapes      (L, 2)         rows are (H_l, W_l)
+ *       level_start_index   (L,)           first pyramid row of each level
  *       sampling_locations  (B, Q, M, L, K, 2), last axis (x, y), normalised
  *       attention_weights   (B, Q, M, L, K)
- *       output              (B, Q, M*D)
- *   - section "Bilinear interpolation: reading between the pixels": the four
- *     corners and their weights, the pixel-centre mapping x = loc_x*W - 0.5,
- *     and zero contribution from corners outside the map;
- *   - section "The simplest possible implementation": the six nested loops,
- *     the use of floor, the per-corner bounds test and the row index
- *     start_l + yy*W_l + xx into the flattened pyramid.
+ *       output              (B, Q, M*D);
+ *   - section "Bilinear interpolation: reading between the pixels": a sample
+ *     between pixels blends the four surrounding pixels, each weighted by the
+ *     product of the fractional distances along x and y, with pixel centres
+ *     at integer coordinates x = loc_x * W - 0.5 and pixels outside the map
+ *     contributing zero.  Written out, that is the tent (hat) kernel:
+ *       sample(x, y) = sum over pixels (i, j) inside the map of
+ *                      tent(x - j) * tent(y - i) * V[i, j],   tent(t) = max(0, 1 - |t|),
+ *     whose non-zero terms are the (at most) four pixels of the cell
+ *     floor(x) .. floor(x) + 1, floor(y) .. floor(y) + 1.  A pixel (i, j) of
+ *     level l is pyramid row level_start_index[l] + i * W_l + j.
  * The pages use the attention weights as given by default (DeformOps page,
  * section "Multi-scale deformable attention"); the same section names a
  * second method, "softmax", that normalises raw logits jointly over levels
@@ -29,15 +36,15 @@
  * the end of this file; the operator itself never normalises.
  *
  * The gradients are not printed on the pages (the course's backward chapter
- * is not among them).  They are derived here by differentiating the forward
- * loop by hand; every formula is stated where it is used.
+ * is not among them).  They follow from the sum above: it is linear in the
+ * weights and in the value, and its x-derivative takes the slope of each tent
+ * factor; every formula is stated where it is used.
  *
  * Arithmetic: all inputs arrive as fp64 (exact upcasts of fp32 or bf16), and
- * every accumulation is fp64.  The pixel coordinate is computed as in the
- * naive loop, a float multiply then a subtraction, in fp64.  The product of a
- * 24-bit significand and an integer size below 2^29 is exact in fp64, so the
- * floor decision is the exact one.  Build with -ffp-contract=off so that no
- * other expression is fused either.
+ * every accumulation is fp64.  The pixel coordinate is a multiply then a
+ * subtraction in fp64; the product of a 24-bit significand and an integer
+ * size below 2^29 is exact in fp64, so the cell is the exact one.  Built with
+ * -ffp-contract=off so that no expression is fused.
  */
 #include <math.h>
 #include <omp.h>
@@ -47,60 +54,55 @@
 /* Threads the oracle's parallel loops use (reported beside its timings). */
 int msda_oracle_threads(void) { return omp_get_max_threads(); }
 
-/* Geometry of one bilinear sample at one pyramid level. */
-typedef struct {
-    int64_t row[4]; /* flattened-pyramid row of corners 00, 01, 10, 11; -1 = outside */
-    double w[4];    /* bilinear weight of each corner */
-    double lx, ly;  /* fractional parts of the pixel coordinate */
-    int any_valid;  /* at least one corner lies inside the map */
-} corner_set;
-
-/*
- * Corners of the sample at normalised (u, v) on a level of H x W pixels whose
- * rows start at `start` in the flattened pyramid.
- * Chapter 1, "Bilinear interpolation": x = u*W - 0.5, y = v*H - 0.5;
- * x0 = floor(x), y0 = floor(y), lx = x - x0, ly = y - y0;
- * corner 00 = (y0, x0) with weight (1-lx)(1-ly), 01 = (y0, x0+1) with
- * lx(1-ly), 10 = (y0+1, x0) with (1-lx)ly, 11 = (y0+1, x0+1) with lx*ly.
- * A corner is used only when 0 <= xx < W and 0 <= yy < H.  The test is made
- * on the floating-point corner position, so a NaN or infinite coordinate
- * fails it and no integer conversion of such a value ever happens.
- */
-static void level_corners(double u, double v, int64_t H, int64_t W, int64_t start,
-                          corner_set *cs)
+/* The tent (hat) kernel of bilinear interpolation. */
+static double tent(double t)
 {
-    double x = u * (double)W - 0.5;
-    double y = v * (double)H - 0.5;
-    double x0 = floor(x);
-    double y0 = floor(y);
-    double lx = x - x0;
-    double ly = y - y0;
-    double cy[4] = {y0, y0, y0 + 1.0, y0 + 1.0};
-    double cx[4] = {x0, x0 + 1.0, x0, x0 + 1.0};
+    double a = fabs(t);
+    return a < 1.0 ? 1.0 - a : 0.0;
+}
 
-    cs->w[0] = (1.0 - lx) * (1.0 - ly);
-    cs->w[1] = lx * (1.0 - ly);
-    cs->w[2] = (1.0 - lx) * ly;
-    cs->w[3] = lx * ly;
-    cs->lx = lx;
-    cs->ly = ly;
-    cs->any_valid = 0;
-    for (int c = 0; c < 4; ++c) {
-        int inside = cx[c] >= 0.0 && cx[c] < (double)W && cy[c] >= 0.0 && cy[c] < (double)H;
-        if (inside) {
-            cs->row[c] = start + (int64_t)cy[c] * W + (int64_t)cx[c];
-            cs->any_valid = 1;
-        } else {
-            cs->row[c] = -1;
+/* The pixels of an H x W map that lie in the cell of (x, y) (pixel
+ * coordinates, centres at integers), with their tent factors along x and y
+ * and the slopes of those factors: on the cell [floor(x), floor(x) + 1] the
+ * factor of the left column falls with slope -1 and that of the right column
+ * rises with slope +1 (the derivative from the right at an integer x, the
+ * side floor() puts the point on; likewise along y). */
+typedef struct {
+    int n;                /* pixels of the cell inside the map (0 to 4) */
+    int64_t pix[4];       /* i * W + j of each */
+    double wx[4], wy[4];  /* tent(x - j), tent(y - i) */
+    double sx[4], sy[4];  /* d tent(x - j) / dx, d tent(y - i) / dy */
+} cell_taps;
+
+static void cell_of(double x, double y, int64_t H, int64_t W, cell_taps *t)
+{
+    double xc = floor(x);
+    double yc = floor(y);
+    t->n = 0;
+    for (int dy = 0; dy < 2; ++dy) {
+        for (int dx = 0; dx < 2; ++dx) {
+            double px = xc + (double)dx;
+            double py = yc + (double)dy;
+            /* the test is made on the floating-point pixel position: a NaN or
+             * infinite coordinate fails it, and no integer conversion of such
+             * a value ever happens */
+            if (!(px >= 0.0 && px < (double)W && py >= 0.0 && py < (double)H))
+                continue;
+            t->pix[t->n] = (int64_t)py * W + (int64_t)px;
+            t->wx[t->n] = tent(x - px);
+            t->wy[t->n] = tent(y - py);
+            t->sx[t->n] = (px == xc) ? -1.0 : 1.0;
+            t->sy[t->n] = (py == yc) ? -1.0 : 1.0;
+            t->n += 1;
         }
     }
 }
 
 /*
- * Forward.  For every (b, q, m):
- *   out[b, q, m*D + d] = sum over l, k, valid corners c of
- *                        a[b,q,m,l,k] * w_c * value[b, row_c, m, d].
- * Loop order and product order follow the naive loop of chapter 1.
+ * Forward.  For every (b, q, m): first the bilinear samples of all levels and
+ * points, then their sum weighted by the attention weights:
+ *   out[b, q, m*D + d] = sum_{l,k} A[b,q,m,l,k] * sample_l(x_lk, y_lk)[d],
+ *   x = u * W_l - 0.5, y = v * H_l - 0.5 for the sample's location (u, v).
  * Parallel over (b, q): each pair writes its own output rows only.
  */
 void msda_oracle_forward(const double *value, const int64_t *spatial_shapes,
@@ -111,28 +113,38 @@ void msda_oracle_forward(const double *value, const int64_t *spatial_shapes,
 #pragma omp parallel for collapse(2) schedule(dynamic, 16)
     for (int64_t b = 0; b < B; ++b) {
         for (int64_t q = 0; q < Q; ++q) {
+            double smp[L * K][D];  /* the sample of every (level, point) */
             for (int64_t m = 0; m < M; ++m) {
-                double *o = out + ((b * Q + q) * M + m) * D;
-                for (int64_t d = 0; d < D; ++d)
-                    o[d] = 0.0;
+                const int64_t hq = (b * Q + q) * M + m;
                 for (int64_t l = 0; l < L; ++l) {
-                    int64_t H = spatial_shapes[2 * l];
-                    int64_t W = spatial_shapes[2 * l + 1];
-                    int64_t start = level_start_index[l];
+                    const int64_t H = spatial_shapes[2 * l];
+                    const int64_t W = spatial_shapes[2 * l + 1];
+                    /* level l of head m of image b: its pixel p is pyramid row start + p */
+                    const double *img = value + ((b * S + level_start_index[l]) * M + m) * D;
                     for (int64_t k = 0; k < K; ++k) {
-                        int64_t s = (((b * Q + q) * M + m) * L + l) * K + k;
-                        double a = attention_weights[s];
-                        corner_set cs;
-                        level_corners(sampling_locations[2 * s], sampling_locations[2 * s + 1],
-                                      H, W, start, &cs);
-                        for (int c = 0; c < 4; ++c) {
-                            if (cs.row[c] < 0)
-                                continue;
-                            const double *vr = value + ((b * S + cs.row[c]) * M + m) * D;
+                        const int64_t s = hq * L * K + l * K + k;
+                        double u = sampling_locations[2 * s], v = sampling_locations[2 * s + 1];
+                        double x = u * (double)W - 0.5;
+                        double y = v * (double)H - 0.5;
+                        cell_taps t;
+                        cell_of(x, y, H, W, &t);
+                        double *dst = smp[l * K + k];
+                        for (int64_t d = 0; d < D; ++d)
+                            dst[d] = 0.0;
+                        for (int c = 0; c < t.n; ++c) {
+                            const double *vr = img + t.pix[c] * M * D;
                             for (int64_t d = 0; d < D; ++d)
-                                o[d] += a * cs.w[c] * vr[d];
+                                dst[d] += t.wx[c] * t.wy[c] * vr[d];
                         }
                     }
+                }
+                double *o = out + hq * D;
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] = 0.0;
+                for (int64_t j = 0; j < L * K; ++j) {
+                    const double a = attention_weights[hq * L * K + j];
+                    for (int64_t d = 0; d < D; ++d)
+                        o[d] += a * smp[j][d];
                 }
             }
         }
@@ -140,20 +152,18 @@ void msda_oracle_forward(const double *value, const int64_t *spatial_shapes,
 }
 
 /*
- * Backward, by differentiating the forward above.  With g = grad_out[b,q,m,:]
- * and, per sample, V_c the value row of corner c (zero when outside):
- *   p_c                      = <g, V_c>
- *   grad_attention_weights   = sum_c w_c p_c
- *   grad_value[b, row_c, m]  += a * w_c * g                 (valid corners)
- *   d out / d lx             = a * ((1-ly)(V01 - V00) + ly (V11 - V10))
- *   d out / d ly             = a * ((1-lx)(V10 - V00) + lx (V11 - V01))
- *   dx/du = W, dy/dv = H  (from x = u*W - 0.5), so
- *   grad_loc_x = a * W * ((1-ly)(p01 - p00) + ly (p11 - p10))
- *   grad_loc_y = a * H * ((1-lx)(p10 - p00) + lx (p11 - p01)).
- * The mask of valid corners is piecewise constant, so outside corners enter
- * as V_c = 0.  On a cell edge (lx or ly exactly 0) these are the derivatives
- * from the right, the side that floor assigns the point to.  A sample with no
- * corner inside the map (including NaN or infinite coordinates) contributes
+ * Backward of <out, g>, g = grad_out[b,q,m,:], from the sum above.  For each
+ * sample, with s = sample(x, y) and its partial derivatives
+ *   ds/dx = sum over the cell's pixels of tent'(x - j) tent(y - i) V[i, j],
+ *   ds/dy = sum over the cell's pixels of tent(x - j) tent'(y - i) V[i, j]
+ * (tent' the slopes of cell_of; outside pixels are zero, a piecewise-constant
+ * mask, so they drop out of the derivatives too):
+ *   grad_attention_weights = <g, s>                       (out is linear in A)
+ *   grad_loc_x             = A * W * <g, ds/dx>            (dx/du = W)
+ *   grad_loc_y             = A * H * <g, ds/dy>            (dy/dv = H)
+ *   grad_value[pixel]     += A * tent(x - j) tent(y - i) * g   (out is linear in V)
+ * A sample whose cell has no pixel inside the map (NaN or infinite
+ * coordinates included) has s = 0 and zero derivatives: it contributes
  * nothing and gets zero gradients.
  *
  * grad_value is overwritten: zeroed, then accumulated.  Parallel over (b, m):
@@ -171,45 +181,49 @@ void msda_oracle_backward(const double *value, const int64_t *spatial_shapes,
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int64_t b = 0; b < B; ++b) {
         for (int64_t m = 0; m < M; ++m) {
+            double smp[D], dsx[D], dsy[D];
             for (int64_t q = 0; q < Q; ++q) {
-                const double *g = grad_out + ((b * Q + q) * M + m) * D;
+                const int64_t hq = (b * Q + q) * M + m;
+                const double *g = grad_out + hq * D;
                 for (int64_t l = 0; l < L; ++l) {
-                    int64_t H = spatial_shapes[2 * l];
-                    int64_t W = spatial_shapes[2 * l + 1];
-                    int64_t start = level_start_index[l];
+                    const int64_t H = spatial_shapes[2 * l];
+                    const int64_t W = spatial_shapes[2 * l + 1];
+                    const int64_t row0 = b * S + level_start_index[l];
+                    const double *img = value + (row0 * M + m) * D;
+                    double *gimg = grad_value + (row0 * M + m) * D;
                     for (int64_t k = 0; k < K; ++k) {
-                        int64_t s = (((b * Q + q) * M + m) * L + l) * K + k;
-                        double a = attention_weights[s];
-                        corner_set cs;
-                        level_corners(sampling_locations[2 * s], sampling_locations[2 * s + 1],
-                                      H, W, start, &cs);
-                        if (!cs.any_valid) {
-                            grad_attn[s] = 0.0;
-                            grad_loc[2 * s] = 0.0;
-                            grad_loc[2 * s + 1] = 0.0;
-                            continue;
+                        const int64_t s = hq * L * K + l * K + k;
+                        const double a = attention_weights[s];
+                        double u = sampling_locations[2 * s], v = sampling_locations[2 * s + 1];
+                        double x = u * (double)W - 0.5;
+                        double y = v * (double)H - 0.5;
+                        cell_taps t;
+                        cell_of(x, y, H, W, &t);
+                        for (int64_t d = 0; d < D; ++d) {
+                            smp[d] = 0.0;
+                            dsx[d] = 0.0;
+                            dsy[d] = 0.0;
                         }
-                        double p[4];
-                        for (int c = 0; c < 4; ++c) {
-                            p[c] = 0.0;
-                            if (cs.row[c] < 0)
-                                continue;
-                            const double *vr = value + ((b * S + cs.row[c]) * M + m) * D;
-                            for (int64_t d = 0; d < D; ++d)
-                                p[c] += g[d] * vr[d];
+                        for (int c = 0; c < t.n; ++c) {
+                            const double *vr = img + t.pix[c] * M * D;
+                            for (int64_t d = 0; d < D; ++d) {
+                                smp[d] += t.wx[c] * t.wy[c] * vr[d];
+                                dsx[d] += t.sx[c] * t.wy[c] * vr[d];
+                                dsy[d] += t.wx[c] * t.sy[c] * vr[d];
+                            }
                         }
-                        double lx = cs.lx, ly = cs.ly;
-                        grad_attn[s] = cs.w[0] * p[0] + cs.w[1] * p[1] + cs.w[2] * p[2] +
-                                       cs.w[3] * p[3];
-                        grad_loc[2 * s] =
-                            a * (double)W * ((1.0 - ly) * (p[1] - p[0]) + ly * (p[3] - p[2]));
-                        grad_loc[2 * s + 1] =
-                            a * (double)H * ((1.0 - lx) * (p[2] - p[0]) + lx * (p[3] - p[1]));
-                        for (int c = 0; c < 4; ++c) {
-                            if (cs.row[c] < 0)
-                                continue;
-                            double *gv = grad_value + ((b * S + cs.row[c]) * M + m) * D;
-                            double aw = a * cs.w[c];
+                        double ga = 0.0, gx = 0.0, gy = 0.0;
+                        for (int64_t d = 0; d < D; ++d) {
+                            ga += g[d] * smp[d];
+                            gx += g[d] * dsx[d];
+                            gy += g[d] * dsy[d];
+                        }
+                        grad_attn[s] = ga;
+                        grad_loc[2 * s] = a * (double)W * gx;
+                        grad_loc[2 * s + 1] = a * (double)H * gy;
+                        for (int c = 0; c < t.n; ++c) {
+                            double *gv = gimg + t.pix[c] * M * D;
+                            double aw = a * t.wx[c] * t.wy[c];
                             for (int64_t d = 0; d < D; ++d)
                                 gv[d] += aw * g[d];
                         }

@@ -22,42 +22,38 @@ def test_pin(pin):
 
 # (description, exact text in msda_oracle.c, replacement)
 MUTANTS = [
-    ("pixel centre offset dropped", "double x = u * (double)W - 0.5;",
-     "double x = u * (double)W;"),
-    ("y scaled by W (transposed shape)", "double y = v * (double)H - 0.5;",
-     "double y = v * (double)W - 0.5;"),
-    ("corner 01 weight transposed", "cs->w[1] = lx * (1.0 - ly);",
-     "cs->w[1] = ly * (1.0 - lx);"),
-    ("corner 11 weight wrong", "cs->w[3] = lx * ly;", "cs->w[3] = lx * lx;"),
-    ("row stride H instead of W", "cs->row[c] = start + (int64_t)cy[c] * W + (int64_t)cx[c];",
-     "cs->row[c] = start + (int64_t)cy[c] * H + (int64_t)cx[c];"),
-    ("level start ignored", "cs->row[c] = start + (int64_t)cy[c] * W + (int64_t)cx[c];",
-     "cs->row[c] = (int64_t)cy[c] * W + (int64_t)cx[c];"),
-    ("x bound off by one", "cx[c] < (double)W", "cx[c] <= (double)W"),
-    ("corner x0+1 swapped to x0-1", "double cx[4] = {x0, x0 + 1.0, x0, x0 + 1.0};",
-     "double cx[4] = {x0, x0 - 1.0, x0, x0 - 1.0};"),
-    ("attention weight dropped in forward", "o[d] += a * cs.w[c] * vr[d];",
-     "o[d] += cs.w[c] * vr[d];"),
-    ("value and head index transposed", "const double *vr = value + ((b * S + cs.row[c]) * M + m) * D;\n"
-     "                            for (int64_t d = 0; d < D; ++d)\n"
-     "                                o[d]",
-     "const double *vr = value + ((b * S + cs.row[c]) * M + (M - 1 - m)) * D;\n"
-     "                            for (int64_t d = 0; d < D; ++d)\n"
-     "                                o[d]"),
-    ("grad_out dropped from p_c", "p[c] += g[d] * vr[d];", "p[c] += vr[d];"),
-    ("grad_attn uses wrong corner", "cs.w[1] * p[1] + cs.w[2] * p[2]",
-     "cs.w[1] * p[2] + cs.w[2] * p[2]"),
-    ("grad_loc_x sign flipped", "((1.0 - ly) * (p[1] - p[0]) + ly * (p[3] - p[2]))",
-     "((1.0 - ly) * (p[0] - p[1]) + ly * (p[3] - p[2]))"),
-    ("grad_loc_x second term wrong corner", "ly * (p[3] - p[2])", "ly * (p[3] - p[1])"),
-    ("grad_loc_y chain factor W", "a * (double)H * ((1.0 - lx)", "a * (double)W * ((1.0 - lx)"),
-    ("grad_loc_y lx and ly transposed", "((1.0 - lx) * (p[2] - p[0]) + lx * (p[3] - p[1]))",
-     "((1.0 - ly) * (p[2] - p[0]) + ly * (p[3] - p[1]))"),
-    ("grad_loc attention weight dropped", "a * (double)W * ((1.0 - ly)", "(double)W * ((1.0 - ly)"),
-    ("grad_value corner weight dropped", "double aw = a * cs.w[c];", "double aw = a;"),
+    ("pixel centre offset dropped", "double x = u * (double)W - 0.5;\n                        double y = v * (double)H - 0.5;\n                        cell_taps t;\n                        cell_of(x, y, H, W, &t);\n                        double *dst",
+     "double x = u * (double)W;\n                        double y = v * (double)H - 0.5;\n                        cell_taps t;\n                        cell_of(x, y, H, W, &t);\n                        double *dst"),
+    ("y scaled by W (transposed shape)", "double y = v * (double)H - 0.5;\n                        cell_taps t;\n                        cell_of(x, y, H, W, &t);\n                        double *dst",
+     "double y = v * (double)W - 0.5;\n                        cell_taps t;\n                        cell_of(x, y, H, W, &t);\n                        double *dst"),
+    ("tent kernel of the wrong shape", "return a < 1.0 ? 1.0 - a : 0.0;",
+     "return a < 1.0 ? 1.0 - a * a : 0.0;"),
+    ("tent factors use one axis twice", "t->wy[t->n] = tent(y - py);", "t->wy[t->n] = tent(x - px);"),
+    ("row stride H instead of W", "t->pix[t->n] = (int64_t)py * W + (int64_t)px;",
+     "t->pix[t->n] = (int64_t)py * H + (int64_t)px;"),
+    ("level start ignored", "const double *img = value + ((b * S + level_start_index[l]) * M + m) * D;",
+     "const double *img = value + ((b * S) * M + m) * D;"),
+    ("x bound off by one", "px < (double)W", "px <= (double)W"),
+    ("second column swapped to x0-1", "double px = xc + (double)dx;", "double px = xc - (double)dx;"),
+    ("attention weight dropped in forward", "o[d] += a * smp[j][d];", "o[d] += smp[j][d];"),
+    ("value and head index transposed",
+     "const double *img = value + ((b * S + level_start_index[l]) * M + m) * D;",
+     "const double *img = value + ((b * S + level_start_index[l]) * M + (M - 1 - m)) * D;"),
+    ("grad_out dropped from grad_attn", "ga += g[d] * smp[d];", "ga += smp[d];"),
+    ("grad_attn takes the x-derivative", "grad_attn[s] = ga;", "grad_attn[s] = gx;"),
+    ("left-column slope sign flipped", "t->sx[t->n] = (px == xc) ? -1.0 : 1.0;",
+     "t->sx[t->n] = (px == xc) ? 1.0 : -1.0;"),
+    ("x-derivative drops the y factor", "dsx[d] += t.sx[c] * t.wy[c] * vr[d];",
+     "dsx[d] += t.sx[c] * vr[d];"),
+    ("grad_loc_y chain factor W", "a * (double)H * gy", "a * (double)W * gy"),
+    ("grad_loc_y takes the x-slopes", "dsy[d] += t.wx[c] * t.sy[c] * vr[d];",
+     "dsy[d] += t.sx[c] * t.wy[c] * vr[d];"),
+    ("grad_loc attention weight dropped", "a * (double)W * gx", "(double)W * gx"),
+    ("grad_value tent weights dropped", "double aw = a * t.wx[c] * t.wy[c];", "double aw = a;"),
     ("grad_value not zeroed", "memset(grad_value, 0, (size_t)(B * S * M * D) * sizeof(double));",
      "grad_value[0] += 0.0;"),
-    ("empty-sample gradient not cleared", "grad_loc[2 * s] = 0.0;\n", "grad_loc[2 * s] = 1.0;\n"),
+    ("grad_value row of the wrong level", "const int64_t row0 = b * S + level_start_index[l];",
+     "const int64_t row0 = b * S + level_start_index[0];"),
     ("softmax not normalised", "a[j] = a[j] / sum;", "a[j] = a[j] / (sum + 1e-3);"),
     ("softmax sum drops the last term", "sum += a[j];", "sum += (j + 1 < lk) ? a[j] : 0.0;"),
     ("softmax derivative sign", "a[j] * (ga[j] - dot)", "a[j] * (ga[j] + dot)"),
