@@ -49,6 +49,10 @@ GROUPS = {
                  ("pipe8", ["-DMSDA_FWD_PIPE=8"])],
     "fwd_block": [("block128", ["-DMSDA_FWD_BLOCK=128"]), ("block256", ["-DMSDA_FWD_BLOCK=256"]),
                   ("block512", ["-DMSDA_FWD_BLOCK=512"]), ("block1024", ["-DMSDA_FWD_BLOCK=1024"])],
+    "win_pipe": [("winpipe2", ["-DMSDA_WIN_PIPE=2"]), ("winpipe4", ["-DMSDA_WIN_PIPE=4"])],
+    "win_blocks": [("winbpc1", ["-DMSDA_WIN_BLOCKS_PER_CU=1"]),
+                   ("winbpc2", ["-DMSDA_WIN_BLOCKS_PER_CU=2"]),
+                   ("winbpc4", ["-DMSDA_WIN_BLOCKS_PER_CU=4"])],
     "bin_chunk": [("chunk256", ["-DMSDA_BIN_CHUNK=256"]), ("chunk512", ["-DMSDA_BIN_CHUNK=512"]),
                   ("chunk1024", ["-DMSDA_BIN_CHUNK=1024"])],
     "bin_tile": [("tile4", ["-DMSDA_BIN_TILE=4"]), ("tile6", ["-DMSDA_BIN_TILE=6"]),
@@ -59,11 +63,16 @@ GROUPS = {
 }
 # the kernels whose resources each group changes (names as the compiler reports them)
 GROUP_KERNELS = {
-    "fwd_pipe": ["fwd_kernel"], "fwd_block": ["fwd_kernel"], "bin_chunk": ["tile_kernel"],
+    "fwd_pipe": ["fwd_kernel"], "fwd_block": ["fwd_kernel"], "win_pipe": ["fwd_win_kernel"],
+    "win_blocks": ["fwd_win_kernel"], "bin_chunk": ["tile_kernel"],
     "bin_tile": ["tile_kernel"], "count_block": ["count_kernel", "scatter_kernel"],
 }
+# forward schedule of the timed step per group: the direct-gather groups force
+# the direct gather (the encoder takes the LDS-window schedule by default)
+GROUP_SCHEDULE = {"fwd_pipe": "direct", "fwd_block": "direct"}
 # library profile names of the kernels
-PROFILE_NAME = {"fwd_kernel": "fwd", "tile_kernel": "bin_tile", "count_kernel": "bin_count",
+PROFILE_NAME = {"fwd_kernel": "fwd", "fwd_win_kernel": "fwd", "tile_kernel": "bin_tile",
+                "count_kernel": "bin_count",
                 "scatter_kernel": "bin_scatter", "merge_kernel": "bin_merge",
                 "plan_kernel": "bin_plan", "zero_kernel": "zero"}
 
@@ -98,6 +107,7 @@ def _resource_remarks(text: str) -> dict:
 # fp32, D = 32, plain-method instantiations (Itanium mangling of the template arguments)
 _INSTANCE = {
     "fwd_kernel": re.compile(r"\d+fwd_kernelIfLi32ELb0ELi(\d+)E"),
+    "fwd_win_kernel": re.compile(r"\d+fwd_win_kernelIfLi32ELb0ELi(\d+)E"),
     "tile_kernel": re.compile(r"\d+tile_kernelIfLi32EE"),
     "count_kernel": re.compile(r"\d+count_kernelIfEE"),
     "scatter_kernel": re.compile(r"\d+scatter_kernelIfLb0EEE"),
@@ -111,7 +121,7 @@ def _relevant(remarks: dict, kernels: list[str]) -> dict:
         for base in kernels:
             m = _INSTANCE[base].search(mangled)
             if m:
-                res[base + (f"<pipe {m.group(1)}>" if base == "fwd_kernel" else "")] = r
+                res[base + (f"<pipe {m.group(1)}>" if base.startswith("fwd") else "")] = r
     return res
 
 
@@ -139,7 +149,8 @@ def build_points(groups: list[str]) -> None:
 
 # --------------------------------------------------------------------- one
 
-def run_one(lib: str, workload: int, steps: int, ref_dir: str, write_ref: bool) -> dict:
+def run_one(lib: str, workload: int, steps: int, ref_dir: str, write_ref: bool,
+            schedule: str = "auto") -> dict:
     """Time one library variant on one GPU (child process) and compare its outputs."""
     import numpy as np
     import torch
@@ -149,6 +160,7 @@ def run_one(lib: str, workload: int, steps: int, ref_dir: str, write_ref: bool) 
     import scale_deformable_attention_msda_amd as msda
 
     msda.load_library(lib)
+    msda.msda_test_set_forward_schedule(schedule)
     wl = workloads.WORKLOADS[workload]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -221,18 +233,17 @@ def _counter_csv_rows(d: str) -> list[dict]:
 
 def _kernel_base(name: str) -> str:
     """'void msda::(anonymous namespace)::tile_kernel<float, 32>(msda::BinArgs)' -> 'tile_kernel'."""
-    base = name.split("<")[0]
-    if "(" in base.split("::")[-1]:  # a kernel without template arguments
-        base = base[:base.rindex("(")]
+    base = name.replace("(anonymous namespace)", "").split("<")[0].split("(")[0]
     return base.split("::")[-1].strip()
 
 
-def _profiled(lib: str, counters: list[str], out_dir: str, ref_dir: str, copy: bool = False) -> dict:
+def _profiled(lib: str, counters: list[str], out_dir: str, ref_dir: str, copy: bool = False,
+              schedule: str = "auto") -> dict:
     """Mean counter values per kernel (library profile names) over one profiled child run."""
     d = tempfile.mkdtemp(prefix="sweep_pmc_", dir=out_dir)
     child = ([sys.executable, os.path.join(ROOT, "bench.py"), "--calibrate-copy"] if copy else
              [sys.executable, "-m", "scale_deformable_attention_msda_amd.sweep", "one", "--lib", lib,
-              "--steps", "3", "--ref-dir", ref_dir])
+              "--steps", "3", "--ref-dir", ref_dir, "--schedule", schedule])
     cmd = ["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "run", "--",
            *child]
     r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=300)
@@ -260,9 +271,10 @@ def run_points(groups: list[str], counters: bool, out_md: str, steps: int) -> No
     ref_dir = tempfile.mkdtemp(prefix="sweep_ref_", dir=out_dir)
     default_lib = os.path.join(PKG, "libmsda.so")
 
-    def child(lib, write_ref=False):
+    def child(lib, write_ref=False, schedule="auto"):
         cmd = [sys.executable, "-m", "scale_deformable_attention_msda_amd.sweep", "one", "--lib", lib,
-               "--steps", str(steps), "--ref-dir", ref_dir] + (["--write-ref"] if write_ref else [])
+               "--steps", str(steps), "--ref-dir", ref_dir, "--schedule", schedule] + \
+              (["--write-ref"] if write_ref else [])
         r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=300)
         if r.returncode != 0:
             return {"error": r.stderr.strip().splitlines()[-1][:300] if r.stderr.strip() else
@@ -292,13 +304,15 @@ def run_points(groups: list[str], counters: bool, out_md: str, steps: int) -> No
             meta = json.load(open(meta_path))
             lib = os.path.join(d, "libmsda.so")
             rec = dict(meta)
+            sched = GROUP_SCHEDULE.get(g, "auto")
+            rec["schedule"] = sched
             if meta["status"] == "built":
-                rec.update(child(lib))
+                rec.update(child(lib, schedule=sched))
                 if counters and "error" not in rec:
                     try:
-                        c1 = _profiled(lib, ["FETCH_SIZE"], out_dir, ref_dir)
+                        c1 = _profiled(lib, ["FETCH_SIZE"], out_dir, ref_dir, schedule=sched)
                         c2 = _profiled(lib, ["WRITE_SIZE", "TCC_HIT_sum", "TCC_MISS_sum"], out_dir,
-                                       ref_dir)
+                                       ref_dir, schedule=sched)
                         traffic = {}
                         for k in set(c1) | set(c2):
                             fkib = c1.get(k, {}).get("FETCH_SIZE")
@@ -355,7 +369,8 @@ def write_summary(path: str, ref: dict, results: list[dict], scale, steps: int, 
         par = r.get("parity", {})
         bad = sum(v["outside"] for v in par.values() if isinstance(v, dict))
         par_s = ("ok" if par and bad == 0 else f"{bad} outside") if par else r.get("error", "-")
-        lines.append(f"| {r['group']} | {r['name']} | {' '.join(r['flags'])} | {r['status']} | "
+        lines.append(f"| {r['group']} | {r['name']} ({r.get('schedule', 'auto')}) | "
+                     f"{' '.join(r['flags'])} | {r['status']} | "
                      f"{res} | {us.get('fwd', '-')} | {us.get('bin_tile', '-')} | "
                      f"{us.get('bin_count', '-')} | {us.get('bin_scatter', '-')} | "
                      f"{us.get('bin_merge', '-')} | {us.get('step', '-')} | {meas} | {par_s} |")
@@ -380,13 +395,15 @@ def main(argv=None) -> int:
     o.add_argument("--steps", type=int, default=20)
     o.add_argument("--ref-dir", required=True)
     o.add_argument("--write-ref", action="store_true")
+    o.add_argument("--schedule", default="auto", choices=["auto", "direct", "window"])
     a = ap.parse_args(argv)
     if a.cmd == "build":
         build_points(a.group or sorted(GROUPS))
     elif a.cmd == "run":
         run_points(a.group or sorted(GROUPS), a.counters, a.out, a.steps)
     else:
-        print(json.dumps(run_one(a.lib, a.workload, a.steps, a.ref_dir, a.write_ref)), flush=True)
+        print(json.dumps(run_one(a.lib, a.workload, a.steps, a.ref_dir, a.write_ref, a.schedule)),
+              flush=True)
     return 0
 
 
