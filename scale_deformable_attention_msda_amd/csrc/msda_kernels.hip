@@ -1147,7 +1147,11 @@ constexpr size_t kWinGeoMax = 75 * 1024;  // the waves' geometry tables together
 #ifndef MSDA_WIN_BLOCKS_PER_CU
 #define MSDA_WIN_BLOCKS_PER_CU 2
 #endif
+#ifndef MSDA_WIN_LDS_BLOCKS
+#define MSDA_WIN_LDS_BLOCKS 1
+#endif
 constexpr int kWinPipe = MSDA_WIN_PIPE;              // samples in flight per lane
+constexpr int kWinLdsBlocks = MSDA_WIN_LDS_BLOCKS;   // blocks sharing one CU's LDS
 constexpr int kWinBlocksPerCu = MSDA_WIN_BLOCKS_PER_CU;  // blocks per CU over the launch
 constexpr size_t kWinStaticReserve = 1024;  // the kernel's static LDS (levels, plan)
 
@@ -1169,17 +1173,19 @@ bool plan_win_launch(const LaunchArgs &a, bool softmax, WinLaunch &w) {
   const int LK = (int)(a.L * a.K);
   const bool staged = softmax && !(LK <= 64 && (LK & (LK - 1)) == 0);
   const size_t per_wave = win_wave_bytes(LK, RL::G, staged);
-  const int nwaves = (int)std::min<size_t>(kWinThreads / 64, kWinGeoMax / per_wave);
-  // the block is the CU's only one (its LDS): with fewer than 16 waves it hides
-  // too little latency (measured slower than the direct gather: bf16 rows with
-  // L*K = 12 or 32 get 11 and 4 waves), unless a test forces the schedule
-  if (nwaves < (g_fwd_schedule == 2 ? 4 : kWinThreads / 64)) return false;
+  const int nwaves = (int)std::min<size_t>(kWinThreads / 64 / kWinLdsBlocks,
+                                           kWinGeoMax / kWinLdsBlocks / per_wave);
+  // the blocks of a CU share its LDS: with fewer than 16 waves on the CU they
+  // hide too little latency (measured slower than the direct gather: bf16 rows
+  // with L*K = 12 or 32 get 11 and 4 waves), unless a test forces the schedule
+  if (nwaves * kWinLdsBlocks < (g_fwd_schedule == 2 ? 4 : kWinThreads / 64)) return false;
   int dev = 0, max_lds = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return false;
-  const size_t total = (size_t)max_lds > kWinStaticReserve ? (size_t)max_lds - kWinStaticReserve : 0;
+  const size_t block_lds = (size_t)max_lds / kWinLdsBlocks;
+  const size_t total = block_lds > kWinStaticReserve ? block_lds - kWinStaticReserve : 0;
   const size_t geo = per_wave * nwaves;
   // the window area must hold the zero row and the cell-row histogram of a window level
   if (total < geo + 32 * 1024) return false;

@@ -9,6 +9,9 @@ measures every variant on one GPU:
 
   fwd_pipe     MSDA_FWD_PIPE        corner-row loads a forward lane keeps in flight (x4)
   fwd_block    MSDA_FWD_BLOCK       lanes per forward block (head-queries per block)
+  win_pipe     MSDA_WIN_PIPE        samples in flight per lane, LDS-window forward
+  win_blocks   MSDA_WIN_BLOCKS_PER_CU  LDS-window blocks per CU over the launch
+  win_lds      MSDA_WIN_LDS_BLOCKS  LDS-window blocks sharing one CU's LDS
   bin_chunk    MSDA_BIN_CHUNK       samples per tile-kernel chunk (binned backward)
   bin_tile     MSDA_BIN_TILE        destination tile edge in pixels (binned backward)
   count_block  MSDA_COUNT_SAMPLES   samples per count / scatter block
@@ -50,6 +53,7 @@ GROUPS = {
     "fwd_block": [("block128", ["-DMSDA_FWD_BLOCK=128"]), ("block256", ["-DMSDA_FWD_BLOCK=256"]),
                   ("block512", ["-DMSDA_FWD_BLOCK=512"]), ("block1024", ["-DMSDA_FWD_BLOCK=1024"])],
     "win_pipe": [("winpipe2", ["-DMSDA_WIN_PIPE=2"]), ("winpipe4", ["-DMSDA_WIN_PIPE=4"])],
+    "win_lds": [("winlds1", ["-DMSDA_WIN_LDS_BLOCKS=1"]), ("winlds2", ["-DMSDA_WIN_LDS_BLOCKS=2"])],
     "win_blocks": [("winbpc1", ["-DMSDA_WIN_BLOCKS_PER_CU=1"]),
                    ("winbpc2", ["-DMSDA_WIN_BLOCKS_PER_CU=2"]),
                    ("winbpc4", ["-DMSDA_WIN_BLOCKS_PER_CU=4"])],
@@ -64,7 +68,7 @@ GROUPS = {
 # the kernels whose resources each group changes (names as the compiler reports them)
 GROUP_KERNELS = {
     "fwd_pipe": ["fwd_kernel"], "fwd_block": ["fwd_kernel"], "win_pipe": ["fwd_win_kernel"],
-    "win_blocks": ["fwd_win_kernel"], "bin_chunk": ["tile_kernel"],
+    "win_blocks": ["fwd_win_kernel"], "win_lds": ["fwd_win_kernel"], "bin_chunk": ["tile_kernel"],
     "bin_tile": ["tile_kernel"], "count_block": ["count_kernel", "scatter_kernel"],
 }
 # forward schedule of the timed step per group: the direct-gather groups force
