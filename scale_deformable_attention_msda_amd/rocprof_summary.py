@@ -10,7 +10,8 @@
       bench.py reads the 'traffic' and 'l2hit' lines while the kernel sources hash to the
       digest written beside them.
   python -m scale_deformable_attention_msda_amd.rocprof_summary counters DIR [DIR ...] --command C
-      per-kernel means of every counter in the directories (one pass each)
+      per-kernel means of every counter in the directories (one pass each), with derived
+      ratios (time waiting, VALU issue, L1 / L2 hit rates, L2 latency, LDS bank conflicts)
 """
 from __future__ import annotations
 
@@ -107,19 +108,56 @@ def traffic(fetch: str, write: str, copy_fetch: str, copy_write: str, workload: 
     return "\n".join(lines) + "\n"
 
 
-def counters(dirs: list[str], command: str) -> str:
+def _ratio(cs: dict, num: str, den: str, one_minus: bool = False):
+    if num not in cs or not cs.get(den):
+        return None
+    r = cs[num] / cs[den]
+    return 1.0 - r if one_minus else r
+
+
+def counters(dirs: list[str], command: str, title: str = "") -> str:
     merged = collections.defaultdict(dict)
     for d in dirs:
         for k, cs in counter_means(d).items():
             merged[k].update(cs)
+    names = sorted((k for k in merged if kernel_base(k) in PROFILE_NAME), key=kernel_base)
     lines = ["# Hardware counters per launch (means over each run's dispatches)", "",
+             *([title, ""] if title else []),
              "Commands (GPU host, `cd /tmp && export TMPDIR=/tmp`; one pass per counter group):", "",
-             f"    {command}", ""]
-    for k in sorted(merged, key=lambda n: kernel_base(n)):
-        if kernel_base(k) not in PROFILE_NAME:
-            continue
+             f"    {command}", "",
+             "SQ_* counters are summed over the device, TCC_* over the L2 channels of the 8 XCDs, "
+             "TCP_* over the vector L1s.", "",
+             "Columns: waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES; issuing VALU = SQ_ACTIVE_INST_VALU / "
+             "SQ_WAVE_CYCLES; L1 hit = 1 - TCP_TCC_READ_REQ / TCP_TOTAL_CACHE_ACCESSES; L2 hit = "
+             "TCC_HIT / (TCC_HIT + TCC_MISS); L2 latency = TCP_TCC_READ_REQ_LATENCY / "
+             "TCP_TCC_READ_REQ (cycles, seen from the L1); LDS conflict = SQ_LDS_BANK_CONFLICT / "
+             "SQ_ACTIVE_INST_LDS.", "",
+             "| kernel | waves | VALU insts | LDS insts | VMEM rd / wr insts | waiting | issuing VALU "
+             "| L1 hit | L2 hit | L2 latency | LDS conflict |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+
+    def f(x, fmt):
+        return "-" if x is None else format(x, fmt)
+
+    for k in names:
         cs = merged[k]
-        lines.append(f"- {pretty(k)}: " + ", ".join(f"{c} {v:.4g}" for c, v in sorted(cs.items())))
+        l2 = None
+        if "TCC_HIT_sum" in cs and cs.get("TCC_HIT_sum", 0) + cs.get("TCC_MISS_sum", 0) > 0:
+            l2 = cs["TCC_HIT_sum"] / (cs["TCC_HIT_sum"] + cs["TCC_MISS_sum"])
+        m = lambda c: None if c not in cs else cs[c] / 1e6
+        lines.append(
+            f"| {pretty(k)} | {f(cs.get('SQ_WAVES'), ',.0f')} | {f(m('SQ_INSTS_VALU'), '.2f')} M | "
+            f"{f(m('SQ_INSTS_LDS'), '.2f')} M | {f(m('SQ_INSTS_VMEM_RD'), '.2f')} / "
+            f"{f(m('SQ_INSTS_VMEM_WR'), '.2f')} M | "
+            f"{f(_ratio(cs, 'SQ_WAIT_ANY', 'SQ_WAVE_CYCLES'), '.2f')} | "
+            f"{f(_ratio(cs, 'SQ_ACTIVE_INST_VALU', 'SQ_WAVE_CYCLES'), '.2f')} | "
+            f"{f(_ratio(cs, 'TCP_TCC_READ_REQ_sum', 'TCP_TOTAL_CACHE_ACCESSES_sum', True), '.2f')} | "
+            f"{f(l2, '.2f')} | "
+            f"{f(_ratio(cs, 'TCP_TCC_READ_REQ_LATENCY_sum', 'TCP_TCC_READ_REQ_sum'), '.0f')} | "
+            f"{f(_ratio(cs, 'SQ_LDS_BANK_CONFLICT', 'SQ_ACTIVE_INST_LDS'), '.2f')} |")
+    lines += ["", "Raw means per launch:", ""]
+    for k in names:
+        lines.append(f"- {pretty(k)}: " + ", ".join(f"{c} {v:.4g}" for c, v in sorted(merged[k].items())))
     return "\n".join(lines) + "\n"
 
 
@@ -136,6 +174,7 @@ def main(argv=None) -> int:
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--command", required=True)
+    c.add_argument("--title", default="")
     for p in (t, f, c):
         p.add_argument("--out", required=True)
     a = ap.parse_args(argv)
@@ -144,7 +183,7 @@ def main(argv=None) -> int:
     elif a.cmd == "traffic":
         text = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.workload, a.scatter, a.command)
     else:
-        text = counters(a.dirs, a.command)
+        text = counters(a.dirs, a.command, a.title)
     open(a.out, "w").write(text)
     print(f"wrote {a.out}")
     return 0
