@@ -666,6 +666,36 @@ __device__ inline void load_vec(const void *base, int64_t e, float (&o)[VEC]) {
   }
 }
 
+// VEC elements of T at byte offset `off` of a buffer, as fp32.
+template <typename T, int VEC>
+__device__ inline void load_vec_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&o)[VEC]) {
+  if constexpr (sizeof(T) == 4 && VEC % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) {
+      uint32_t w[4];
+      buffer_load<4>(r, off + 16 * k, w);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[4 * k + i] = __uint_as_float(w[i]);
+    }
+  } else if constexpr (sizeof(T) == 2 && VEC == 8) {
+    uint32_t w[4];
+    buffer_load<4>(r, off, w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = Half<T>::lo(w[k]);
+      o[2 * k + 1] = Half<T>::hi(w[k]);
+    }
+  } else if constexpr (sizeof(T) * VEC == 8) {
+    uint32_t w[2];
+    buffer_load<2>(r, off, w);
+    unpack<T, 2>(w, o);
+  } else {
+    uint32_t w[1];
+    buffer_load<1>(r, off, w);
+    unpack<T, 1>(w, o);
+  }
+}
+
 // ceil(n / d) for n <= 2^12 and 1 <= d <= 2^12, rd ~ 1/d within a few ulp: the
 // float quotient is off by less than 2^-10 from n / d, so at most the floor of
 // an exact integer quotient comes out one low, and one integer check fixes it.
@@ -750,7 +780,22 @@ __device__ inline void plan_items(const uint32_t *cnt, const uint32_t *cstart, u
   }
 }
 
-template <typename T, int D>
+// n / d for n < 2^31: the magic product is below n, so its sum with n stays
+// below 2^32 and the division needs no 64-bit step.
+__device__ inline uint32_t fdiv31(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+template <int CTRL>
+__device__ inline uint32_t dpp_move_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// FAST: every sample id is below 2^31 and the launch's grad_out image below
+// 2^31 bytes (the launch checks both), so ids divide in 32 bits and grad_out
+// rows load through a buffer descriptor with 32-bit offsets: fewer
+// instructions per sample in the item loop than 64-bit addresses.
+template <typename T, int D, bool FAST>
 __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   using TL = TileLayout<D>;
   using SM = TileSmem<D>;
@@ -761,6 +806,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   constexpr int kPer = kChunk / 256;                 // phase-A samples per thread
   constexpr int kRowIters = (NROWS + 1 + NG - 1) / NG;
   constexpr uint32_t kDropped = 0xffffffffu;
+  constexpr int kRowShift = __builtin_ctz(D * (int)sizeof(T));  // bytes of a grad_out row, log2
   extern __shared__ __align__(16) char smem[];
   float *vt = reinterpret_cast<float *>(smem + SM::vt);
   float *stage = reinterpret_cast<float *>(smem + SM::stage);
@@ -776,6 +822,10 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   LevelTab *lt = reinterpret_cast<LevelTab *>(smem + SM::lvl);
 
   const BinPlan &p = a.p;
+  const __amdgpu_buffer_rsrc_t gsrc =
+      make_rsrc(a.grad_out, FAST ? (uint32_t)((uint64_t)p.B * (uint64_t)p.Q * (uint64_t)p.M *
+                                               (uint64_t)(D * (int)sizeof(T)))
+                                  : 0u);
   // the chunk count and this block's first chunk entry do not depend on each
   // other: issue the loads together
   const uint32_t nchunks = *a.w.nchunks;
@@ -859,10 +909,10 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       const uint32_t id = rc[r].x;
       const float su = __uint_as_float(rc[r].y), sv = __uint_as_float(rc[r].z);
       if (id < p.total) {
-        const uint32_t hq = fdiv(id, p.div_lk);
+        const uint32_t hq = FAST ? fdiv31(id, p.div_lk) : fdiv(id, p.div_lk);
         const uint32_t j = id - hq * (uint32_t)(p.L * p.K);
         Cell c;
-        if ((int)fdiv(j, p.div_k) == l && cell_of(su, sv, H, W, c)) {
+        if ((int)fdiv31(j, p.div_k) == l && cell_of(su, sv, H, W, c)) {
           const int cy = c.y0 - py0 + 1, cx = c.x0 - px0 + 1;
           if (cy >= 0 && cy < kEdge && cx >= 0 && cx < kEdge) {
             const uint32_t cell = (uint32_t)(cy * kEdge + cx);
@@ -913,7 +963,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           V[q][i] = (double)src[i];
-          acc[q][i] = 0.0f;
+          if constexpr (G != 4) acc[q][i] = 0.0f;
         }
       }
       if constexpr (G == 4) {
@@ -927,20 +977,25 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
         uint32_t ids[1][4];    // sample ids of the four slots
         float g[1][4][VEC];    // grad_out rows (this lane's channels) of the four slots
         auto fetch = [&](uint32_t k0, int buf) {
+          // slot t of lane j is lane (j ^ t)'s own sample: its id comes by a lane move
+          own[buf] = reinterpret_cast<const uint4 *>(sorted)[s0 + min(k0 + (uint32_t)lane, n - 1)];
+          ids[buf][0] = own[buf].x;
+          ids[buf][1] = dpp_move_u32<kDppQuadXor1>(own[buf].x);
+          ids[buf][2] = dpp_move_u32<kDppQuadXor2>(own[buf].x);
+          ids[buf][3] = dpp_move_u32<kDppQuadXor3>(own[buf].x);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const uint32_t pos = s0 + min(k0 + (uint32_t)(lane ^ t), n - 1);
-            if (t == 0) {
-              own[buf] = reinterpret_cast<const uint4 *>(sorted)[pos];
-              ids[buf][0] = own[buf].x;
+            if constexpr (FAST) {
+              const uint32_t off = (fdiv31(ids[buf][t], p.div_lk) << kRowShift) +
+                                   (uint32_t)(lane * VEC * (int)sizeof(T));
+              load_vec_buf<T, VEC>(gsrc, off, g[buf][t]);
             } else {
-              ids[buf][t] = sorted[pos].id;
+              load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(ids[buf][t], p.div_lk) * D + lane * VEC,
+                               g[buf][t]);
             }
-            load_vec<T, VEC>(a.grad_out, (int64_t)fdiv(ids[buf][t], p.div_lk) * D + lane * VEC,
-                             g[buf][t]);
           }
         };
-        auto consume = [&](uint32_t k0, int buf) {
+        auto consume = [&](uint32_t k0, int buf, auto first) {
           double P[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -978,15 +1033,25 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
           for (int q = 0; q < 4; ++q) {
             const float at[4] = {aw[q], dpp_move<kDppQuadXor1>(aw[q]),
                                  dpp_move<kDppQuadXor2>(aw[q]), dpp_move<kDppQuadXor3>(aw[q])};
+            if constexpr (decltype(first)::value) {
+              // the item's first batch starts its sums
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+              for (int i = 0; i < VEC; ++i) acc[q][i] = at[0] * g[buf][0][i];
+            } else {
+#pragma unroll
+              for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(at[0], g[buf][0][i], acc[q][i]);
+            }
+#pragma unroll
+            for (int t = 1; t < 4; ++t)
 #pragma unroll
               for (int i = 0; i < VEC; ++i) acc[q][i] = fmaf(at[t], g[buf][t][i], acc[q][i]);
           }
         };
-        for (uint32_t k0 = 0; k0 < n; k0 += kU) {
+        fetch(0, 0);
+        consume(0, 0, std::true_type{});
+        for (uint32_t k0 = kU; k0 < n; k0 += kU) {
           fetch(k0, 0);
-          consume(k0, 0);
+          consume(k0, 0, std::false_type{});
         }
       } else {
         // batches of kU samples; the records and grad_out rows of the next batch
@@ -1237,7 +1302,10 @@ template <typename T, int D>
 hipError_t launch_tile_and_merge(const BinArgs &a, hipStream_t s) {
   const size_t lds = tile_lds_bytes<T, D>();
   // persistent tile blocks: as many as fit on the device at once, at most one per chunk
-  auto kernel = tile_kernel<T, D>;
+  const uint64_t gout_bytes =
+      (uint64_t)a.p.B * (uint64_t)a.p.Q * (uint64_t)a.p.M * (uint64_t)D * sizeof(T);
+  const bool fast = a.p.total < (1u << 31) && gout_bytes < (uint64_t(1) << 31);
+  auto kernel = fast ? tile_kernel<T, D, true> : tile_kernel<T, D, false>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
