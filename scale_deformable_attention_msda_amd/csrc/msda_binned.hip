@@ -1127,13 +1127,28 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     // ---- per-sample results back in record order: the scatter pass wrote a
     // bin's records in sample order, so neighbouring lanes store neighbouring
     // ids and the stores of a sample's points merge
-    for (uint32_t i = tid; i < count; i += blockDim.x) {
-      const uint32_t t = tag[i];
-      if (t == kDropped) continue;
-      const uint4 r = reinterpret_cast<const uint4 *>(sorted)[cstart[t & 0xffu] + (t >> 8)];
-      store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + r.x, __uint_as_float(r.y));
-      store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)r.x, __uint_as_float(r.z),
-                    __uint_as_float(r.w));
+    // (the thread's kPer records go through each step together, so their LDS
+    // reads are in flight at once)
+    {
+      uint32_t tg[kPer], pos[kPer];
+      uint4 rr[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const uint32_t i = tid + r * 256;
+        tg[r] = i < count ? tag[i] : kDropped;
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r)
+        pos[r] = tg[r] != kDropped ? cstart[tg[r] & 0xffu] + (tg[r] >> 8) : 0u;
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) rr[r] = reinterpret_cast<const uint4 *>(sorted)[pos[r]];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        if (tg[r] == kDropped) continue;
+        store_scalar<T>(reinterpret_cast<T *>(a.grad_attn) + rr[r].x, __uint_as_float(rr[r].y));
+        store_pair<T>(reinterpret_cast<T *>(a.grad_loc) + 2 * (int64_t)rr[r].x,
+                      __uint_as_float(rr[r].z), __uint_as_float(rr[r].w));
+      }
     }
 
     // ---- every pixel of the tile and its rim sums the items of the cells it is
@@ -1143,17 +1158,33 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       const int iy = r / kEdge, ix = r - (r / kEdge) * kEdge;
       const int py = py0 + iy, px = px0 + ix;
       if (py >= H || px >= W) continue;
-      float v[VEC];
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] = 0.0f;
       // pixel (iy, ix) is corner 00 of cell (iy+1, ix+1), 01 of (iy+1, ix),
-      // 10 of (iy, ix+1) and 11 of (iy, ix)
+      // 10 of (iy, ix+1) and 11 of (iy, ix).  The first piece of each of the
+      // four cells (the zero row for a cell with none) is read with all loads
+      // in flight together; the further pieces of split cells follow.
+      uint32_t ib[4], ie[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cy = iy + 1 - (q >> 1), cx = ix + 1 - (q & 1);
-        if (cy >= kEdge || cx >= kEdge) continue;
-        const int c = cy * kEdge + cx;
-        for (uint32_t it = istart[c]; it < istart[c + 1]; ++it) {
+        const bool in = cy < kEdge && cx < kEdge;
+        const int c = in ? cy * kEdge + cx : 0;
+        ib[q] = in ? istart[c] : 0u;
+        ie[q] = in ? istart[c + 1] : 0u;
+      }
+      float f[4][VEC];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float *src = ib[q] < ie[q] ? stage + (ib[q] * 4 + q) * RS + lane * VEC
+                                         : vt + kZeroRow * RS + lane * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) f[q][i] = src[i];
+      }
+      float v[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] = (f[0][i] + f[1][i]) + (f[2][i] + f[3][i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        for (uint32_t it = ib[q] + 1; it < ie[q]; ++it) {
           const float *src = stage + (it * 4 + q) * RS + lane * VEC;
 #pragma unroll
           for (int i = 0; i < VEC; ++i) v[i] += src[i];

@@ -112,7 +112,7 @@ def _resource_remarks(text: str) -> dict:
 _INSTANCE = {
     "fwd_kernel": re.compile(r"\d+fwd_kernelIfLi32ELb0ELi(\d+)E"),
     "fwd_win_kernel": re.compile(r"\d+fwd_win_kernelIfLi32ELb0ELi(\d+)E"),
-    "tile_kernel": re.compile(r"\d+tile_kernelIfLi32EE"),
+    "tile_kernel": re.compile(r"\d+tile_kernelIfLi32ELb1EE"),
     "count_kernel": re.compile(r"\d+count_kernelIfEE"),
     "scatter_kernel": re.compile(r"\d+scatter_kernelIfLb0EEE"),
 }
