@@ -566,9 +566,17 @@ struct TileSmem {
   static constexpr size_t sched = items + (size_t)kMaxItems * 4;
   static constexpr size_t next = sched + (size_t)kMaxItems * 4;
   static constexpr size_t lvl = next + 16;
-  static constexpr size_t bytes = lvl + (size_t)kMaxLevels * sizeof(LevelTab);
+  // the planner's batch-count histogram: in the stage area past the unsorted
+  // records when it fits there (that part is free until the item loop), else
+  // after the level table
+  static constexpr size_t hist_bytes = 4 * ((size_t)kChunk / kU + 1);
+  static constexpr bool hist_in_stage = item_bytes >= rec_bytes + hist_bytes;
+  static constexpr size_t tail = (lvl + (size_t)kMaxLevels * sizeof(LevelTab) + 15) / 16 * 16;
+  static constexpr size_t hist = hist_in_stage ? stage + rec_bytes : tail;
+  static constexpr size_t bytes = hist_in_stage ? tail : tail + hist_bytes;
 };
 static_assert(kChunk <= 1024, "item packing keeps 10-bit first / length fields");
+static_assert(TileSmem<32>::hist_in_stage, "no LDS growth for the D = 32 rows");
 
 // Level, batch, head and tile of a bin.  The search runs over compile-time
 // level indices only, so the plan arrays stay in scalar registers instead of
@@ -717,12 +725,36 @@ __device__ inline void cell_starts(const uint32_t *cnt, uint32_t *cstart) {
   if (c1 <= (uint32_t)kCells) cstart[c1] = inc1 - n1;
 }
 
-// Wave 0 of the tile kernel, step 2: the item table and the schedule.
+// Inclusive prefix maximum over the 64 lanes (values >= 0).
+__device__ inline uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, dpp_u32<0x111>(x));  // row_shr:1 (lanes past a row's start read 0)
+  x = max(x, dpp_u32<0x112>(x));  // row_shr:2
+  x = max(x, dpp_u32<0x114>(x));  // row_shr:4
+  x = max(x, dpp_u32<0x118>(x));  // row_shr:8
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
+  const uint32_t row = (threadIdx.x & 63) >> 4;
+  return max(x, max(row >= 1 ? t0 : 0u, max(row >= 2 ? t1 : 0u, row >= 3 ? t2 : 0u)));
+}
+
+// Wave 0 of the tile kernel, step 2: the item table and the schedule.  Past
+// the choice of P every step is a fixed sequence of wave-wide operations (no
+// loop over the pieces of a cell or over the batch counts present), since this
+// runs on one wave while the block waits for it.
+//   - items: lane j holds items j and j + 64.  The first item of every
+//     non-empty cell is marked with the cell (+1) in `sched`, and a prefix
+//     maximum over the items gives each item its cell; the piece index follows
+//     from the cell's first item.
+//   - schedule: items by decreasing number of batches (ceil(length / kU)), a
+//     counting sort with the histogram in `scratch` (at least kChunk / kU + 1
+//     words); the order inside one batch count is free, since the schedule
+//     only decides which lane group runs an item, never a result.
 __device__ inline void plan_items(const uint32_t *cnt, const uint32_t *cstart, uint32_t *istart,
-                                  uint32_t *items, uint32_t *sched) {
-  const uint32_t c0 = threadIdx.x, c1 = threadIdx.x + 64;
+                                  uint32_t *items, uint32_t *sched, uint32_t *scratch) {
+  const uint32_t lane = threadIdx.x;
+  const uint32_t c0 = lane, c1 = lane + 64;
   const uint32_t n0 = cnt[c0], n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
-  const uint32_t cs0 = cstart[c0], cs1 = c1 < (uint32_t)kCells ? cstart[c1] : 0u;
   const uint32_t total = cstart[kCells];
   // smallest P = kU * m with at most kMaxItems pieces: linear steps up from
   // the lower bound total / kMaxItems, then a binary search if that is slow
@@ -753,31 +785,58 @@ __device__ inline void plan_items(const uint32_t *cnt, const uint32_t *cstart, u
   const uint32_t itotal0 = __builtin_amdgcn_readlane(iinc0, 63);
   const uint32_t iinc1 = itotal0 + wave_incl_scan(k1);
   const uint32_t is0 = iinc0 - k0, is1 = iinc1 - k1;
+  const uint32_t nitems = __builtin_amdgcn_readlane(iinc1, 63);
   istart[c0] = is0;
   if (c1 <= (uint32_t)kCells) istart[c1] = is1;  // istart[kCells] = number of items
-  for (uint32_t j = 0; j < k0; ++j)
-    items[is0 + j] = (cs0 + j * P) | ((min(P, n0 - j * P) - 1) << 10) | (c0 << 20);
-  for (uint32_t j = 0; j < k1; ++j)
-    items[is1 + j] = (cs1 + j * P) | ((min(P, n1 - j * P) - 1) << 10) | (c1 << 20);
-  // schedule: items by decreasing batch count (full pieces have m batches,
-  // the last piece of a cell ceil(rest / kU)); order within a count is free
-  const uint32_t lb0 = k0 ? (n0 - (k0 - 1) * P + kU - 1) / kU : 0u;
-  const uint32_t lb1 = k1 ? (n1 - (k1 - 1) * P + kU - 1) / kU : 0u;
-  uint32_t pos = 0, b = m;
-  while (b > 0) {
-    const uint32_t full = b == m ? (k0 ? k0 - 1 : 0u) + (k1 ? k1 - 1 : 0u) : 0u;
-    const uint32_t c = full + (lb0 == b ? 1u : 0u) + (lb1 == b ? 1u : 0u);
-    const uint32_t inc = wave_incl_scan(c);
-    uint32_t w = pos + inc - c;
-    if (b == m) {
-      for (uint32_t j = 0; j + 1 < k0; ++j) sched[w++] = is0 + j;
-      for (uint32_t j = 0; j + 1 < k1; ++j) sched[w++] = is1 + j;
-    }
-    if (lb0 == b) sched[w++] = is0 + k0 - 1;
-    if (lb1 == b) sched[w++] = is1 + k1 - 1;
-    pos += __builtin_amdgcn_readlane(inc, 63);
-    b = wave_max(max(lb0 < b ? lb0 : 0u, lb1 < b ? lb1 : 0u));
+  // cell of every item: markers, then a prefix maximum (one wave: its LDS
+  // operations complete in program order)
+  const uint32_t i0 = lane, i1 = lane + 64;
+  sched[i0] = 0u;
+  if (i1 < (uint32_t)kMaxItems) sched[i1] = 0u;
+  if (k0) sched[is0] = c0 + 1;
+  if (k1) sched[is1] = c1 + 1;
+  const uint32_t mk0 = i0 < nitems ? sched[i0] : 0u;
+  const uint32_t mk1 = i1 < nitems ? sched[i1] : 0u;
+  const uint32_t own0 = wave_incl_max(mk0);
+  const uint32_t own1 = max(wave_incl_max(mk1), __builtin_amdgcn_readlane(own0, 63));
+  // (cell, piece) of items i0 and i1; batch counts b0, b1 (0: no such item)
+  uint32_t b[2] = {0u, 0u};
+  const uint32_t ii[2] = {i0, i1}, own[2] = {own0, own1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (ii[h] >= nitems) continue;
+    const uint32_t c = own[h] - 1;
+    const uint32_t j = ii[h] - istart[c];
+    const uint32_t first = cstart[c] + j * P, len = min(P, cnt[c] - j * P);
+    items[ii[h]] = first | ((len - 1) << 10) | (c << 20);
+    b[h] = (len + kU - 1) / kU;
   }
+  // schedule: counting sort by decreasing batch count, counts 1 .. m
+  for (uint32_t e = lane; e <= m; e += 64) scratch[e] = 0u;
+  uint32_t rank[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (b[h]) rank[h] = __hip_atomic_fetch_add(&scratch[b[h]], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_WORKGROUP);
+  // first position of batch count b = items with more batches: lane L sums the
+  // counts m - 4L .. m - 4L - 3, a wave scan puts the lanes in order
+  uint32_t h4[4], run = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int bb = (int)m - (int)(4 * lane) - t;
+    h4[t] = bb >= 1 ? scratch[bb] : 0u;
+    run += h4[t];
+  }
+  uint32_t pos = wave_incl_scan(run) - run;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int bb = (int)m - (int)(4 * lane) - t;
+    if (bb >= 1) scratch[bb] = pos;
+    pos += h4[t];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (b[h]) sched[scratch[b[h]] + rank[h]] = ii[h];
 }
 
 // n / d for n < 2^31: the magic product is below n, so its sum with n stays
@@ -930,7 +989,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     __syncthreads();
     // wave 0 plans the items while the other waves put the records in cell order
     if (tid < 64) {
-      plan_items(cnt, cstart, istart, items, sched);
+      plan_items(cnt, cstart, istart, items, sched, reinterpret_cast<uint32_t *>(smem + SM::hist));
     } else {
       for (uint32_t i = tid - 64; i < count; i += blockDim.x - 64) {
         const uint32_t t = tag[i];
