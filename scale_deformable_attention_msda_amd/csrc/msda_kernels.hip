@@ -243,8 +243,9 @@ __global__ __launch_bounds__(kMaxBlock) void fwd_kernel(LaunchArgs a, int hqb) {
 // After staging, every wavefront walks its own chunks of 64 / G head-queries
 // with fwd_kernel's two phases (geometry one lane per sample into the wave's
 // LDS table; gather one lane group per head-query), with no block barrier, so
-// the geometry of one wave overlaps the gathers of the others.  LDS-mode corners carry kLdsFlag in their offset; an invalid
-// corner of an LDS-mode sample reads the zero row at the window area's head.
+// the geometry of one wave overlaps the gathers of the others.  LDS-mode
+// corners carry kLdsFlag in their offset; an invalid corner of an LDS-mode
+// sample reads the zero row at the window area's head.
 constexpr uint32_t kLdsFlag = 0x40000000u;   // bit 30 set, bit 31 clear: an LDS offset
 constexpr int kWinThreads = 1024;
 constexpr int kWinMinRows = 4;               // a window level holds at least this many rows
@@ -1142,7 +1143,7 @@ hipError_t bwd_launch(const LaunchArgs &a, hipStream_t stream) {
 // too little LDS; the direct gather runs then.
 constexpr size_t kWinGeoMax = 75 * 1024;  // the waves' geometry tables together
 #ifndef MSDA_WIN_PIPE
-#define MSDA_WIN_PIPE 2
+#define MSDA_WIN_PIPE 4
 #endif
 #ifndef MSDA_WIN_BLOCKS_PER_CU
 #define MSDA_WIN_BLOCKS_PER_CU 2
