@@ -67,6 +67,15 @@ void msda_test_set_plan_wait_limit(uint32_t polls);
  */
 void msda_test_set_forward_schedule(int schedule);
 
+/*
+ * Test hook: with wide != 0, later binned backward calls on this thread run
+ * the tile pass with 64-bit sample-id division and grad_out addresses, the
+ * path it otherwise takes only when a launch's sample ids or grad_out image
+ * reach 2^31 (sizes too large to check against the oracle element by
+ * element).  0 restores the default.  Both paths compute the same sums.
+ */
+void msda_test_set_tile_wide_addressing(int wide);
+
 /* Memory-path microbenchmarks (msda_microbench_run). */
 typedef enum {
     /* streaming read of the buffer (16-byte loads); units = bytes read */

@@ -120,6 +120,8 @@ def load_library(path: str = LIB_PATH):
     lib.msda_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.msda_test_set_forward_schedule.argtypes = [ctypes.c_int]
     lib.msda_test_set_forward_schedule.restype = None
+    lib.msda_test_set_tile_wide_addressing.argtypes = [ctypes.c_int]
+    lib.msda_test_set_tile_wide_addressing.restype = None
     lib.msda_test_set_plan_wait_limit.argtypes = [ctypes.c_uint32]
     lib.msda_test_set_plan_wait_limit.restype = None
     lib.msda_microbench_run.argtypes = [ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_size_t,
@@ -172,6 +174,12 @@ def msda_test_set_forward_schedule(schedule: str) -> None:
     """Test hook: forward schedule of later calls on this thread ("auto", "direct" or
     "window")."""
     load_library().msda_test_set_forward_schedule(FORWARD_SCHEDULE[schedule])
+
+
+def msda_test_set_tile_wide_addressing(wide: bool) -> None:
+    """Test hook: later binned backward calls on this thread run the tile pass's 64-bit
+    addressing path (True) or pick it by size (False, the default)."""
+    load_library().msda_test_set_tile_wide_addressing(1 if wide else 0)
 
 
 def msda_test_set_plan_wait_limit(polls: int) -> None:

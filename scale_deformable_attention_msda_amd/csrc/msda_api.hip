@@ -575,6 +575,8 @@ void msda_test_set_plan_wait_limit(uint32_t polls) { msda::set_plan_spin_limit(p
 
 void msda_test_set_forward_schedule(int schedule) { msda::set_forward_schedule(schedule); }
 
+void msda_test_set_tile_wide_addressing(int wide) { msda::set_tile_wide_addressing(wide != 0); }
+
 const char *msda_status_string(msda_status status) {
   switch (status) {
     case MSDA_OK: return "MSDA_OK";

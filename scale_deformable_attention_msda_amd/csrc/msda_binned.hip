@@ -347,6 +347,8 @@ __device__ inline void block_scan3(uint32_t (&v)[3], uint32_t (&tot)[3], uint32_
 // later passes then write NaN gradients instead of using overlapping ranges.
 constexpr uint32_t kPlanSpinLimit = 1u << 24;
 thread_local uint32_t g_spin_limit = kPlanSpinLimit;
+// test hook: the tile pass takes its 64-bit addressing path at every size
+thread_local bool g_tile_wide = false;
 
 __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
   __shared__ uint32_t wsum[3 * (kPlanBlock / 64)];
@@ -1394,7 +1396,7 @@ hipError_t launch_tile_and_merge(const BinArgs &a, hipStream_t s) {
   // persistent tile blocks: as many as fit on the device at once, at most one per chunk
   const uint64_t gout_bytes =
       (uint64_t)a.p.B * (uint64_t)a.p.Q * (uint64_t)a.p.M * (uint64_t)D * sizeof(T);
-  const bool fast = a.p.total < (1u << 31) && gout_bytes < (uint64_t(1) << 31);
+  const bool fast = !g_tile_wide && a.p.total < (1u << 31) && gout_bytes < (uint64_t(1) << 31);
   auto kernel = fast ? tile_kernel<T, D, true> : tile_kernel<T, D, false>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1590,6 +1592,7 @@ size_t binned_workspace_bytes(const BinPlan &p) { return layout(p, nullptr, null
 size_t binned_error_offset(const BinPlan &p) { return error_offset_in_counts(p); }
 
 void set_plan_spin_limit(uint32_t polls) { g_spin_limit = polls; }
+void set_tile_wide_addressing(bool wide) { g_tile_wide = wide; }
 uint32_t plan_spin_limit() { return g_spin_limit; }
 
 BinScratch carve_bin_scratch(const BinPlan &p, void *workspace) {

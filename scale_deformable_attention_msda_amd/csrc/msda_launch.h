@@ -169,6 +169,10 @@ enum class Dtype { F32, BF16, F16 };
 // in the data type (BF16 or F16 data only)
 enum class Accum { F32, PACKED };
 
+// Tile pass of the binned backward on this thread (test hook): its 64-bit
+// addressing path at every size instead of only where ids or the grad_out
+// image reach 2^31.
+void set_tile_wide_addressing(bool wide);
 // Forward schedule for later launches on this thread (test hook): 0 automatic,
 // 1 always the direct gather, 2 the LDS-window gather whenever it fits.
 void set_forward_schedule(int schedule);
