@@ -118,12 +118,14 @@ def load_library(path: str = LIB_PATH):
     lib.msda_backward_noalloc.restype = ctypes.c_int
     lib.msda_noalloc_scratch_bytes.argtypes = []
     lib.msda_noalloc_scratch_bytes.restype = ctypes.c_size_t
-    lib.msda_test_set_forward_schedule.argtypes = [ctypes.c_int]
-    lib.msda_test_set_forward_schedule.restype = None
-    lib.msda_test_set_tile_wide_addressing.argtypes = [ctypes.c_int]
-    lib.msda_test_set_tile_wide_addressing.restype = None
-    lib.msda_test_set_plan_wait_limit.argtypes = [ctypes.c_uint32]
-    lib.msda_test_set_plan_wait_limit.restype = None
+    # test hooks: bound where the library has them (a tuning variant built from
+    # older sources may lack a newer hook; calling a missing one raises)
+    for name, arg in (("msda_test_set_forward_schedule", ctypes.c_int),
+                      ("msda_test_set_tile_wide_addressing", ctypes.c_int),
+                      ("msda_test_set_plan_wait_limit", ctypes.c_uint32)):
+        if hasattr(lib, name):
+            getattr(lib, name).argtypes = [arg]
+            getattr(lib, name).restype = None
     lib.msda_microbench_run.argtypes = [ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_size_t,
                                         ctypes.c_int, vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double)]
