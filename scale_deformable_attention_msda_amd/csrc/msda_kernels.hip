@@ -550,6 +550,41 @@ __global__ __launch_bounds__(kWinThreads) void fwd_win_kernel(LaunchArgs a, WinA
   const int grp = wlane / G, lane = wlane % G;
   const uint32_t lane_off = (uint32_t)(lane * RL::kLaneBytes);
 
+  // sample s of a chunk (s = entry * L*K + j): location and raw weight
+  auto load_sample = [&](const T *locp, const T *attp, int s, float &u, float &v, float &wraw) {
+    const int hl = (int)fdiv((uint32_t)s, wa.div_lk);
+    const int j = s - hl * LK;
+    const uint32_t gs = (uint32_t)hl * (uint32_t)(M * LK) + (uint32_t)j;
+    if constexpr (sizeof(T) == 4) {
+      const float2 uv = reinterpret_cast<const float2 *>(locp)[gs];
+      u = uv.x;
+      v = uv.y;
+    } else {
+      const uint32_t uv = reinterpret_cast<const uint32_t *>(locp)[gs];
+      u = Half<T>::lo(uv);
+      v = Half<T>::hi(uv);
+    }
+    wraw = to_float<T>(attp[gs]);
+  };
+  // the first kPf samples of each lane in the chunk at h0n, loaded ahead
+  // (where a chunk holds at most 8 head-queries: with more, two samples a
+  // lane cover too little of it to pay for the registers; the softmax forms
+  // hold more registers already)
+  constexpr int kPf = !SOFTMAX && HPW <= 8 ? 2 : 0;
+  float pf_u[kPf > 0 ? kPf : 1], pf_v[kPf > 0 ? kPf : 1], pf_w[kPf > 0 ? kPf : 1];
+  auto prefetch = [&](int h0n) {
+    const int nhn = min(HPW, nq - h0n);
+    const int64_t hqf = ((int64_t)b * a.Q + q0 + min(h0n, nq - 1)) * M + m;
+    const T *locp = reinterpret_cast<const T *>(a.loc) + 2 * hqf * LK;
+    const T *attp = reinterpret_cast<const T *>(a.attn) + hqf * LK;
+#pragma unroll
+    for (int k = 0; k < kPf; ++k) {
+      pf_u[k] = pf_v[k] = pf_w[k] = 0.0f;
+      if (wlane + 64 * k < nhn * LK) load_sample(locp, attp, wlane + 64 * k, pf_u[k], pf_v[k], pf_w[k]);
+    }
+  };
+  prefetch(wave * HPW);
+
   for (int h0 = wave * HPW; h0 < nq; h0 += wa.nwaves * HPW) {
     const int nh = min(HPW, nq - h0);
     const int64_t hq_first = ((int64_t)b * a.Q + q0 + h0) * M + m;  // hq of chunk entry 0
@@ -575,35 +610,35 @@ __global__ __launch_bounds__(kWinThreads) void fwd_win_kernel(LaunchArgs a, WinA
       }
       wave_lds_sync();
     }
-    // geometry, one lane per sample (32-bit sample offsets from the chunk's first)
+    // geometry, one lane per sample (32-bit sample offsets from the chunk's
+    // first); the first kPf samples of each lane come from the prefetch
     const T *locp = reinterpret_cast<const T *>(a.loc) + 2 * hq_first * LK;
     const T *attp = reinterpret_cast<const T *>(a.attn) + hq_first * LK;
-    for (int s = wlane; s < nh * LK; s += 64) {
+    auto geometry = [&](int s, float u, float v, float wraw) {
       const int hl = (int)fdiv((uint32_t)s, wa.div_lk);
       const int j = s - hl * LK;
-      const uint32_t gs = (uint32_t)hl * (uint32_t)(M * LK) + (uint32_t)j;
-      float u, v;
-      if constexpr (sizeof(T) == 4) {
-        const float2 uv = reinterpret_cast<const float2 *>(locp)[gs];
-        u = uv.x;
-        v = uv.y;
-      } else {
-        const uint32_t uv = reinterpret_cast<const uint32_t *>(locp)[gs];
-        u = Half<T>::lo(uv);
-        v = Half<T>::hi(uv);
-      }
       float w;
       if constexpr (SOFTMAX)
-        w = in_lanes ? group_softmax(to_float<T>(attp[gs]), LK) : zb[hl * (LK + 1) + j] * inv[hl];
+        w = in_lanes ? group_softmax(wraw, LK) : zb[hl * (LK + 1) + j] * inv[hl];
       else
-        w = to_float<T>(attp[gs]);
+        w = wraw;
       const int l = (int)fdiv((uint32_t)j, wa.div_k);
       Corners cs;
       sample_corners_any(u, v, lv[l], wl[l], (uint32_t)RB, row_base, row_stride, head_off, cs);
 #pragma unroll
       for (int c = 0; c < 4; ++c) cs.w[c] *= w;
       geo[j * gs_stride + hl] = cs;
+    };
+#pragma unroll
+    for (int k = 0; k < kPf; ++k)
+      if (wlane + 64 * k < nh * LK) geometry(wlane + 64 * k, pf_u[k], pf_v[k], pf_w[k]);
+    for (int s = wlane + 64 * kPf; s < nh * LK; s += 64) {
+      float u, v, wraw;
+      load_sample(locp, attp, s, u, v, wraw);
+      geometry(s, u, v, wraw);
     }
+    // the next chunk's locations and weights: in flight during this gather
+    prefetch(h0 + wa.nwaves * HPW);
     wave_lds_sync();
 
     // gather, in two passes, so that the registers LDS reads fill are never
