@@ -578,7 +578,8 @@ struct TileSmem {
   static constexpr size_t bytes = hist_in_stage ? tail : tail + hist_bytes;
 };
 static_assert(kChunk <= 1024, "item packing keeps 10-bit first / length fields");
-static_assert(TileSmem<32>::hist_in_stage, "no LDS growth for the D = 32 rows");
+// with the default 8x8 tiles the histogram costs the D = 32 rows no LDS
+static_assert(kTile != 8 || TileSmem<32>::hist_in_stage, "no LDS growth for the D = 32 rows");
 
 // Level, batch, head and tile of a bin.  The search runs over compile-time
 // level indices only, so the plan arrays stay in scalar registers instead of
