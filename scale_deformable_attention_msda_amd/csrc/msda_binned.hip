@@ -292,7 +292,14 @@ __device__ inline uint32_t ceil_div(uint32_t n, uint32_t d) { return (n + d - 1)
 // (decoupled look-back).  A block only ever waits for lower-numbered blocks,
 // which are dispatched before it and wait for nobody later, so the waits end.
 
-constexpr int kPlanBlock = 256;
+#ifndef MSDA_PLAN_BLOCK
+#define MSDA_PLAN_BLOCK 64
+#endif
+// bins (and lanes) per plan block: one wave measured faster than 128, 256,
+// 512 or 1024 bins a block (the per-block scan and chunk writes outweigh the
+// longer look-back)
+constexpr int kPlanBlock = MSDA_PLAN_BLOCK;
+static_assert(kPlanBlock % 64 == 0 && kPlanBlock <= 1024, "plan block of whole waves");
 
 // Position j of the chunk order is a bin: (batch, head) major, then the
 // levels coarsest first, then the tiles of a level row-major, so that the

@@ -15,6 +15,7 @@ measures every variant on one GPU:
   bin_chunk    MSDA_BIN_CHUNK       samples per tile-kernel chunk (binned backward)
   bin_tile     MSDA_BIN_TILE        destination tile edge in pixels (binned backward)
   count_block  MSDA_COUNT_SAMPLES   samples per count / scatter block
+  plan_block   MSDA_PLAN_BLOCK      bins per plan block (look-back over the blocks)
 
 Per point it records the registers, LDS and waves per SIMD the compiler reports
 for the kernels the constant touches, the per-kernel µs of a forward + binned
@@ -64,12 +65,15 @@ GROUPS = {
     "count_block": [("count2048", ["-DMSDA_COUNT_SAMPLES=2048"]),
                     ("count4096", ["-DMSDA_COUNT_SAMPLES=4096"]),
                     ("count8192", ["-DMSDA_COUNT_SAMPLES=8192"])],
+    "plan_block": [("plan64", ["-DMSDA_PLAN_BLOCK=64"]), ("plan128", ["-DMSDA_PLAN_BLOCK=128"]),
+                   ("plan256", ["-DMSDA_PLAN_BLOCK=256"])],
 }
 # the kernels whose resources each group changes (names as the compiler reports them)
 GROUP_KERNELS = {
     "fwd_pipe": ["fwd_kernel"], "fwd_block": ["fwd_kernel"], "win_pipe": ["fwd_win_kernel"],
     "win_blocks": ["fwd_win_kernel"], "win_lds": ["fwd_win_kernel"], "bin_chunk": ["tile_kernel"],
     "bin_tile": ["tile_kernel"], "count_block": ["count_kernel", "scatter_kernel"],
+    "plan_block": ["plan_kernel"],
 }
 # forward schedule of the timed step per group: the direct-gather groups force
 # the direct gather (the encoder takes the LDS-window schedule by default)
@@ -115,6 +119,7 @@ _INSTANCE = {
     "tile_kernel": re.compile(r"\d+tile_kernelIfLi32ELb1EE"),
     "count_kernel": re.compile(r"\d+count_kernelIfEE"),
     "scatter_kernel": re.compile(r"\d+scatter_kernelIfLb0EEE"),
+    "plan_kernel": re.compile(r"\d+plan_kernelENS_7BinArgsE"),
 }
 
 
@@ -358,9 +363,9 @@ def write_summary(path: str, ref: dict, results: list[dict], scale, steps: int, 
             % (scale if scale else (float("nan"), float("nan"))))
     lines += ["", f"In-tree library: {json.dumps(ref.get('us', ref))}", ""]
     lines.append("| group | point | flags | status | kernel resources (VGPRs / LDS B / waves per SIMD) "
-                 "| fwd µs | tile µs | count µs | scatter µs | merge µs | step µs | measured MB "
+                 "| fwd µs | tile µs | count µs | plan µs | scatter µs | merge µs | step µs | measured MB "
                  "(kernel: bytes, L2 hit) | parity |")
-    lines.append("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    lines.append("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in results:
         us = r.get("us", {})
         res = "; ".join(f"{k}: {v.get('vgprs')} / {v.get('lds')} / {v.get('waves_per_simd')}"
@@ -368,7 +373,7 @@ def write_summary(path: str, ref: dict, results: list[dict], scale, steps: int, 
         cnt = r.get("counters", {})
         meas = "; ".join(
             f"{k}: {v['bytes'] / 1e6:.1f}, {v['l2_hit']:.2f}" for k, v in sorted(cnt.items())
-            if k in ("fwd", "bin_tile", "bin_count", "bin_scatter", "bin_merge")
+            if k in ("fwd", "bin_tile", "bin_count", "bin_plan", "bin_scatter", "bin_merge")
             and v.get("bytes") is not None and v.get("l2_hit") is not None)
         par = r.get("parity", {})
         bad = sum(v["outside"] for v in par.values() if isinstance(v, dict))
@@ -376,7 +381,7 @@ def write_summary(path: str, ref: dict, results: list[dict], scale, steps: int, 
         lines.append(f"| {r['group']} | {r['name']} ({r.get('schedule', 'auto')}) | "
                      f"{' '.join(r['flags'])} | {r['status']} | "
                      f"{res} | {us.get('fwd', '-')} | {us.get('bin_tile', '-')} | "
-                     f"{us.get('bin_count', '-')} | {us.get('bin_scatter', '-')} | "
+                     f"{us.get('bin_count', '-')} | {us.get('bin_plan', '-')} | {us.get('bin_scatter', '-')} | "
                      f"{us.get('bin_merge', '-')} | {us.get('step', '-')} | {meas} | {par_s} |")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     open(path, "w").write("\n".join(lines) + "\n")
