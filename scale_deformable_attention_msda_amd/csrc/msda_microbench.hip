@@ -1,6 +1,6 @@
 // Microbenchmarks of the gfx950 memory paths the MSDA kernels depend on.
 //
-// They measure the ceilings the operator's kernels are judged against: what a
+// They measure the ceilings the operator's kernels are measured against: what a
 // streaming read and a copy reach in HBM, how many fp32 and packed-bf16
 // global atomic adds per second the memory side retires (spread over a large
 // span, or piled on a small hot set, as the coarse pyramid levels pile the

@@ -275,8 +275,7 @@ def _profiled(lib: str, counters: list[str], out_dir: str, ref_dir: str, copy: b
 
 
 def run_points(groups: list[str], counters: bool, out_md: str, steps: int) -> None:
-    out_dir = os.path.join(ROOT, "gpurun_out")
-    os.makedirs(out_dir, exist_ok=True)
+    out_dir = tempfile.mkdtemp(prefix="msda_sweep_")  # reference outputs and counter runs
     ref_dir = tempfile.mkdtemp(prefix="sweep_ref_", dir=out_dir)
     default_lib = os.path.join(PKG, "libmsda.so")
 
@@ -338,7 +337,7 @@ def run_points(groups: list[str], counters: bool, out_md: str, steps: int) -> No
                         rec["counters_error"] = str(e)[:300]
             results.append(rec)
             print(f"[sweep] {g}/{name} {json.dumps(rec)}", flush=True)
-    shutil.rmtree(ref_dir, ignore_errors=True)
+    shutil.rmtree(out_dir, ignore_errors=True)
     write_summary(out_md, ref, results, scale, steps, counters)
 
 
