@@ -208,7 +208,7 @@ CUS = 256
 
 
 def microbenchmarks(msda, dev, stream) -> dict:
-    """Ceilings of the memory paths on this machine, from the library's microbenchmarks
+    """Ceilings of the memory paths on this GPU, from the library's microbenchmarks
     (include/msda_bench.h): streaming read and copy of 1 GiB, fp32 and packed-bf16 global
     atomics over whole 128-byte rows (random over 256 MiB, and piled on a 64 KiB hot set),
     gathers of random 128-byte rows from the vector L1 (16 KiB span), an L2-sized span
@@ -657,7 +657,7 @@ def main(argv=None) -> int:
                                                    for n, v in cold_k.items()}
         del scratch
 
-        # what the box's memory paths reach (the library's own microbenchmarks)
+        # what this GPU's memory paths reach (the library's own microbenchmarks)
         log("[bench] memory-path microbenchmarks")
         extras["achievable"] = microbenchmarks(msda, dev, stream)
 
@@ -701,8 +701,8 @@ def main(argv=None) -> int:
             extras["query_order"] = orders
 
         # the atomic scatter (the pages' design) against what device-scope fp32
-        # atomics reach on this machine: torch's index_add_ of whole 128-byte rows
-        # (32 lanes x 4 B per row, the best pattern measured)
+        # atomics reach on this GPU: the atomic_f32 microbenchmark (whole 128-byte
+        # rows per instruction, the best pattern measured)
         log("[bench] atomic scatter and the atomic-add ceiling")
         adds = bm["samples"] * 4 * wl.D
         t0 = batches[0]
@@ -871,7 +871,7 @@ def main(argv=None) -> int:
     if "achievable" in extras:
         ach = extras["achievable"]
         res["fwd_frac_of_read"] = round(bm["fwd"] / (fwd_us * 1e-6) / 1e9 / ach["read_gbps"], 4)
-        # the forward's corner-row gather against the gather ceilings of the box
+        # the forward's corner-row gather against the GPU's measured gather ceilings
         rate = bm["corner_rows"] / (fwd_us * 1e-6) / 1e9
         res["fwd_corner_gather"] = {
             "gbps": round(rate, 1),

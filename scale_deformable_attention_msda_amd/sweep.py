@@ -352,7 +352,7 @@ def write_summary(path: str, ref: dict, results: list[dict], scale, steps: int, 
              f"µs: mean HIP-event duration per step over {steps} steps (2 input batches "
              "alternating). Registers / LDS / waves per SIMD: the compiler's resource report for "
              "the fp32, D = 32 instantiation. Parity: every output against the in-tree library "
-             "(the oracle-gated build), elements outside rtol 1e-5 / atol 1e-6 (forward) and "
+             "(whose tests check it against the oracle), elements outside rtol 1e-5 / atol 1e-6 (forward) and "
              "1e-4 / 1e-5 (backward)."]
     if counters:
         lines.append(

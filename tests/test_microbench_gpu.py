@@ -1,6 +1,6 @@
 """GPU: the memory-path microbenchmarks of libmsda.so run and report plausible rates
 for one MI355X (wide bounds: they catch a broken kernel or a wrong unit count, not a
-slow box)."""
+slow GPU)."""
 import pytest
 import torch
 
