@@ -1,7 +1,7 @@
 """Build ``libmsda.so`` (the C-ABI MSDA library) for gfx950 with hipcc, in-tree.
 
 Each source compiles to an object of its own (in parallel), then hipcc links
-the shared library.  ``extra_flags`` (e.g. ``-DMSDA_BIN_TILE=16``) reach every
+the shared library.  ``extra_flags`` (e.g. ``-DMSDA_BIN_TILE=10``) reach every
 compile, which is how the tuning sweep builds its variants.
 """
 from __future__ import annotations

@@ -61,9 +61,11 @@ constexpr int kEdge = kTile + 1;              // tile plus its one-pixel rim, pe
 constexpr int kCells = kEdge * kEdge;         // bilinear cells whose top-left corner is in [-1, T)
 constexpr int kChunk = MSDA_BIN_CHUNK;        // samples per tile-kernel block at most
 constexpr int kCountSamples = MSDA_COUNT_SAMPLES;  // samples per count / scatter block
-// wave 0 of the tile kernel plans with two cells per lane; the item fields hold
-// 10-bit positions; count and scatter threads own whole rounds of 256 samples
-static_assert(kTile >= 2 && kCells <= 128, "tile edge 2..10");
+// wave 0 of the tile kernel plans with two cells per lane, cells j and j + 64
+// of lane j, and indexes the first 64 cells and items without a bound check, so
+// the tile holds 64..128 cells; the item fields hold 10-bit positions; count and
+// scatter threads own whole rounds of 256 samples
+static_assert(kCells >= 64 && kCells <= 128, "tile edge 7..10");
 static_assert(kChunk % 256 == 0 && kChunk <= 1024, "chunk a multiple of 256, at most 1024");
 static_assert(kCountSamples % 256 == 0 && kCountSamples <= 16384, "count block of 256..16384");
 constexpr int kHistLdsBytes = 48 * 1024;

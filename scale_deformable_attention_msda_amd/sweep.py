@@ -60,8 +60,8 @@ GROUPS = {
                    ("winbpc4", ["-DMSDA_WIN_BLOCKS_PER_CU=4"])],
     "bin_chunk": [("chunk256", ["-DMSDA_BIN_CHUNK=256"]), ("chunk512", ["-DMSDA_BIN_CHUNK=512"]),
                   ("chunk1024", ["-DMSDA_BIN_CHUNK=1024"])],
-    "bin_tile": [("tile4", ["-DMSDA_BIN_TILE=4"]), ("tile6", ["-DMSDA_BIN_TILE=6"]),
-                 ("tile8", ["-DMSDA_BIN_TILE=8"]), ("tile10", ["-DMSDA_BIN_TILE=10"])],
+    "bin_tile": [("tile7", ["-DMSDA_BIN_TILE=7"]), ("tile8", ["-DMSDA_BIN_TILE=8"]),
+                 ("tile9", ["-DMSDA_BIN_TILE=9"]), ("tile10", ["-DMSDA_BIN_TILE=10"])],
     "count_block": [("count2048", ["-DMSDA_COUNT_SAMPLES=2048"]),
                     ("count4096", ["-DMSDA_COUNT_SAMPLES=4096"]),
                     ("count8192", ["-DMSDA_COUNT_SAMPLES=8192"])],
