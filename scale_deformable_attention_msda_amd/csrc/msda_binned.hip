@@ -285,6 +285,45 @@ __device__ inline uint32_t wave_max(uint32_t x) {
 
 __device__ inline uint32_t ceil_div(uint32_t n, uint32_t d) { return (n + d - 1) / d; }
 
+// Level, batch, head and tile of a bin.  The search runs over compile-time
+// level indices only, so the plan arrays stay in scalar registers instead of
+// being fetched from the argument segment with a computed index.
+struct BinPos {
+  int l, b, m, ty, tx, H, W, ntx;
+  int64_t start;  // first pyramid row of the level
+};
+
+__device__ inline BinPos decode_bin(const BinPlan &p, int bin) {
+  const int BM = (int)p.B * p.M;
+  int l = 0, base = 0, nt = 1, ntx = 1, H = 1, W = 1;
+  int64_t start = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxLevels; ++k) {
+    if (k < p.L && bin >= p.bin_base[k] && bin < p.bin_base[k] + BM * p.ntiles[k]) {
+      l = k;
+      base = p.bin_base[k];
+      nt = p.ntiles[k];
+      ntx = p.ntx[k];
+      H = p.H[k];
+      W = p.W[k];
+      start = p.start[k];
+    }
+  }
+  BinPos r;
+  const int rem = bin - base;
+  const int bm = rem / nt, t = rem - bm * nt;
+  r.l = l;
+  r.b = bm / p.M;
+  r.m = bm - r.b * p.M;
+  r.ty = t / ntx;
+  r.tx = t - r.ty * ntx;
+  r.H = H;
+  r.W = W;
+  r.ntx = ntx;
+  r.start = start;
+  return r;
+}
+
 // ---------------------------------------------------------------- plan pass
 //
 // Many blocks of kPlanBlock bins each, in chunk order, one bin per thread.
@@ -307,15 +346,21 @@ static_assert(kPlanBlock % 64 == 0 && kPlanBlock <= 1024, "plan block of whole w
 // levels coarsest first, then the tiles of a level row-major, so that the
 // chunks running at one time share the grad_out rows of one head of one image.
 struct OrderTab {
-  int tile_off, ntiles, bin_base;
+  int tile_off, ntiles, bin_base, ntx;
 };
 
-__device__ inline int bin_of_order(const BinPlan &p, const OrderTab *ot, int j) {
+// Bin at position j of the chunk order, and its position (level | head << 4,
+// batch, tile row, tile column) for the tile pass.
+__device__ inline int bin_of_order(const BinPlan &p, const OrderTab *ot, int j, uint4 &where) {
   const int bm = j / p.tiles_bm;
   const int off = j - bm * p.tiles_bm;
   int k = 0;
   while (k + 1 < p.L && !(off >= ot[k].tile_off && off < ot[k].tile_off + ot[k].ntiles)) ++k;
-  return ot[k].bin_base + bm * ot[k].ntiles + (off - ot[k].tile_off);
+  const int t = off - ot[k].tile_off;
+  const int b = bm / p.M, ty = t / ot[k].ntx;
+  where = make_uint4((uint32_t)k | ((uint32_t)(bm - b * p.M) << 4), (uint32_t)b, (uint32_t)ty,
+                     (uint32_t)(t - ty * ot[k].ntx));
+  return ot[k].bin_base + bm * ot[k].ntiles + t;
 }
 
 __device__ inline uint32_t chunks_of(const BinPlan &p, uint32_t c) {
@@ -365,13 +410,14 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
   const BinPlan &p = a.p;
   if (threadIdx.x < (unsigned)p.L) {
     const int l = threadIdx.x;
-    ot[l] = OrderTab{p.tile_off[l], p.ntiles[l], p.bin_base[l]};
+    ot[l] = OrderTab{p.tile_off[l], p.ntiles[l], p.bin_base[l], p.ntx[l]};
   }
   lds_barrier();
   const int n = p.nbins;
   const int j = (int)blockIdx.x * kPlanBlock + (int)threadIdx.x;
   const bool live = j < n;
-  const int i = bin_of_order(p, ot, min(j, n - 1));
+  uint4 where;
+  const int i = bin_of_order(p, ot, min(j, n - 1), where);
   uint32_t cs[kStripes];
 #pragma unroll
   for (int k = 0; k < kStripes; ++k) cs[k] = a.w.counts[counter_index(i, k)];
@@ -418,10 +464,13 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(BinArgs a) {
     a.w.bin_start[i] = pos;
     a.w.bin_nch[i] = nch;
     a.w.bin_slot0[i] = nch > 1 ? slot : kNoSlot;
+    // the bin's position is stored with each chunk, so that the tile pass
+    // decodes no bin index
     for (uint32_t k = 0; k < nch; ++k) {
       const uint32_t first = k * (uint32_t)p.chunk;
       const uint32_t cnt = c > first ? min((uint32_t)p.chunk, c - first) : 0u;
       a.w.chunks[ch + k] = make_uint4((uint32_t)i, pos + first, cnt, nch > 1 ? slot + k : kNoSlot);
+      a.w.chunk_pos[ch + k] = where;
     }
   }
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
@@ -559,7 +608,8 @@ constexpr int kMaxItems = kCells;   // stage slots, one per item
 //   items  [kMaxItems] u32         first | (len - 1) << 10 | cell << 20 of each item
 //   sched  [kMaxItems] u32         items by decreasing number of batches
 //   next   u32                     the block's next chunk, claimed by thread 0
-//   lvl    [kMaxLevels] LevelTab   level table for decoding the bins of later chunks
+//   lvl    [kMaxLevels] LevelTab   level extents for the positions of later chunks
+//   lstart [kMaxLevels] i64        first pyramid row of each level
 template <int D>
 struct TileSmem {
   static constexpr int RS = TileLayout<D>::RS;
@@ -582,7 +632,8 @@ struct TileSmem {
   // after the level table
   static constexpr size_t hist_bytes = 4 * ((size_t)kChunk / kU + 1);
   static constexpr bool hist_in_stage = item_bytes >= rec_bytes + hist_bytes;
-  static constexpr size_t tail = (lvl + (size_t)kMaxLevels * sizeof(LevelTab) + 15) / 16 * 16;
+  static constexpr size_t lstart = (lvl + (size_t)kMaxLevels * sizeof(LevelTab) + 7) / 8 * 8;
+  static constexpr size_t tail = (lstart + (size_t)kMaxLevels * 8 + 15) / 16 * 16;
   static constexpr size_t hist = hist_in_stage ? stage + rec_bytes : tail;
   static constexpr size_t bytes = hist_in_stage ? tail : tail + hist_bytes;
 };
@@ -590,63 +641,22 @@ static_assert(kChunk <= 1024, "item packing keeps 10-bit first / length fields")
 // with the default 8x8 tiles the histogram costs the D = 32 rows no LDS
 static_assert(kTile != 8 || TileSmem<32>::hist_in_stage, "no LDS growth for the D = 32 rows");
 
-// Level, batch, head and tile of a bin.  The search runs over compile-time
-// level indices only, so the plan arrays stay in scalar registers instead of
-// being fetched from the argument segment with a computed index.
-struct BinPos {
-  int l, b, m, ty, tx, H, W, ntx;
-};
-
-__device__ inline BinPos decode_bin(const BinPlan &p, int bin) {
-  const int BM = (int)p.B * p.M;
-  int l = 0, base = 0, nt = 1, ntx = 1, H = 1, W = 1;
-#pragma unroll
-  for (int k = 0; k < kMaxLevels; ++k) {
-    if (k < p.L && bin >= p.bin_base[k] && bin < p.bin_base[k] + BM * p.ntiles[k]) {
-      l = k;
-      base = p.bin_base[k];
-      nt = p.ntiles[k];
-      ntx = p.ntx[k];
-      H = p.H[k];
-      W = p.W[k];
-    }
-  }
+// A chunk's bin position as the plan pass stored it (chunk_pos), with the
+// level's extent from the level table in LDS: no search and no division in the
+// tile pass's chunk loop.  The entry is wave-uniform, and so are the results.
+__device__ inline BinPos chunk_bin_pos(const uint4 &c, const LevelTab *lt, const int64_t *lstart) {
   BinPos r;
-  const int rem = bin - base;
-  const int bm = rem / nt, t = rem - bm * nt;
-  r.l = l;
-  r.b = bm / p.M;
-  r.m = bm - r.b * p.M;
-  r.ty = t / ntx;
-  r.tx = t - r.ty * ntx;
-  r.H = H;
-  r.W = W;
-  r.ntx = ntx;
-  return r;
-}
-
-// decode_bin from the level table in LDS: inside the tile kernel's chunk loop
-// the plan's per-level arrays would otherwise stay in scalar registers for the
-// whole loop.  bin is wave-uniform, and so are the results.
-__device__ inline BinPos decode_bin_lds(const BinPlan &p, const LevelTab *lt, int bin) {
-  const int BM = (int)p.B * p.M;
-  int l = 0;
-  while (l + 1 < p.L && !(bin >= lt[l].bin_base && bin < lt[l].bin_base + BM * lt[l].ntiles)) ++l;
-  l = __builtin_amdgcn_readfirstlane(l);
-  const int base = __builtin_amdgcn_readfirstlane(lt[l].bin_base);
-  const int nt = __builtin_amdgcn_readfirstlane(lt[l].ntiles);
-  const int ntx = __builtin_amdgcn_readfirstlane(lt[l].ntx);
-  BinPos r;
-  const int rem = bin - base;
-  const int bm = rem / nt, t = rem - bm * nt;
-  r.l = l;
-  r.b = bm / p.M;
-  r.m = bm - r.b * p.M;
-  r.ty = t / ntx;
-  r.tx = t - r.ty * ntx;
-  r.H = __builtin_amdgcn_readfirstlane(lt[l].H);
-  r.W = __builtin_amdgcn_readfirstlane(lt[l].W);
-  r.ntx = ntx;
+  r.l = __builtin_amdgcn_readfirstlane((int)(c.x & 15u));
+  r.m = __builtin_amdgcn_readfirstlane((int)(c.x >> 4));
+  r.b = __builtin_amdgcn_readfirstlane((int)c.y);
+  r.ty = __builtin_amdgcn_readfirstlane((int)c.z);
+  r.tx = __builtin_amdgcn_readfirstlane((int)c.w);
+  r.H = __builtin_amdgcn_readfirstlane(lt[r.l].H);
+  r.W = __builtin_amdgcn_readfirstlane(lt[r.l].W);
+  r.ntx = __builtin_amdgcn_readfirstlane(lt[r.l].ntx);
+  const int64_t st = lstart[r.l];
+  r.start = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)((uint64_t)st >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)st));
   return r;
 }
 
@@ -891,6 +901,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   uint32_t *sched = reinterpret_cast<uint32_t *>(smem + SM::sched);
   uint32_t *next_slot = reinterpret_cast<uint32_t *>(smem + SM::next);
   LevelTab *lt = reinterpret_cast<LevelTab *>(smem + SM::lvl);
+  int64_t *lstart = reinterpret_cast<int64_t *>(smem + SM::lstart);
 
   const BinPlan &p = a.p;
   const __amdgpu_buffer_rsrc_t gsrc =
@@ -917,7 +928,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   auto load_chunk = [&](const uint4 &c, const BinPos &q, uint32_t tid) {
     const int grp = (int)tid / G, lane = (int)tid % G;
     const uint32_t f = c.y, n = min(c.z, (uint32_t)kChunk);
-    const int64_t st = a.starts[q.l];
+    const int64_t st = q.start;
     loaded_start = st;
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
@@ -939,6 +950,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   BinPos loaded_pos = decode_bin(p, (int)ck.x);
   load_chunk(ck, loaded_pos, threadIdx.x);
   stage_level_tab(p, lt);  // read after the first barrier below
+  if (threadIdx.x < (unsigned)p.L) lstart[threadIdx.x] = p.start[threadIdx.x];
 
   for (;;) {
     // the thread index, made opaque to the compiler once per chunk: otherwise it
@@ -970,6 +982,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     // the next chunk's entry: needed only for the prefetch after the item loop
     const uint32_t cn = __builtin_amdgcn_readfirstlane(*next_slot);
     const uint4 ck_next = a.w.chunks[min(cn, nchunks - 1)];
+    const uint4 cp_next = a.w.chunk_pos[min(cn, nchunks - 1)];
 
     // ---- phase A: cell of each sample and its rank inside the cell
 #pragma unroll
@@ -1192,7 +1205,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
     // the next chunk's records and value rows: in flight during the two passes
     // below (after the last chunk this loads a chunk again and leaves it unused,
     // which keeps the registers of the loads out of the item loop)
-    loaded_pos = decode_bin_lds(p, lt, (int)ck_next.x);
+    loaded_pos = chunk_bin_pos(cp_next, lt, lstart);
     load_chunk(ck_next, loaded_pos, tid);
 
     // ---- per-sample results back in record order: the scatter pass wrote a
@@ -1253,13 +1266,22 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       float v[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) v[i] = (f[0][i] + f[1][i]) + (f[2][i] + f[3][i]);
+      // further pieces: step s reads piece s of all four cells together (the
+      // zero row where a cell has fewer), so four loads are in flight per step
+      uint32_t steps = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        for (uint32_t it = ib[q] + 1; it < ie[q]; ++it) {
-          const float *src = stage + (it * 4 + q) * RS + lane * VEC;
+      for (int q = 0; q < 4; ++q) steps = max(steps, ie[q] - ib[q]);
+      for (uint32_t st = 1; st < steps; ++st) {
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) v[i] += src[i];
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t it = ib[q] + st;
+          const float *src = it < ie[q] ? stage + (it * 4 + q) * RS + lane * VEC
+                                        : vt + kZeroRow * RS + lane * VEC;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) f[q][i] = src[i];
         }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] += (f[0][i] + f[1][i]) + (f[2][i] + f[3][i]);
       }
       if (slot != kNoSlot) {
         float *dst = a.w.slots + ((int64_t)slot * NROWS + r) * D + lane * VEC;
@@ -1576,6 +1598,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
   char *b0 = take(nb4 * sizeof(uint32_t));
   char *nc = take(16);
   char *ch = take((size_t)p.max_chunks * sizeof(uint4));
+  char *cp = take((size_t)p.max_chunks * sizeof(uint4));
   char *recs = take((size_t)p.total * sizeof(uint4));
   char *rim = take((size_t)p.nbins * 4 * kTile * p.D * sizeof(float));
   char *sl = take((size_t)p.max_slots * E * E * p.D * sizeof(float));
@@ -1589,6 +1612,7 @@ static size_t layout(const BinPlan &p, BinScratch *w, char *base) {
     w->bin_slot0 = reinterpret_cast<uint32_t *>(b0);
     w->nchunks = reinterpret_cast<uint32_t *>(nc);
     w->chunks = reinterpret_cast<uint4 *>(ch);
+    w->chunk_pos = reinterpret_cast<uint4 *>(cp);
     w->recs = reinterpret_cast<uint4 *>(recs);
     w->rim = reinterpret_cast<float *>(rim);
     w->slots = reinterpret_cast<float *>(sl);

@@ -76,6 +76,8 @@ struct BinScratch {
   uint32_t *bin_slot0;  // [nbins] first partial-tile slot of a split bin
   uint32_t *nchunks;    // [2] chunks in use; the tile pass's counter of claimed chunks
   uint4 *chunks;        // [max_chunks] (bin, first position, count, slot or ~0) in chunk order
+  uint4 *chunk_pos;     // [max_chunks] (level | head << 4, batch, tile row, tile column) of each
+                        // chunk's bin
   uint4 *recs;          // [total] (id, u, v, A) of every live sample, sorted by bin
   float *rim;           // [nbins][4*tile][D] edge rows and halo of single-chunk tiles
   float *slots;         // [max_slots][(tile+1)^2][D] whole partial tiles of split bins
