@@ -735,16 +735,28 @@ __device__ inline uint32_t ceil_div_small(uint32_t n, uint32_t d, float rd) {
   return q + (q * d < n ? 1u : 0u);
 }
 
-// Wave 0 of the tile kernel, step 1: cell starts (exclusive scan of the
-// per-cell counts, cstart[kCells] = live samples).  Lane j holds cells j and j + 64.
-__device__ inline void cell_starts(const uint32_t *cnt, uint32_t *cstart) {
-  const uint32_t c0 = threadIdx.x, c1 = threadIdx.x + 64;
-  const uint32_t n0 = cnt[c0], n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
-  const uint32_t inc0 = wave_incl_scan(n0);
-  const uint32_t total0 = __builtin_amdgcn_readlane(inc0, 63);
-  const uint32_t inc1 = total0 + wave_incl_scan(n1);
-  cstart[c0] = inc0 - n0;
-  if (c1 <= (uint32_t)kCells) cstart[c1] = inc1 - n1;
+// Cell starts in registers, computed by every wave of the tile kernel: lane j
+// holds the exclusive starts s0, s1 of cells j and j + 64 (the count of cell
+// kCells reads as 0, so the start of cell kCells is the number of live samples).
+struct CellScan {
+  uint32_t n0, n1, s0, s1, total;
+};
+__device__ inline CellScan cell_scan(const uint32_t *cnt) {
+  const uint32_t lane = threadIdx.x & 63, c1 = lane + 64;
+  CellScan r;
+  r.n0 = cnt[lane];
+  r.n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
+  const uint32_t inc0 = wave_incl_scan(r.n0);
+  const uint32_t inc1 = __builtin_amdgcn_readlane(inc0, 63) + wave_incl_scan(r.n1);
+  r.s0 = inc0 - r.n0;
+  r.s1 = inc1 - r.n1;
+  r.total = __builtin_amdgcn_readlane(inc1, 63);
+  return r;
+}
+
+// Value v of lane src (0..63) of the wave; every lane must be active.
+__device__ inline uint32_t lane_value(uint32_t src, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)v);
 }
 
 // Inclusive prefix maximum over the 64 lanes (values >= 0).
@@ -760,7 +772,7 @@ __device__ inline uint32_t wave_incl_max(uint32_t x) {
   return max(x, max(row >= 1 ? t0 : 0u, max(row >= 2 ? t1 : 0u, row >= 3 ? t2 : 0u)));
 }
 
-// Wave 0 of the tile kernel, step 2: the item table and the schedule.  Past
+// Wave 0 of the tile kernel, after the cell scan: the item table and the schedule.  Past
 // the choice of P every step is a fixed sequence of wave-wide operations (no
 // loop over the pieces of a cell or over the batch counts present), since this
 // runs on one wave while the block waits for it.
@@ -772,12 +784,13 @@ __device__ inline uint32_t wave_incl_max(uint32_t x) {
 //     counting sort with the histogram in `scratch` (at least kChunk / kU + 1
 //     words); the order inside one batch count is free, since the schedule
 //     only decides which lane group runs an item, never a result.
-__device__ inline void plan_items(const uint32_t *cnt, const uint32_t *cstart, uint32_t *istart,
-                                  uint32_t *items, uint32_t *sched, uint32_t *scratch) {
+__device__ inline void plan_items(const CellScan &cs, const uint32_t *cnt, const uint32_t *cstart,
+                                  uint32_t *istart, uint32_t *items, uint32_t *sched,
+                                  uint32_t *scratch) {
   const uint32_t lane = threadIdx.x;
   const uint32_t c0 = lane, c1 = lane + 64;
-  const uint32_t n0 = cnt[c0], n1 = c1 < (uint32_t)kCells ? cnt[c1] : 0u;
-  const uint32_t total = cstart[kCells];
+  const uint32_t n0 = cs.n0, n1 = cs.n1;
+  const uint32_t total = cs.total;
   // smallest P = kU * m with at most kMaxItems pieces: linear steps up from
   // the lower bound total / kMaxItems, then a binary search if that is slow
   // (m = kChunk / kU leaves one piece per non-empty cell, at most kCells)
@@ -1010,15 +1023,22 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       tag[i] = t;
     }
     __syncthreads();
-    if (tid < 64) cell_starts(cnt, cstart);
-    __syncthreads();
-    // wave 0 plans the items while the other waves put the records in cell order
+    // every wave scans the cell counts itself; wave 0 stores the starts and
+    // plans the items while the other waves put the records in cell order,
+    // looking the starts up in their own registers
+    const CellScan cs = cell_scan(cnt);
     if (tid < 64) {
-      plan_items(cnt, cstart, istart, items, sched, reinterpret_cast<uint32_t *>(smem + SM::hist));
+      cstart[tid] = cs.s0;
+      if (tid + 64 <= (uint32_t)kCells) cstart[tid + 64] = cs.s1;
+      plan_items(cs, cnt, cstart, istart, items, sched, reinterpret_cast<uint32_t *>(smem + SM::hist));
     } else {
-      for (uint32_t i = tid - 64; i < count; i += blockDim.x - 64) {
-        const uint32_t t = tag[i];
-        if (t != kDropped) sorted[cstart[t & 0xffu] + (t >> 8)] = raw[i];
+      // whole waves per step, so that every lane takes part in the lane lookups
+      for (uint32_t base = 0; base < count; base += blockDim.x - 64) {
+        const uint32_t i = base + tid - 64;
+        const uint32_t t = i < count ? tag[i] : kDropped;
+        const uint32_t c = t & 63u;
+        const uint32_t lo = lane_value(c, cs.s0), hi = lane_value(c, cs.s1);
+        if (t != kDropped) sorted[((t & 0xffu) < 64u ? lo : hi) + (t >> 8)] = raw[i];
       }
     }
     __syncthreads();
