@@ -601,7 +601,8 @@ constexpr int kMaxItems = kCells;   // stage slots, one per item
 //   vt     [kEdge^2 + 1][RS] f32   value rows of the tile and its rim, then one zero row
 //   stage  [kMaxItems][4][RS] f32  per-item corner sums; holds the unsorted records in phase A
 //   sorted [kChunk] SampleRec      samples sorted by cell
-//   tag    [kChunk] u32            cell | rank << 8 of each unsorted record (~0: dropped)
+//   tag    [kChunk] u32            cell | rank << 8 of each unsorted record, after the
+//                                  sort its sorted position (~0: dropped)
 //   cnt    [kCells + 1] u32        samples per cell
 //   cstart [kCells + 1] u32        first sorted position of each cell
 //   istart [kCells + 1] u32        first item of each cell; istart[kCells] = items in all
@@ -759,6 +760,11 @@ __device__ inline uint32_t lane_value(uint32_t src, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)v);
 }
 
+// Set bits of a 64-lane mask below the calling lane.
+__device__ inline uint32_t lanes_below(uint64_t k) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(k >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)k, 0u));
+}
+
 // Inclusive prefix maximum over the 64 lanes (values >= 0).
 __device__ inline uint32_t wave_incl_max(uint32_t x) {
   x = max(x, dpp_u32<0x111>(x));  // row_shr:1 (lanes past a row's start read 0)
@@ -846,7 +852,21 @@ __device__ inline void plan_items(const CellScan &cs, const uint32_t *cnt, const
     items[ii[h]] = first | ((len - 1) << 10) | (c << 20);
     b[h] = (len + kU - 1) / kU;
   }
-  // schedule: counting sort by decreasing batch count, counts 1 .. m
+  // schedule: items by decreasing batch count (1 .. m); the order inside one
+  // count is free.  With few counts (the common case) one pair of wave
+  // ballots per count places the items; else a counting sort with the
+  // histogram in scratch
+  if (m <= 16) {
+    uint32_t base = 0;
+    for (uint32_t bb = m; bb >= 1; --bb) {
+      const uint64_t k0 = __ballot(b[0] == bb), k1 = __ballot(b[1] == bb);
+      const uint32_t n0 = (uint32_t)__popcll(k0);
+      if (b[0] == bb) sched[base + lanes_below(k0)] = ii[0];
+      if (b[1] == bb) sched[base + n0 + lanes_below(k1)] = ii[1];
+      base += n0 + (uint32_t)__popcll(k1);
+    }
+    return;
+  }
   for (uint32_t e = lane; e <= m; e += 64) scratch[e] = 0u;
   uint32_t rank[2] = {0u, 0u};
 #pragma unroll
@@ -1038,7 +1058,11 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
         const uint32_t t = i < count ? tag[i] : kDropped;
         const uint32_t c = t & 63u;
         const uint32_t lo = lane_value(c, cs.s0), hi = lane_value(c, cs.s1);
-        if (t != kDropped) sorted[((t & 0xffu) < 64u ? lo : hi) + (t >> 8)] = raw[i];
+        if (t != kDropped) {
+          const uint32_t d = ((t & 0xffu) < 64u ? lo : hi) + (t >> 8);
+          sorted[d] = raw[i];
+          tag[i] = d;  // the result pass finds the record here
+        }
       }
     }
     __syncthreads();
@@ -1243,7 +1267,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < kPer; ++r)
-        pos[r] = tg[r] != kDropped ? cstart[tg[r] & 0xffu] + (tg[r] >> 8) : 0u;
+        pos[r] = tg[r] != kDropped ? tg[r] : 0u;
 #pragma unroll
       for (int r = 0; r < kPer; ++r) rr[r] = reinterpret_cast<const uint4 *>(sorted)[pos[r]];
 #pragma unroll
