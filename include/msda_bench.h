@@ -76,6 +76,21 @@ void msda_test_set_forward_schedule(int schedule);
  */
 void msda_test_set_tile_wide_addressing(int wide);
 
+/*
+ * Diagnostic: shader-clock sums of the phases of the last binned tile pass on
+ * the current device, one row of 12 unsigned 64-bit values per tile block
+ * (row = block index), copied into out (host memory, nblocks * 12 values,
+ * owned by the caller).  Each row is wave 0's view of its block: slot 0
+ * staging and the chunk claim, 1 cell pass, 2 cell scan, plan and record sort,
+ * 3 item loop, 4 the next chunk's position, 5 its loads issued, 6 result pass,
+ * 7 pixel pass, 8 the last barrier, 9 and 10 unused, 11 chunks processed.
+ * Only a library built with -DMSDA_TILE_PHASE_CLOCKS records them; any other
+ * build returns MSDA_ERR_UNSUPPORTED without touching the device.  Errors:
+ * MSDA_ERR_NULL_POINTER, MSDA_ERR_INVALID_DIMS (nblocks outside 0..2048),
+ * MSDA_ERR_HIP.
+ */
+msda_status msda_test_tile_phase_clocks(unsigned long long *out, int nblocks);
+
 /* Memory-path microbenchmarks (msda_microbench_run). */
 typedef enum {
     /* streaming read of the buffer (16-byte loads); units = bytes read */

@@ -126,6 +126,9 @@ def load_library(path: str = LIB_PATH):
         if hasattr(lib, name):
             getattr(lib, name).argtypes = [arg]
             getattr(lib, name).restype = None
+    if hasattr(lib, "msda_test_tile_phase_clocks"):
+        lib.msda_test_tile_phase_clocks.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), ctypes.c_int]
+        lib.msda_test_tile_phase_clocks.restype = ctypes.c_int
     lib.msda_microbench_run.argtypes = [ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_size_t,
                                         ctypes.c_int, vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double)]
@@ -182,6 +185,17 @@ def msda_test_set_tile_wide_addressing(wide: bool) -> None:
     """Test hook: later binned backward calls on this thread run the tile pass's 64-bit
     addressing path (True) or pick it by size (False, the default)."""
     load_library().msda_test_set_tile_wide_addressing(1 if wide else 0)
+
+
+def msda_test_tile_phase_clocks(nblocks: int = 2048) -> list[list[int]]:
+    """Diagnostic: per-block shader-clock sums of the last tile pass's phases,
+    nblocks rows of 12 values (see msda_bench.h).  Raises unless the loaded library
+    was built with -DMSDA_TILE_PHASE_CLOCKS."""
+    buf = (ctypes.c_ulonglong * (nblocks * 12))()
+    st = load_library().msda_test_tile_phase_clocks(buf, nblocks)
+    if st != 0:
+        raise MsdaError(st, "msda_test_tile_phase_clocks")
+    return [list(buf[12 * b:12 * b + 12]) for b in range(nblocks)]
 
 
 def msda_test_set_plan_wait_limit(polls: int) -> None:

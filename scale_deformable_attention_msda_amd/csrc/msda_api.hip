@@ -577,6 +577,14 @@ void msda_test_set_forward_schedule(int schedule) { msda::set_forward_schedule(s
 
 void msda_test_set_tile_wide_addressing(int wide) { msda::set_tile_wide_addressing(wide != 0); }
 
+msda_status msda_test_tile_phase_clocks(unsigned long long *out, int nblocks) {
+  if (out == nullptr) return MSDA_ERR_NULL_POINTER;
+  if (nblocks < 0 || nblocks > 2048) return MSDA_ERR_INVALID_DIMS;
+  const hipError_t e = msda::tile_phase_clocks(out, nblocks);
+  if (e == hipErrorNotSupported) return MSDA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? MSDA_OK : MSDA_ERR_HIP;
+}
+
 const char *msda_status_string(msda_status status) {
   switch (status) {
     case MSDA_OK: return "MSDA_OK";

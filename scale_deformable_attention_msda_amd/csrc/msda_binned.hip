@@ -905,6 +905,27 @@ __device__ inline uint32_t dpp_move_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
+// Diagnostic build (-DMSDA_TILE_PHASE_CLOCKS): every wave of a tile block
+// reads the shader clock (s_memtime) after each phase of a chunk and sums the
+// intervals; thread 0 leaves its block's sums, wave 0's view of the block's
+// phases, in g_tile_phase when the block ends.  The default build compiles
+// none of it.  Slots: 0 staging and the chunk claim, 1 cell pass, 2 cell scan,
+// plan and record sort, 3 item loop, 4 the next chunk's position, 5 its loads
+// issued, 6 result pass, 7 pixel pass, 8 last barrier; slot 11 counts chunks.
+constexpr int kPhaseSlots = 12;
+constexpr int kPhaseBlocks = 2048;
+#ifdef MSDA_TILE_PHASE_CLOCKS
+__device__ unsigned long long g_tile_phase[kPhaseBlocks][kPhaseSlots];
+#define TILE_PHASE(k)                                  \
+  do {                                                 \
+    const unsigned long long now = __builtin_amdgcn_s_memtime(); \
+    phase_sum[k] += now - phase_t;                     \
+    phase_t = now;                                     \
+  } while (0)
+#else
+#define TILE_PHASE(k) do { } while (0)
+#endif
+
 // FAST: every sample id is below 2^31 and the launch's grad_out image below
 // 2^31 bytes (the launch checks both), so ids divide in 32 bits and grad_out
 // rows load through a buffer descriptor with 32-bit offsets: fewer
@@ -985,6 +1006,10 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
   stage_level_tab(p, lt);  // read after the first barrier below
   if (threadIdx.x < (unsigned)p.L) lstart[threadIdx.x] = p.start[threadIdx.x];
 
+#ifdef MSDA_TILE_PHASE_CLOCKS
+  unsigned long long phase_sum[kPhaseSlots] = {};
+  unsigned long long phase_t = __builtin_amdgcn_s_memtime();
+#endif
   for (;;) {
     // the thread index, made opaque to the compiler once per chunk: otherwise it
     // hoists the index arithmetic of every phase out of the loop, and those
@@ -1012,6 +1037,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       *next_slot = gridDim.x + __hip_atomic_fetch_add(a.w.nchunks + 1, 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
+    TILE_PHASE(0);
     // the next chunk's entry: needed only for the prefetch after the item loop
     const uint32_t cn = __builtin_amdgcn_readfirstlane(*next_slot);
     const uint4 ck_next = a.w.chunks[min(cn, nchunks - 1)];
@@ -1043,6 +1069,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       tag[i] = t;
     }
     __syncthreads();
+    TILE_PHASE(1);
     // every wave scans the cell counts itself; wave 0 stores the starts and
     // plans the items while the other waves put the records in cell order,
     // looking the starts up in their own registers
@@ -1066,6 +1093,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       }
     }
     __syncthreads();
+    TILE_PHASE(2);
 
     // ---- item loop: lane group g takes the schedule's entries g, 2NG-1-g,
     // 2NG+g, ... (largest items first, snaking so the groups of a wave get items
@@ -1245,12 +1273,15 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
         for (int i = 0; i < VEC; ++i) stage[(item * 4 + q) * RS + lane * VEC + i] = acc[q][i];
     }
     __syncthreads();
+    TILE_PHASE(3);
 
     // the next chunk's records and value rows: in flight during the two passes
     // below (after the last chunk this loads a chunk again and leaves it unused,
     // which keeps the registers of the loads out of the item loop)
     loaded_pos = chunk_bin_pos(cp_next, lt, lstart);
+    TILE_PHASE(4);
     load_chunk(ck_next, loaded_pos, tid);
+    TILE_PHASE(5);
 
     // ---- per-sample results back in record order: the scatter pass wrote a
     // bin's records in sample order, so neighbouring lanes store neighbouring
@@ -1279,6 +1310,7 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
       }
     }
 
+    TILE_PHASE(6);
     // ---- every pixel of the tile and its rim sums the items of the cells it is
     // a corner of, then goes to grad_value (interior), the rim (edge / halo) or
     // the chunk's slot
@@ -1344,10 +1376,19 @@ __global__ __launch_bounds__(256) void tile_kernel(BinArgs a) {
         for (int i = 0; i < VEC; ++i) dst[i] = v[i];
       }
     }
+    TILE_PHASE(7);
+#ifdef MSDA_TILE_PHASE_CLOCKS
+    phase_sum[kPhaseSlots - 1] += 1;
+#endif
     if (cn >= nchunks) break;
     __syncthreads();  // the next chunk reuses every LDS array
+    TILE_PHASE(8);
     ck = ck_next;
   }
+#ifdef MSDA_TILE_PHASE_CLOCKS
+  if (threadIdx.x == 0 && blockIdx.x < (unsigned)kPhaseBlocks)
+    for (int k = 0; k < kPhaseSlots; ++k) g_tile_phase[blockIdx.x][k] = phase_sum[k];
+#endif
 }
 
 // --------------------------------------------------------------- merge pass
@@ -1671,6 +1712,18 @@ size_t binned_error_offset(const BinPlan &p) { return error_offset_in_counts(p);
 
 void set_plan_spin_limit(uint32_t polls) { g_spin_limit = polls; }
 void set_tile_wide_addressing(bool wide) { g_tile_wide = wide; }
+
+hipError_t tile_phase_clocks(unsigned long long *host, int nblocks) {
+#ifdef MSDA_TILE_PHASE_CLOCKS
+  if (host == nullptr || nblocks < 0 || nblocks > kPhaseBlocks) return hipErrorInvalidValue;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_tile_phase),
+                             (size_t)nblocks * kPhaseSlots * sizeof(unsigned long long));
+#else
+  (void)host;
+  (void)nblocks;
+  return hipErrorNotSupported;
+#endif
+}
 uint32_t plan_spin_limit() { return g_spin_limit; }
 
 BinScratch carve_bin_scratch(const BinPlan &p, void *workspace) {

@@ -175,6 +175,10 @@ enum class Accum { F32, PACKED };
 // addressing path at every size instead of only where ids or the grad_out
 // image reach 2^31.
 void set_tile_wide_addressing(bool wide);
+// Per-block phase clock sums of the last tile pass (diagnostic build only, see
+// msda_binned.hip): nblocks x 12 values into host; hipErrorNotSupported in the
+// default build.
+hipError_t tile_phase_clocks(unsigned long long *host, int nblocks);
 // Forward schedule for later launches on this thread (test hook): 0 automatic,
 // 1 always the direct gather, 2 the LDS-window gather whenever it fits.
 void set_forward_schedule(int schedule);

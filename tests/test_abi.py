@@ -48,6 +48,18 @@ def test_library_exports_every_declared_symbol(lib):
     assert not missing, f"not exported: {missing}"
 
 
+def test_phase_clocks_need_the_diagnostic_build(lib):
+    """The default library records no tile-pass phase clocks: the call reports
+    MSDA_ERR_UNSUPPORTED without touching a device, and checks its arguments first."""
+    null_pointer, invalid_dims, unsupported = 1, 2, 3  # msda_status in include/msda.h
+    buf = (ctypes.c_ulonglong * 12)()
+    assert lib.msda_test_tile_phase_clocks(buf, 1) == unsupported
+    assert lib.msda_test_tile_phase_clocks(None, 1) == null_pointer
+    assert lib.msda_test_tile_phase_clocks(buf, 4096) == invalid_dims
+    with pytest.raises(msda.MsdaError):
+        msda.msda_test_tile_phase_clocks(1)
+
+
 def test_status_strings(lib):
     for code in range(7):
         assert msda.msda_status_string(code).startswith("MSDA_")
