@@ -23,8 +23,9 @@ backward step (HIP events on the launch stream), and, with --counters, the
 FETCH_SIZE / WRITE_SIZE / L2 hit rate rocprofv3 reads per launch (FETCH scaled
 by the factor a plain copy of known size gives).  Every variant's outputs are
 compared with those of the in-tree library on the same inputs (rtol 1e-5 /
-atol 1e-6 forward, 1e-4 / 1e-5 backward); that library is the one the parity
-tests check against the oracle.
+atol 1e-6 forward, 1e-4 / 1e-5 backward; 1e-2 / 1e-3 for the 16-bit outputs of
+the half-precision workloads, which `one --workload` also runs); that library
+is the one the parity tests check against the oracle.
 
   python -m scale_deformable_attention_msda_amd.sweep build [--group G ...]   (CPU: compile)
   python -m scale_deformable_attention_msda_amd.sweep run [--group G ...] [--counters]
@@ -171,14 +172,15 @@ def run_one(lib: str, workload: int, steps: int, ref_dir: str, write_ref: bool,
     msda.load_library(lib)
     msda.msda_test_set_forward_schedule(schedule)
     wl = workloads.WORKLOADS[workload]
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     batches = []
     for r in range(2):
         x = workloads.make_inputs(wl, seed=workloads.BASE_SEED + workload + 1000 * r)
-        t = {k: torch.from_numpy(x[k]).to(dev) for k in
-             ("value", "sampling_locations", "attention_weights", "grad_out", "spatial_shapes",
-              "level_start_index")}
+        t = {k: torch.from_numpy(x[k]).to(dev).to(dt) for k in
+             ("value", "sampling_locations", "attention_weights", "grad_out")}
+        t.update({k: torch.from_numpy(x[k]).to(dev) for k in ("spatial_shapes", "level_start_index")})
         batches.append(t)
     shapes_host = x["spatial_shapes"]
     t0 = batches[0]
@@ -186,7 +188,8 @@ def run_one(lib: str, workload: int, steps: int, ref_dir: str, write_ref: bool,
     gv, gl, ga = (torch.empty_like(t0["value"]), torch.empty_like(t0["sampling_locations"]),
                   torch.empty_like(t0["attention_weights"]))
     dims = msda.MsdaDims(wl.B, wl.S, wl.M, wl.D, wl.L, wl.num_queries, wl.K)
-    need = msda.msda_backward_workspace_bytes(dims, msda.MSDA_FP32, msda.MSDA_FP32,
+    mdt = {"fp32": msda.MSDA_FP32, "bf16": msda.MSDA_BF16, "fp16": msda.MSDA_FP16}[wl.dtype]
+    need = msda.msda_backward_workspace_bytes(dims, mdt, msda.MSDA_FP32,
                                               msda.MSDA_SCATTER_BINNED, shapes_host)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
@@ -216,14 +219,17 @@ def run_one(lib: str, workload: int, steps: int, ref_dir: str, write_ref: bool,
     got = {"out": out, "grad_value": gv, "grad_loc": gl, "grad_attn": ga}
     parity = {}
     for k, v in got.items():
-        a = v.cpu().numpy()
+        a = v.float().cpu().numpy()
         path = os.path.join(ref_dir, k + ".npy")
         if write_ref:
             np.save(path, a)
             parity[k] = "reference"
             continue
         ref = np.load(path)
-        rtol, atol = (1e-5, 1e-6) if k == "out" else (1e-4, 1e-5)
+        if wl.dtype != "fp32":  # 16-bit outputs: a few units in the last place
+            rtol, atol = 1e-2, 1e-3
+        else:
+            rtol, atol = (1e-5, 1e-6) if k == "out" else (1e-4, 1e-5)
         err = np.abs(a.astype(np.float64) - ref)
         bad = int((~(err <= atol + rtol * np.abs(ref.astype(np.float64)))).sum())
         parity[k] = {"max_abs": float(err.max()), "outside": bad}
