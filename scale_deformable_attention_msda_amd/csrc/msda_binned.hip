@@ -16,8 +16,10 @@
 // grad_value in LDS, writing every row once with plain stores:
 //   count    per-block LDS histogram of samples per bin, one global integer
 //            atomic per touched bin (dead samples get zero gradients here);
-//   plan     one block: exclusive scan -> bin starts, chunks of <= `chunk`
-//            samples per bin, partial-tile slots for bins split in chunks;
+//   plan     blocks of kPlanBlock bins, chained by a decoupled look-back:
+//            exclusive scans -> bin starts, chunks of <= `chunk` samples per
+//            bin with each chunk's bin position, partial-tile slots for bins
+//            split in chunks;
 //   scatter  recount in LDS, reserve each block's range per bin with one
 //            atomic, write a 16-byte record (id, location, weight) of every
 //            sample in bin order, so the tile pass reads its samples
@@ -26,12 +28,13 @@
 //            and value rows are loaded while the current one writes its
 //            results): stage the (T+1)^2 value rows of the tile
 //            (plus rim) in LDS, counting-sort the chunk's samples by their
-//            bilinear cell (integer LDS atomics), then one lane group per
-//            cell keeps the cell's four corner rows and four accumulators in
-//            registers while it walks the cell's samples: p_c, grad_loc,
-//            grad_attn, and A * w_c * grad_out summed in registers.  Each cell
-//            stores its four sums once to LDS; every pixel then adds the (up
-//            to four) cells around it.  Interior rows go straight to
+//            bilinear cell (integer LDS atomics), cut each cell's samples
+//            into pieces, then one lane group per piece keeps the cell's four
+//            corner rows and four accumulators in registers while it walks
+//            the piece's samples: p_c, grad_loc, grad_attn, and A * w_c *
+//            grad_out summed in registers.  Each piece stores its four sums
+//            once to LDS; every pixel then adds the pieces of the (up to
+//            four) cells around it.  Interior rows go straight to
 //            grad_value, edge / rim rows (or the whole partial tile of a
 //            split bin) to scratch.  No floating-point atomics: on this GPU
 //            they are an order of magnitude slower than plain LDS traffic;
